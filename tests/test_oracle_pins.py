@@ -1,0 +1,387 @@
+"""Pins of the fp64 oracle against what the CompKV page and mathematics fix.
+
+Each test names the statement it checks. None of them retypes the oracle's
+formulas: they compare it with an independent construction (token-level
+distributions, library attention, exact variances, brute-force subset search)
+or with a closed form derived from the page's definitions.
+CompKV page = onedev.kr/papers/157.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import compkv as ok
+from oracle import theory as th
+from block_sparse_kv_stats_amd import synth
+
+H16 = np.array([[1]])
+for _ in range(4):
+    H16 = np.block([[H16, H16], [H16, -H16]])
+
+
+def torch_dense(q, k, v, T):
+    """Dense attention by torch's library routine, fp64 on the CPU."""
+    qt = torch.tensor(np.asarray(q, dtype=np.float64))[None, :, None, :]
+    G = qt.shape[1]
+    kt = torch.tensor(np.asarray(k, dtype=np.float64)[:T])[None, None].expand(1, G, T, -1)
+    vt = torch.tensor(np.asarray(v, dtype=np.float64)[:T])[None, None].expand(1, G, T, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+    return o[0, :, 0, :].numpy()
+
+
+def random_unit(T, d=64, G=4, seed=0, needles=True):
+    w = synth.Workload("t", 900 + seed, S=1, H=1, G=G, d=d, r=4, budget=128,
+                       prefill=(T - 1,), steps=1, needles=needles)
+    u = synth.gen_unit(w, 0, 0)
+    return u["q"][0].astype(np.float64), u["k"], u["v"]
+
+
+def one_coordinate_keys(NB, d, rng, amp, T=None, mean_scale=1.0):
+    """Blocks whose keys differ from the block mean in one coordinate only,
+    with symmetric deviations (so every odd cumulant of the block logits is 0)."""
+    T = NB * 16 if T is None else T
+    u = np.array([1, -1, 2, -2, 0.5, -0.5, 1.5, -1.5, 0.25, -0.25, 3, -3, 0.75, -0.75, 2.5, -2.5])
+    k = np.empty((T, d))
+    for b in range(NB):
+        s, e = b * 16, min(b * 16 + 16, T)
+        mu = mean_scale * rng.standard_normal(d)
+        c = rng.integers(d)
+        k[s:e] = mu
+        k[s:e, c] += amp[b] * u[:e - s]
+    return k
+
+
+# ---------------------------------------------------------------- P1
+@pytest.mark.parametrize("T", [1024, 1000, 37])
+def test_p1_all_blocks_kept_is_dense_attention(T):
+    """Keeping every block (budget >= blocks) leaves nothing to compensate:
+    the output must be softmax attention over all tokens (torch SDPA, fp64)."""
+    q, kb, vb = random_unit(T, seed=T)
+    NB = ok.num_blocks(T)
+    res = ok.decode_step(q, kb, vb, T, r=4, budget=16 * NB)
+    assert list(res["sel"]) == list(range(NB))
+    k, v = ok.decode_bf16(kb), ok.decode_bf16(vb)
+    ref = torch_dense(q, k, v, T)
+    np.testing.assert_allclose(res["o"], ref, rtol=1e-11, atol=1e-12)
+    o_d, lse_d = ok.dense_attention(q, k, v, T)
+    np.testing.assert_allclose(o_d, ref, rtol=1e-11, atol=1e-12)
+    z = q @ k[:T].T / math.sqrt(q.shape[1])
+    np.testing.assert_allclose(lse_d, np.log(np.exp(z).sum(axis=1)), rtol=1e-12)
+    np.testing.assert_allclose(res["lse"], lse_d, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- P2
+def test_p2_constant_blocks_compensate_exactly():
+    """Blocks of identical keys have zero logit variance: D̄ = 0, σ̂² = 0,
+    S_b = 0, and Mean compensation is exact, so any selection gives dense
+    attention. With all scores tied the lowest indices fill the budget."""
+    rng = np.random.default_rng(7)
+    T, d, G = 16 * 20 + 5, 64, 4
+    NB = ok.num_blocks(T)
+    mus = rng.standard_normal((NB, d))
+    k = np.repeat(mus, 16, axis=0)[:T]
+    v = rng.standard_normal((T, d))
+    q = rng.standard_normal((G, d))
+    kb, vb = synth.bf16_bits(k), synth.bf16_bits(v)
+    res = ok.decode_step(q, kb, vb, T, r=4, budget=8 * 16)
+    assert np.all(res["dbar"] == 0) and np.all(res["sig2"] == 0) and np.all(res["S"] == 0)
+    Kb = 8
+    assert list(res["sel"]) == list(range(Kb - 2)) + [NB - 2, NB - 1]
+    ref = torch_dense(q, ok.decode_bf16(kb), ok.decode_bf16(vb), T)
+    np.testing.assert_allclose(res["o"], ref, rtol=1e-10, atol=1e-12)
+    for trial in range(5):
+        extra = rng.choice(np.arange(1, NB - 2), size=5, replace=False)
+        sel = np.sort(np.concatenate([[0, NB - 2, NB - 1], extra]))
+        other = ok.decode_step(q, kb, vb, T, r=4, budget=8 * 16, sel=sel)
+        np.testing.assert_allclose(other["o"], ref, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P3
+@pytest.mark.parametrize("T", [16 * 12, 16 * 12 - 5])
+def test_p3_single_coordinate_keys_give_exact_logit_variance(T):
+    """Keys varying in one coordinate, r = d: the page's grouped estimator
+    σ̂² equals the exact population variance of the logits over the block."""
+    rng = np.random.default_rng(3)
+    d, G = 32, 3
+    NB = ok.num_blocks(T)
+    k = one_coordinate_keys(NB, d, rng, amp=rng.uniform(0.1, 2.0, NB), T=T)
+    v = rng.standard_normal((T, d))
+    q = rng.standard_normal((G, d))
+    cnt, kbar, dbar, vbar = ok.block_summaries(k, v, T, r=d)
+    sc = ok.block_scores(q, cnt, kbar, dbar)
+    ex = th.exact_block_quantities(q, k, T)
+    np.testing.assert_allclose(sc["sig2"], ex["sigma2"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(sc["zbar"], ex["zmean"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(cnt, ex["size"])
+
+
+# ---------------------------------------------------------------- P4
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+def test_p4_isotropic_blocks_closed_form_any_r(r):
+    """Blocks built from 8 orthogonal zero-mean ±1 Hadamard columns have every
+    coordinate variance equal to s_b² and no covariance: D̄_b = s_b² in every
+    group, and σ̂² = |q|² s_b² / d = the exact logit variance, for every r."""
+    rng = np.random.default_rng(11)
+    d, G, NB = 8, 2, 6
+    T = 16 * NB
+    s = rng.uniform(0.2, 1.5, NB)
+    k = np.empty((T, d))
+    for b in range(NB):
+        k[16 * b:16 * b + 16] = rng.standard_normal(d) + s[b] * H16[:, 1:1 + d]
+    v = rng.standard_normal((T, d))
+    q = rng.standard_normal((G, d))
+    cnt, kbar, dbar, vbar = ok.block_summaries(k, v, T, r=r)
+    np.testing.assert_allclose(dbar, np.repeat(s[:, None] ** 2, r, axis=1), rtol=1e-12)
+    sc = ok.block_scores(q, cnt, kbar, dbar)
+    closed = (q ** 2).sum(axis=1)[:, None] * s[None, :] ** 2 / d
+    np.testing.assert_allclose(sc["sig2"], closed, rtol=1e-12)
+    ex = th.exact_block_quantities(q, k, T)
+    np.testing.assert_allclose(sc["sig2"], ex["sigma2"], rtol=1e-10)
+
+
+def test_p4_r1_uses_mean_coordinate_variance():
+    """r = 1: σ̂² = |q|²/d times the mean over coordinates of the population
+    variance of the block's keys (numpy var)."""
+    q, kb, vb = random_unit(16 * 9 + 3, d=64, seed=4)
+    T = 16 * 9 + 3
+    k, v = ok.decode_bf16(kb), ok.decode_bf16(vb)
+    cnt, kbar, dbar, vbar = ok.block_summaries(k, v, T, r=1)
+    sc = ok.block_scores(q, cnt, kbar, dbar)
+    for b in range(ok.num_blocks(T)):
+        kbk = k[16 * b:min(16 * b + 16, T)]
+        mv = kbk.var(axis=0).mean()
+        np.testing.assert_allclose(sc["sig2"][:, b], (q ** 2).sum(axis=1) * mv / 64, rtol=1e-12)
+        np.testing.assert_allclose(kbar[b], kbk.mean(axis=0), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(vbar[b], v[16 * b:min(16 * b + 16, T)].mean(axis=0),
+                                   rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- P5
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_p5_log_partition_identity_and_token_level_output(seed):
+    """Mean compensation equals attention under the token-level compensated
+    distribution Q (skipped tokens get their block-mean logit): the oracle's
+    output is sum_i Q_i v_i, and KL(Q||P) summed directly equals
+    ln Z - ln Z' (the page's exact log-partition identity)."""
+    T = 16 * 40 + 9
+    q, kb, vb = random_unit(T, d=64, seed=20 + seed)
+    k, v = ok.decode_bf16(kb), ok.decode_bf16(vb)
+    rng = np.random.default_rng(seed)
+    NB = ok.num_blocks(T)
+    extra = rng.choice(np.arange(1, NB - 2), size=7, replace=False)
+    sel = np.sort(np.concatenate([[0, NB - 2, NB - 1], extra]))
+    res = ok.decode_step(q, kb, vb, T, r=4, budget=10 * 16, sel=sel)
+    logQ, logP = th.compensated_token_distribution(q, k, T, sel)
+    np.testing.assert_allclose(res["o"], np.exp(logQ) @ v[:T], rtol=1e-10, atol=1e-12)
+    kl_direct = (np.exp(logQ) * (logQ - logP)).sum(axis=1)
+    _, lse_dense = ok.dense_attention(q, k, v, T)
+    np.testing.assert_allclose(kl_direct, lse_dense - res["lse"], rtol=1e-8, atol=1e-12)
+    ex = th.exact_block_quantities(q, k, T)
+    per_g = -np.log1p(-ex["delta"][:, np.setdiff1d(np.arange(NB), sel)].sum(axis=1))
+    np.testing.assert_allclose(kl_direct, per_g, rtol=1e-8, atol=1e-12)
+    assert np.all(kl_direct >= -1e-14)
+
+
+# ---------------------------------------------------------------- P6
+def test_p6_taylor_mass_deficit():
+    """δ_{g,b} = p_{g,b}(1 - |b| e^{z̄}/Z) approaches p_{g,b} σ²_{g,b}/2 as the
+    within-block logit spread shrinks (the page's second-order expansion)."""
+    rng = np.random.default_rng(5)
+    d, G, NB = 16, 2, 12
+    amp = rng.uniform(0.5, 1.5, NB)
+    devs = []
+    for scale in (1.0, 0.1, 0.01):
+        k = one_coordinate_keys(NB, d, np.random.default_rng(6), amp=scale * amp)
+        q = np.random.default_rng(8).standard_normal((G, d))
+        ex = th.exact_block_quantities(q, k, 16 * NB)
+        ratio = ex["delta"] / (0.5 * ex["p"] * ex["sigma2"])
+        devs.append(np.median(np.abs(ratio - 1)))
+    assert devs[1] < devs[0] / 5 and devs[2] < devs[1] / 5
+    assert devs[2] < 1e-3
+
+
+# ---------------------------------------------------------------- P7
+@pytest.mark.parametrize("seed", range(6))
+def test_p7_no_compensation_single_head_is_topk_mass(seed):
+    """Without Mean compensation and with one query head the objective's
+    minimiser over all budget-feasible kept sets is the forced set plus Top-K
+    by exact block attention mass (the page's appendix reduction). The
+    oracle's no-compensation output matches that loss: ln Z - ln Z_kept."""
+    T, NB, Kb = 16 * 10 - 3, 10, 5
+    q, kb, vb = random_unit(T, d=32, G=1, seed=40 + seed)
+    k, v = ok.decode_bf16(kb), ok.decode_bf16(vb)
+    ex = th.exact_block_quantities(q, k, T)
+    best, bl, second = th.brute_force_best(lambda s: th.no_compensation_loss(ex["p"], s), NB, Kb)
+    np.testing.assert_array_equal(ok.select_blocks(ex["p"][0], Kb), best)
+    cnt, kbar, dbar, vbar = ok.block_summaries(k, v, T, r=4)
+    _, lse_nc = ok.compensated_attention(q, k, v, T, best, cnt, kbar, vbar, compensate=False)
+    _, lse_d = ok.dense_attention(q, k, v, T)
+    np.testing.assert_allclose(lse_d - lse_nc, bl, rtol=1e-9)
+
+
+# ---------------------------------------------------------------- P8
+@pytest.mark.parametrize("seed", range(4))
+def test_p8_forced_set_and_budget_by_brute_force(seed):
+    """select_blocks keeps F and fills the budget to minimise the estimated
+    surrogate (1/2) sum_skipped S_b: brute force over all feasible sets."""
+    rng = np.random.default_rng(seed)
+    NB, Kb = 11, 6
+    S = rng.exponential(size=NB)
+    best, _, _ = th.brute_force_best(lambda s: th.estimated_loss(S, s), NB, Kb)
+    np.testing.assert_array_equal(ok.select_blocks(S, Kb), best)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_p8_single_head_exact_loss_is_topk_delta(seed):
+    """G = 1: the exact KL loss is -ln(1 - sum_skipped δ_b), monotone in the
+    skipped δ mass, so its brute-force minimiser is F + Top-K by δ_b."""
+    T, NB, Kb = 16 * 10, 10, 5
+    q, kb, vb = random_unit(T, d=32, G=1, seed=60 + seed)
+    k = ok.decode_bf16(kb)
+    ex = th.exact_block_quantities(q, k, T)
+    best, _, _ = th.brute_force_best(lambda s: th.exact_loss(ex["delta"], s), NB, Kb)
+    np.testing.assert_array_equal(ok.select_blocks(ex["delta"][0], Kb), best)
+
+
+def test_p8_small_spread_selection_minimises_exact_kl():
+    """End to end: with single-coordinate keys (so σ̂² is exact at r = d) and a
+    small within-block spread, the oracle's selection from block summaries
+    alone equals the brute-force minimiser of the exact summed KL loss over
+    every budget-feasible kept set, for G = 4 query heads (whose losses add)."""
+    agree, clear = 0, 0
+    for seed in range(20):
+        rng = np.random.default_rng(100 + seed)
+        d, G, NB, Kb = 16, 4, 12, 6
+        T = 16 * NB
+        amp = 0.06 * np.exp(rng.uniform(-1.5, 1.5, NB))
+        k = one_coordinate_keys(NB, d, rng, amp=amp, mean_scale=0.7)
+        v = rng.standard_normal((T, d))
+        q = rng.standard_normal((G, d))
+        cnt, kbar, dbar, vbar = ok.block_summaries(k, v, T, r=d)
+        sel = ok.select_blocks(ok.block_scores(q, cnt, kbar, dbar)["S"], Kb)
+        ex = th.exact_block_quantities(q, k, T)
+        best, bl, second = th.brute_force_best(lambda s: th.exact_loss(ex["delta"], s), NB, Kb)
+        if second > bl * 1.05:
+            clear += 1
+            agree += int(np.array_equal(sel, best))
+    assert clear >= 12
+    assert agree == clear
+
+
+# ---------------------------------------------------------------- P9
+def test_p9_second_order_mass_estimate_converges_at_fourth_order():
+    """With exact σ̂² (single-coordinate keys, r = d) and symmetric spread,
+    ln(Z_b/|b|) = z̄ + σ²/2 + O(σ⁴), so p̂ -> p with error O(σ⁴): halving the
+    spread cuts the error ~16x. The first-order estimate (no σ²/2) converges
+    only at O(σ²) (~4x); the test tells the two apart."""
+    rng = np.random.default_rng(9)
+    d, G, NB = 16, 2, 12
+    amp = rng.uniform(0.5, 1.5, NB)
+    q = rng.standard_normal((G, d))
+
+    def err(scale, order):
+        k = one_coordinate_keys(NB, d, np.random.default_rng(10), amp=scale * amp)
+        v = np.zeros((16 * NB, d))
+        cnt, kbar, dbar, vbar = ok.block_summaries(k, v, 16 * NB, r=d)
+        sc = ok.block_scores(q, cnt, kbar, dbar, mass_order=order)
+        ex = th.exact_block_quantities(q, k, 16 * NB)
+        return np.abs(np.log(sc["phat"]) - np.log(ex["p"])).max()
+
+    r2 = err(0.2, 2) / err(0.1, 2)
+    r1 = err(0.2, 1) / err(0.1, 1)
+    assert 12 < r2 < 20, r2
+    assert 3 < r1 < 5, r1
+    assert err(0.1, 2) < 1e-4
+
+
+# ---------------------------------------------------------------- P10
+@pytest.mark.parametrize("T,Kb", [(1, 3), (16, 3), (17, 3), (33, 3), (48, 3), (16 * 8, 8), (16 * 8 - 1, 8)])
+def test_p10_small_contexts_keep_everything(T, Kb):
+    q, kb, vb = random_unit(max(T, 2), d=64, seed=T)
+    res = ok.decode_step(q, kb, vb, T, r=4, budget=16 * Kb)
+    assert list(res["sel"]) == list(range(ok.num_blocks(T)))
+
+
+def test_p10_empty_context():
+    res = ok.decode_step(np.ones((2, 8)), np.zeros((0, 8), np.uint16), np.zeros((0, 8), np.uint16),
+                         0, r=4, budget=64)
+    assert len(res["sel"]) == 0 and np.all(res["o"] == 0) and np.all(np.isneginf(res["lse"]))
+
+
+# ---------------------------------------------------------------- P11
+def test_p11_output_is_affine_in_values():
+    """o is a convex combination of values and block-mean values with weights
+    that do not depend on V: o(aV + c) = a o(V) + c."""
+    T = 16 * 30 + 11
+    q, kb, vb = random_unit(T, d=64, seed=31)
+    k, v = ok.decode_bf16(kb), ok.decode_bf16(vb)
+    a, c = -1.7, np.linspace(-2, 2, 64)
+    cnt, kbar, dbar, vbar = ok.block_summaries(k, v, T, r=4)
+    sel = ok.select_blocks(ok.block_scores(q, cnt, kbar, dbar)["S"], 8)
+    o1, _ = ok.compensated_attention(q, k, v, T, sel, cnt, kbar, vbar)
+    v2 = a * v + c
+    cnt2, kbar2, dbar2, vbar2 = ok.block_summaries(k, v2, T, r=4)
+    o2, _ = ok.compensated_attention(q, k, v2, T, sel, cnt2, kbar2, vbar2)
+    np.testing.assert_allclose(o2, a * o1 + c, rtol=1e-11, atol=1e-12)
+
+
+def test_p11_group_permutation_invariance():
+    """Permuting coordinates (of q and keys together) inside a variance group
+    leaves every score unchanged; moving a coordinate across groups changes
+    the scores of anisotropic keys (the groups are contiguous ranges)."""
+    T = 16 * 24
+    w = synth.WORKLOADS["qwen32b_64k"].replace(prefill=(T - 1,), d=64, G=4)
+    u = synth.gen_unit(w, 0, 0)
+    q = u["q"][0].astype(np.float64)
+    k, v = ok.decode_bf16(u["k"]), ok.decode_bf16(u["v"])
+    r = 4
+
+    def scores(perm):
+        cnt, kbar, dbar, vbar = ok.block_summaries(k[:, perm], v, T, r=r)
+        return ok.block_scores(q[:, perm], cnt, kbar, dbar)["S"]
+
+    base = scores(np.arange(64))
+    rng = np.random.default_rng(0)
+    within = np.concatenate([16 * t + rng.permutation(16) for t in range(r)])
+    np.testing.assert_allclose(scores(within), base, rtol=1e-12)
+    across = np.arange(64)
+    across[[3, 40]] = across[[40, 3]]
+    assert np.max(np.abs(scores(across) / base - 1)) > 1e-3
+
+
+# ---------------------------------------------------------------- P12
+def test_p12_streaming_summaries_equal_rebuild():
+    """The per-step update of the open block (page: the current block's
+    statistics are refreshed every step) gives the same summaries as building
+    every block from the cache, across block-close events."""
+    w = synth.WORKLOADS["qwen8b_128k"].replace(prefill=(16 * 20 - 5,), steps=40, d=64)
+    u = synth.gen_unit(w, 0, 0)
+    T0 = w.prefill[0]
+    su = ok.StreamingUnit(u["k"], u["v"], T0, r=w.r, cap_tokens=T0 + w.steps)
+    for t in range(w.steps):
+        su.append(u["k"][T0 + t], u["v"][T0 + t])
+        T = T0 + t + 1
+        ref = ok.block_summaries(ok.decode_bf16(u["k"]), ok.decode_bf16(u["v"]), T, r=w.r)
+        for got, want in zip(su.summaries(), ref):
+            np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
+    out = su.step(u["q"][w.steps - 1], w.budget)
+    full = ok.decode_step(u["q"][w.steps - 1], u["k"], u["v"], su.T, r=w.r, budget=w.budget)
+    np.testing.assert_array_equal(out["sel"], full["sel"])
+    np.testing.assert_allclose(out["o"], full["o"], rtol=1e-12)
+
+
+# ---------------------------------------------------------------- generator sanity
+def test_generator_needles_raise_mean_query_logit():
+    w = synth.WORKLOADS["llama8b_32k"].replace(prefill=(4095,))
+    u = synth.gen_unit(w, 0, 3)
+    rng = np.random.default_rng([w.cfg_id, 0, 3])
+    q0 = u["q"][0].astype(np.float64)
+    qbar = q0.mean(axis=0)
+    k = ok.decode_bf16(u["k"])
+    z = k @ qbar / math.sqrt(w.d)
+    # needles sit ~DELTA above the bulk of the logits
+    hi = z > np.percentile(z, 50) + 6
+    assert 0.005 < hi.mean() < 0.02
+    assert u["k"].dtype == np.uint16 and u["q"].dtype == np.float32
