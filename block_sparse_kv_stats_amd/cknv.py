@@ -1,0 +1,260 @@
+"""Thin Python binding of libcknv (the C ABI in include/cknv.h).
+
+Argument marshalling only: torch tensors provide device memory and the HIP
+stream; every step of the decode path runs in the library's kernels. The
+library is loaded on first use; if it is missing this raises (there is no
+fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcknv.so")
+
+OK, EINVAL, EUNSUPPORTED, ENOSPACE, EHIP = 0, -1, -2, -3, -4
+BLOCK = 16
+
+
+class CknvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("r", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("cap_blocks", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("kbar", ctypes.c_void_p),
+                ("dbar", ctypes.c_void_p), ("cnt", ctypes.c_void_p), ("vbar", ctypes.c_void_p),
+                ("seq_len", ctypes.c_void_p)]
+
+
+_lib = None
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+SZ = ctypes.c_size_t
+SIGNATURES = {
+    "cknv_workspace_size": [ctypes.POINTER(Shape), I32, I32, ctypes.POINTER(SZ)],
+    "cknv_workspace_init": [ctypes.POINTER(Shape), I32, I32, P, SZ, P],
+    "cknv_append": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, I32, I32, P, SZ, P],
+    "cknv_build_summaries": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), I32, P],
+    "cknv_score_select": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, I32, I32, P, P, P, P,
+                          SZ, P],
+    "cknv_attend": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P, I32, I32, P, P, P, SZ,
+                    P],
+    "cknv_dense_attend": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, I32, I32, P, P, P, SZ,
+                          P],
+}
+
+
+def lib():
+    """The loaded libcknv (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_kv_stats_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.cknv_status_str.argtypes = [ctypes.c_int]
+        L.cknv_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().cknv_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise CknvError(status, what)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, dtype=None, numel=None, what=""):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+    if dtype is not None and t.dtype not in dtype:
+        raise ValueError(f"{what}: dtype {t.dtype} not in {dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{what}: {t.numel()} elements, need {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def make_shape(S, H, G, d, r, cap_blocks, flags=0) -> Shape:
+    return Shape(S, H, G, d, r, BLOCK, cap_blocks, flags)
+
+
+@dataclasses.dataclass
+class LayerCache:
+    """Device tensors of one layer's KV cache and summary store (see cknv.h)."""
+    shape: Shape
+    k: object        # bf16 [S][H][cap_blocks*16][d]
+    v: object
+    kbar: object     # fp32 [S][H][cap_blocks][d]
+    dbar: object     # fp32 [S][H][cap_blocks][r]
+    cnt: object      # fp32 [S][H][cap_blocks]
+    vbar: object     # fp32 [S][H][cap_blocks][d]
+    seq_len: object  # int32 [S]
+
+    @staticmethod
+    def allocate(shape: Shape, device="cuda"):
+        import torch
+        S, H, d, r, cb = shape.S, shape.H, shape.d, shape.r, shape.cap_blocks
+        f32 = dict(dtype=torch.float32, device=device)
+        return LayerCache(
+            shape,
+            torch.zeros((S, H, cb * BLOCK, d), dtype=torch.bfloat16, device=device),
+            torch.zeros((S, H, cb * BLOCK, d), dtype=torch.bfloat16, device=device),
+            torch.zeros((S, H, cb, d), **f32), torch.zeros((S, H, cb, r), **f32),
+            torch.zeros((S, H, cb), **f32), torch.zeros((S, H, cb, d), **f32),
+            torch.zeros((S,), dtype=torch.int32, device=device))
+
+    def c_struct(self) -> Cache:
+        import torch
+        s = self.shape
+        n_tok = s.S * s.H * s.cap_blocks * BLOCK * s.d
+        n_row = s.S * s.H * s.cap_blocks
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        f32 = (torch.float32,)
+        return Cache(_ptr(self.k, bf, n_tok, "k"), _ptr(self.v, bf, n_tok, "v"),
+                     _ptr(self.kbar, f32, n_row * s.d, "kbar"),
+                     _ptr(self.dbar, f32, n_row * s.r, "dbar"),
+                     _ptr(self.cnt, f32, n_row, "cnt"),
+                     _ptr(self.vbar, f32, n_row * s.d, "vbar"),
+                     _ptr(self.seq_len, (torch.int32,), s.S, "seq_len"))
+
+
+def workspace_size(shape: Shape, max_blocks: int, budget: int) -> int:
+    n = SZ(0)
+    _check(lib().cknv_workspace_size(ctypes.byref(shape), max_blocks, budget, ctypes.byref(n)),
+           "cknv_workspace_size")
+    return int(n.value)
+
+
+def allocate_workspace(shape: Shape, max_blocks: int, budget: int, device="cuda", stream=None):
+    """A zeroed-counter workspace (uint8 tensor) for these sizes."""
+    import torch
+    ws = torch.empty(workspace_size(shape, max_blocks, budget), dtype=torch.uint8, device=device)
+    _check(lib().cknv_workspace_init(ctypes.byref(shape), max_blocks, budget, _ptr(ws, what="ws"),
+                                     ws.numel(), _stream(stream)), "cknv_workspace_init")
+    return ws
+
+
+def append(cache: LayerCache, new_k, new_v, max_blocks: int, budget: int, ws, stream=None):
+    import torch
+    s = cache.shape
+    n = s.S * s.H * s.d
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    c = cache.c_struct()
+    _check(lib().cknv_append(ctypes.byref(s), ctypes.byref(c), _ptr(new_k, bf, n, "new_k"),
+                             _ptr(new_v, bf, n, "new_v"), max_blocks, budget,
+                             _ptr(ws, what="ws"), ws.numel(), _stream(stream)), "cknv_append")
+
+
+def build_summaries(cache: LayerCache, max_blocks: int, stream=None):
+    c = cache.c_struct()
+    _check(lib().cknv_build_summaries(ctypes.byref(cache.shape), ctypes.byref(c), max_blocks,
+                                      _stream(stream)), "cknv_build_summaries")
+
+
+def score_select(cache: LayerCache, q, budget: int, max_blocks: int, sel, n_sel, ws,
+                 scores=None, stream=None):
+    import torch
+    s = cache.shape
+    Kb = budget // BLOCK
+    c = cache.c_struct()
+    _check(lib().cknv_score_select(
+        ctypes.byref(s), ctypes.byref(c), _ptr(q, (torch.float32,), s.S * s.H * s.G * s.d, "q"),
+        budget, max_blocks,
+        _ptr(scores, (torch.float32,), s.S * s.H * s.cap_blocks, "scores"),
+        _ptr(sel, (torch.int32,), s.S * s.H * Kb, "sel"),
+        _ptr(n_sel, (torch.int32,), s.S * s.H, "n_sel"),
+        _ptr(ws, what="ws"), ws.numel(), _stream(stream)), "cknv_score_select")
+
+
+def attend(cache: LayerCache, q, sel, n_sel, budget: int, max_blocks: int, out, ws, lse=None,
+           stream=None):
+    import torch
+    s = cache.shape
+    Kb = budget // BLOCK
+    nq = s.S * s.H * s.G
+    c = cache.c_struct()
+    _check(lib().cknv_attend(
+        ctypes.byref(s), ctypes.byref(c), _ptr(q, (torch.float32,), nq * s.d, "q"),
+        _ptr(sel, (torch.int32,), s.S * s.H * Kb, "sel"),
+        _ptr(n_sel, (torch.int32,), s.S * s.H, "n_sel"), budget, max_blocks,
+        _ptr(out, (torch.float32,), nq * s.d, "out"), _ptr(lse, (torch.float32,), nq, "lse"),
+        _ptr(ws, what="ws"), ws.numel(), _stream(stream)), "cknv_attend")
+
+
+def dense_attend(cache: LayerCache, q, max_blocks: int, budget: int, out, ws, lse=None,
+                 stream=None):
+    import torch
+    s = cache.shape
+    nq = s.S * s.H * s.G
+    c = cache.c_struct()
+    _check(lib().cknv_dense_attend(
+        ctypes.byref(s), ctypes.byref(c), _ptr(q, (torch.float32,), nq * s.d, "q"), max_blocks,
+        budget, _ptr(out, (torch.float32,), nq * s.d, "out"),
+        _ptr(lse, (torch.float32,), nq, "lse"), _ptr(ws, what="ws"), ws.numel(),
+        _stream(stream)), "cknv_dense_attend")
+
+
+class DecodeStep:
+    """Buffers for one CompKV decode step of a layer: append, score/select, attend.
+
+    Holds the workspace and the sel/n_sel/out/lse tensors sized for
+    (max_blocks, budget)."""
+
+    def __init__(self, cache: LayerCache, max_blocks: int, budget: int, want_scores=False,
+                 stream=None):
+        import torch
+        s = cache.shape
+        dev = cache.k.device
+        self.cache, self.max_blocks, self.budget = cache, max_blocks, budget
+        self.Kb = budget // BLOCK
+        self.ws = allocate_workspace(s, max_blocks, budget, device=dev, stream=stream)
+        self.sel = torch.zeros((s.S * s.H, self.Kb), dtype=torch.int32, device=dev)
+        self.n_sel = torch.zeros((s.S * s.H,), dtype=torch.int32, device=dev)
+        self.out = torch.zeros((s.S, s.H * s.G, s.d), dtype=torch.float32, device=dev)
+        self.lse = torch.zeros((s.S, s.H * s.G), dtype=torch.float32, device=dev)
+        self.scores = (torch.zeros((s.S, s.H, s.cap_blocks), dtype=torch.float32, device=dev)
+                       if want_scores else None)
+
+    def __call__(self, q, new_k=None, new_v=None, stream=None):
+        if new_k is not None:
+            append(self.cache, new_k, new_v, self.max_blocks, self.budget, self.ws, stream)
+        score_select(self.cache, q, self.budget, self.max_blocks, self.sel, self.n_sel, self.ws,
+                     self.scores, stream)
+        attend(self.cache, q, self.sel, self.n_sel, self.budget, self.max_blocks, self.out,
+               self.ws, self.lse, stream)
+        return self.out
+
+
+def blocks_for(tokens: int) -> int:
+    return int(math.ceil(tokens / BLOCK))

@@ -1,0 +1,214 @@
+// C ABI of libcknv: argument validation, workspace plan, kernel launches.
+// Validation runs before any HIP call; on error nothing is enqueued.
+#include <math.h>
+
+#include "cknv_internal.h"
+
+namespace cknv {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int check_shape(const cknv_shape* sh) {
+  if (!sh) return CKNV_EINVAL;
+  if (sh->S < 1 || sh->H < 1 || sh->G < 1 || sh->d < 1 || sh->r < 1 || sh->cap_blocks < 1)
+    return CKNV_EINVAL;
+  if (sh->block != kBlock) return CKNV_EUNSUPPORTED;
+  if (sh->d != 64 && sh->d != 128) return CKNV_EUNSUPPORTED;
+  if (sh->G != 1 && sh->G != 2 && sh->G != 4 && sh->G != 8) return CKNV_EUNSUPPORTED;
+  if (sh->r > sh->d || sh->d % sh->r != 0) return CKNV_EUNSUPPORTED;
+  if (sh->flags != 0u) return CKNV_EUNSUPPORTED;
+  if ((long long)sh->S * sh->H > (1 << 20)) return CKNV_EUNSUPPORTED;
+  return CKNV_OK;
+}
+
+static int check_cache(const cknv_cache* c) {
+  if (!c || !c->k || !c->v || !c->kbar || !c->dbar || !c->cnt || !c->vbar || !c->seq_len)
+    return CKNV_EINVAL;
+  return CKNV_OK;
+}
+
+int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if (max_blocks < 1) return CKNV_EINVAL;
+  if (max_blocks > sh->cap_blocks) return CKNV_ENOSPACE;
+  if (budget_tokens < 3 * kBlock) return CKNV_EINVAL;  // must hold the forced set
+  const int G = sh->G, d = sh->d, r = sh->r;
+  Plan q{};
+  q.U = sh->S * sh->H;
+  q.NBmax = max_blocks;
+  q.NG = (max_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
+  q.Kb = budget_tokens / kBlock;
+  const int iters = (max_blocks + kBlocksPerIter - 1) / kBlocksPerIter;
+  q.C = iters < kMaxChunks ? iters : kMaxChunks;
+  const int ipc = (iters + q.C - 1) / q.C;
+  q.BPC = ipc * kBlocksPerIter;
+  q.C = (max_blocks + q.BPC - 1) / q.BPC;
+  q.P = (q.Kb + kWaves - 1) / kWaves;
+  const int want = (kDenseTargetWGs + q.U - 1) / q.U;
+  const int most = (max_blocks + kWaves - 1) / kWaves;
+  q.Pd = want < most ? want : most;
+  if (q.Pd < 1) q.Pd = 1;
+  const size_t W = (size_t)d + 2;
+  size_t off = 0;
+  q.off_ctr = off;
+  q.n_ctr = (size_t)kCtrRows * (size_t)(q.U > sh->S ? q.U : sh->S);
+  off = align256(off + q.n_ctr * 4);
+  q.off_grp = off;
+  off = align256(off + (size_t)q.U * q.NG * G * 2 * 4);
+  q.off_u = off;
+  off = align256(off + (size_t)q.U * max_blocks * G * 4);
+  q.off_comp = off;
+  off = align256(off + (size_t)q.U * q.C * G * W * 4);
+  q.off_attp = off;
+  off = align256(off + (size_t)q.U * q.P * G * W * 4);
+  q.off_dense = off;
+  off = align256(off + (size_t)q.U * q.Pd * G * W * 4);
+  q.total = off;
+  const size_t main_lds = ((size_t)G * d + (size_t)G * r + (size_t)kWaves * 16 * G + (size_t)kWaves * G * W) * 4;
+  const size_t kp = (size_t)max_blocks + (size_t)max_blocks / 32 + 2;
+  const size_t tail_lds = kp * 4 + (size_t)q.NG * G * 4 + ((size_t)kWaves * G * 2 + G + 3) * 4 + 256 * 4 + 16 * 4;
+  q.score_lds = main_lds > tail_lds ? main_lds : tail_lds;
+  if (q.score_lds > kMaxLds) return CKNV_EUNSUPPORTED;
+  *p = q;
+  return CKNV_OK;
+}
+
+static uint32_t* ctr_row(void* ws, const Plan& p, int row) {
+  const size_t rowlen = p.n_ctr / kCtrRows;
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.off_ctr) + (size_t)row * rowlen;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? CKNV_OK : CKNV_EHIP; }
+
+}  // namespace cknv
+
+using namespace cknv;
+
+extern "C" {
+
+int cknv_workspace_size(const cknv_shape* shape, int32_t max_blocks, int32_t budget_tokens,
+                        size_t* bytes) {
+  if (!bytes) return CKNV_EINVAL;
+  Plan p;
+  const int st = make_plan(shape, max_blocks, budget_tokens, &p);
+  if (st) return st;
+  *bytes = p.total;
+  return CKNV_OK;
+}
+
+int cknv_workspace_init(const cknv_shape* shape, int32_t max_blocks, int32_t budget_tokens,
+                        void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, max_blocks, budget_tokens, &p);
+  if (st) return st;
+  if (!ws) return CKNV_EINVAL;
+  if (ws_bytes < p.total) return CKNV_ENOSPACE;
+  return hip_status(launch_zero_u32(ctr_row(ws, p, 0), p.n_ctr, (hipStream_t)stream));
+}
+
+int cknv_append(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                const uint16_t* new_v, int32_t max_blocks, int32_t budget_tokens, void* ws,
+                size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, max_blocks, budget_tokens, &p);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!new_k || !new_v || !ws) return CKNV_EINVAL;
+  if (ws_bytes < p.total) return CKNV_ENOSPACE;
+  AppendArgs a{cache->k, cache->v, cache->kbar, cache->dbar, cache->cnt, cache->vbar,
+               cache->seq_len, new_k, new_v, ctr_row(ws, p, kCtrAppend),
+               shape->S, shape->H, shape->r, shape->cap_blocks};
+  return hip_status(launch_append(shape->d, a, p.U, (hipStream_t)stream));
+}
+
+int cknv_build_summaries(const cknv_shape* shape, const cknv_cache* cache, int32_t max_blocks,
+                         void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (max_blocks < 1) return CKNV_EINVAL;
+  if (max_blocks > shape->cap_blocks) return CKNV_ENOSPACE;
+  BuildArgs a{cache->k, cache->v, cache->kbar, cache->dbar, cache->cnt, cache->vbar,
+              cache->seq_len, shape->S, shape->H, shape->r, shape->cap_blocks, max_blocks};
+  return hip_status(launch_build(shape->d, a, shape->S * shape->H, (hipStream_t)stream));
+}
+
+int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                      int32_t budget_tokens, int32_t max_blocks, float* scores, int32_t* sel,
+                      int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, max_blocks, budget_tokens, &p);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!q || !sel || !n_sel || !ws) return CKNV_EINVAL;
+  if (ws_bytes < p.total) return CKNV_ENOSPACE;
+  char* w = static_cast<char*>(ws);
+  ScoreArgs a{};
+  a.kbar = cache->kbar; a.dbar = cache->dbar; a.cnt = cache->cnt; a.vbar = cache->vbar;
+  a.seq_len = cache->seq_len; a.q = q;
+  a.scores = scores; a.sel = sel; a.n_sel = n_sel;
+  a.ctr = ctr_row(ws, p, kCtrScore);
+  a.grp = reinterpret_cast<float*>(w + p.off_grp);
+  a.u = reinterpret_cast<float*>(w + p.off_u);
+  a.comp = reinterpret_cast<float*>(w + p.off_comp);
+  a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
+  a.max_blocks = max_blocks; a.NG = p.NG; a.Kb = p.Kb; a.C = p.C; a.BPC = p.BPC;
+  a.xcd = (p.U % 8) == 0;
+  a.isd = 1.0f / sqrtf((float)shape->d);
+  return hip_status(launch_score(shape->d, shape->G, a, p.U, p.score_lds, (hipStream_t)stream));
+}
+
+static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                         const int32_t* sel, const int32_t* n_sel, int32_t budget_tokens,
+                         int32_t max_blocks, float* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream, bool dense) {
+  Plan p;
+  int st = make_plan(shape, max_blocks, budget_tokens, &p);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!q || !out || !ws) return CKNV_EINVAL;
+  if (!dense && (!sel || !n_sel)) return CKNV_EINVAL;
+  if (ws_bytes < p.total) return CKNV_ENOSPACE;
+  char* w = static_cast<char*>(ws);
+  AttendArgs a{};
+  a.k = cache->k; a.v = cache->v; a.kbar = cache->kbar; a.vbar = cache->vbar; a.cnt = cache->cnt;
+  a.seq_len = cache->seq_len; a.q = q; a.sel = sel; a.n_sel = n_sel;
+  a.out = out; a.lse = lse;
+  a.ctr = ctr_row(ws, p, dense ? kCtrDense : kCtrAttend);
+  a.comp = reinterpret_cast<const float*>(w + p.off_comp);
+  a.part = reinterpret_cast<float*>(w + (dense ? p.off_dense : p.off_attp));
+  a.S = shape->S; a.H = shape->H; a.cap_blocks = shape->cap_blocks; a.max_blocks = max_blocks;
+  a.Kb = p.Kb; a.C = p.C; a.P = dense ? p.Pd : p.P;
+  a.xcd = (p.U % 8) == 0;
+  a.isd = 1.0f / sqrtf((float)shape->d);
+  return hip_status(launch_attend(shape->d, shape->G, dense, a, p.U, (hipStream_t)stream));
+}
+
+int cknv_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                const int32_t* sel, const int32_t* n_sel, int32_t budget_tokens,
+                int32_t max_blocks, float* out, float* lse, void* ws, size_t ws_bytes,
+                void* stream) {
+  return attend_common(shape, cache, q, sel, n_sel, budget_tokens, max_blocks, out, lse, ws,
+                       ws_bytes, stream, false);
+}
+
+int cknv_dense_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                      int32_t max_blocks, int32_t budget_tokens, float* out, float* lse,
+                      void* ws, size_t ws_bytes, void* stream) {
+  return attend_common(shape, cache, q, nullptr, nullptr, budget_tokens, max_blocks, out, lse,
+                       ws, ws_bytes, stream, true);
+}
+
+const char* cknv_status_str(int status) {
+  switch (status) {
+    case CKNV_OK: return "CKNV_OK";
+    case CKNV_EINVAL: return "CKNV_EINVAL: null pointer or invalid size";
+    case CKNV_EUNSUPPORTED: return "CKNV_EUNSUPPORTED: shape not handled by the kernels";
+    case CKNV_ENOSPACE: return "CKNV_ENOSPACE: workspace too small or max_blocks beyond capacity";
+    case CKNV_EHIP: return "CKNV_EHIP: HIP launch or runtime error";
+    default: return "unknown cknv status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Block-summary kernels: the per-step append (new token + open-block
+// refresh) and the bulk build of every block's summary from the cache.
+//
+// CompKV page (onedev.kr/papers/157), "What differs": a block's summary is
+// {|b|, mean key, D̄_b, mean value}, where D̄_b holds for each of the r groups
+// of key coordinates the mean of those coordinates' variances.
+// "How to use it": every decode step a fused kernel refreshes the current
+// block's statistics and stores the new K/V.
+//
+// Both kernels recompute a block from its (at most 16) BF16 tokens with the
+// same device function: two passes in FP32 (mean, then the mean squared
+// deviation, i.e. the population variance), summed in token order.
+#include "cknv_internal.h"
+
+namespace cknv {
+
+// Mean and population variance of x[0..n) (n in 1..16), x held in registers.
+__device__ __forceinline__ void mean_var16(const float (&x)[16], int n, float& mean, float& var) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += (j < n) ? x[j] : 0.f;
+  mean = s / (float)n;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float dl = x[j] - mean;
+    q += (j < n) ? dl * dl : 0.f;
+  }
+  var = q / (float)n;
+}
+
+// D̄_t = mean of the coordinate variances of group t = [t*gs, (t+1)*gs).
+__device__ __forceinline__ float group_mean(const float* cvar, int t, int gs) {
+  float s = 0.f;
+  for (int m = 0; m < gs; ++m) s += cvar[t * gs + m];
+  return s / (float)gs;
+}
+
+// One workgroup per unit, one thread per key coordinate.
+template <int D>
+__global__ __launch_bounds__(D) void append_kernel(AppendArgs a) {
+  __shared__ float cvar[D];
+  __shared__ int last;
+  const int unit = blockIdx.x, s = unit / a.H, c = threadIdx.x;
+  const int T = a.seq_len[s];
+  const long cap_tok = (long)a.cap_blocks * kBlock;
+  const bool room = T < cap_tok;
+  int b = 0, n = 0;
+  if (room) {
+    b = T / kBlock;
+    n = T - b * kBlock + 1;  // tokens in the block once the new one is in
+    const size_t tok0 = (size_t)unit * cap_tok + (size_t)b * kBlock;
+    const uint16_t* kb = a.k + tok0 * D + c;
+    const uint16_t* vb = a.v + tok0 * D + c;
+    const uint16_t nk = a.new_k[(size_t)unit * D + c];
+    const uint16_t nv = a.new_v[(size_t)unit * D + c];
+    float kx[16], vx[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bool old = j < n - 1;
+      kx[j] = old ? bf16_1(kb[(size_t)j * D]) : (j == n - 1 ? bf16_1(nk) : 0.f);
+      vx[j] = old ? bf16_1(vb[(size_t)j * D]) : (j == n - 1 ? bf16_1(nv) : 0.f);
+    }
+    a.k[(tok0 + n - 1) * D + c] = nk;
+    a.v[(tok0 + n - 1) * D + c] = nv;
+    float km, kv, vm, vv;
+    mean_var16(kx, n, km, kv);
+    mean_var16(vx, n, vm, vv);
+    const size_t row = (size_t)unit * a.cap_blocks + b;
+    a.kbar[row * D + c] = km;
+    a.vbar[row * D + c] = vm;
+    cvar[c] = kv;
+    if (c == 0) a.cnt[row] = (float)n;
+  }
+  __syncthreads();
+  if (room && c < a.r) {
+    const size_t row = (size_t)unit * a.cap_blocks + b;
+    a.dbar[row * a.r + c] = group_mean(cvar, c, D / a.r);
+  }
+  // The last head of sequence s to finish advances seq_len[s]: every head has
+  // read it by then.
+  if (last_arriver(a.ctr + s, a.H, &last) && c == 0) {
+    a.ctr[s] = 0;
+    if (room) a.seq_len[s] = T + 1;
+  }
+}
+
+// Bulk build: 256 threads = 256/D blocks per workgroup, one thread per coordinate.
+template <int D>
+__global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
+  constexpr int SLOTS = kThreads / D;
+  __shared__ float cvar[kThreads];
+  const int unit = blockIdx.y, s = unit / a.H;
+  const int slot = threadIdx.x / D, c = threadIdx.x % D;
+  const int T = a.seq_len[s];
+  const long cap_tok = (long)a.cap_blocks * kBlock;
+  int NB = (T + kBlock - 1) / kBlock;
+  NB = NB < a.max_blocks ? NB : a.max_blocks;
+  const int b = blockIdx.x * SLOTS + slot;
+  const bool valid = b < NB;
+  if (valid) {
+    const int n = (T - b * kBlock) < kBlock ? (T - b * kBlock) : kBlock;
+    const size_t tok0 = (size_t)unit * cap_tok + (size_t)b * kBlock;
+    const uint16_t* kb = a.k + tok0 * D + c;
+    const uint16_t* vb = a.v + tok0 * D + c;
+    float kx[16], vx[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      kx[j] = (j < n) ? bf16_1(kb[(size_t)j * D]) : 0.f;
+      vx[j] = (j < n) ? bf16_1(vb[(size_t)j * D]) : 0.f;
+    }
+    float km, kv, vm, vv;
+    mean_var16(kx, n, km, kv);
+    mean_var16(vx, n, vm, vv);
+    const size_t row = (size_t)unit * a.cap_blocks + b;
+    a.kbar[row * D + c] = km;
+    a.vbar[row * D + c] = vm;
+    cvar[threadIdx.x] = kv;
+    if (c == 0) a.cnt[row] = (float)n;
+  }
+  __syncthreads();
+  if (valid && c < a.r) {
+    const size_t row = (size_t)unit * a.cap_blocks + b;
+    a.dbar[row * a.r + c] = group_mean(cvar + slot * D, c, D / a.r);
+  }
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_append(int d, const AppendArgs& a, int U, hipStream_t st) {
+  void* args[] = {(void*)&a};
+  const void* f = d == 128 ? (const void*)append_kernel<128> : (const void*)append_kernel<64>;
+  return hipLaunchKernel(f, dim3(U), dim3(d), args, 0, st);
+}
+
+hipError_t launch_build(int d, const BuildArgs& a, int U, hipStream_t st) {
+  void* args[] = {(void*)&a};
+  const int slots = kThreads / d;
+  const int gx = (a.max_blocks + slots - 1) / slots;
+  const void* f = d == 128 ? (const void*)build_kernel<128> : (const void*)build_kernel<64>;
+  return hipLaunchKernel(f, dim3(gx, U), dim3(kThreads), args, 0, st);
+}
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
+  void* args[] = {(void*)&p, (void*)&n};
+  const unsigned g = (unsigned)((n + 255) / 256);
+  return hipLaunchKernel((const void*)zero_u32_kernel, dim3(g ? g : 1), dim3(256), args, 0, st);
+}
+
+}  // namespace cknv

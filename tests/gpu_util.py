@@ -1,0 +1,121 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the C-ABI
+path, compare with the fp64 oracle to the stated tolerances."""
+import math
+
+import numpy as np
+
+from block_sparse_kv_stats_amd import cknv, synth
+from oracle import compkv as ok
+
+SCORE_RTOL = 1e-4      # S_b relative tolerance
+SCORE_FLOOR = 1e-7     # ... with an absolute floor of this times max_b S_b
+TIE_BAND = 1e-5        # kept sets may differ only between blocks this close to the cut score
+OUT_RTOL_L2 = 2e-3     # relative L2 error of each query head's output
+
+
+def to_dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def upload(w: synth.Workload, data: dict, cap_blocks=None, max_blocks=None):
+    """LayerCache holding each sequence's prefill tokens (later slots zero),
+    seq_len = prefill, summaries built on the GPU."""
+    import torch
+    cb = cap_blocks or w.cap_blocks
+    shape = cknv.make_shape(w.S, w.H, w.G, w.d, w.r, cb)
+    cache = cknv.LayerCache.allocate(shape)
+    k = np.zeros((w.S, w.H, cb * 16, w.d), dtype=np.uint16)
+    v = np.zeros_like(k)
+    n = min(cb * 16, data["k"].shape[2])
+    for s, T in enumerate(data["prefill"]):
+        T = int(min(T, n))
+        k[s, :, :T] = data["k"][s, :, :T]
+        v[s, :, :T] = data["v"][s, :, :T]
+    cache.k.copy_(to_dev_bf16(k))
+    cache.v.copy_(to_dev_bf16(v))
+    cache.seq_len.copy_(torch.tensor(np.asarray(data["prefill"], dtype=np.int32)))
+    cknv.build_summaries(cache, max_blocks or cb)
+    return cache
+
+
+def new_token(data: dict, t_index):
+    """bf16 [S][H][d] of token position t_index[s] of every sequence."""
+    S = data["k"].shape[0]
+    kt = np.stack([data["k"][s, :, t_index[s]] for s in range(S)])
+    vt = np.stack([data["v"][s, :, t_index[s]] for s in range(S)])
+    return to_dev_bf16(kt), to_dev_bf16(vt)
+
+
+def check_selection(S_ref, sel_gpu, n_gpu, Kb):
+    """The GPU kept set equals the oracle's, up to swaps between blocks whose
+    fp64 scores lie within TIE_BAND (relative) of the cut score."""
+    NB = len(S_ref)
+    sel_gpu = np.asarray(sel_gpu[:n_gpu])
+    if NB <= Kb:
+        assert n_gpu == NB
+        np.testing.assert_array_equal(sel_gpu, np.arange(NB))
+        return
+    assert n_gpu == Kb
+    assert np.all(np.diff(sel_gpu) > 0), "kept list must be ascending and distinct"
+    assert {0, NB - 2, NB - 1} <= set(sel_gpu.tolist())
+    ref = ok.select_blocks(S_ref, Kb)
+    diff = set(ref.tolist()) ^ set(sel_gpu.tolist())
+    if not diff:
+        return
+    cand = np.setdiff1d(np.arange(NB), [0, NB - 2, NB - 1])
+    order = cand[np.lexsort((cand, -S_ref[cand]))]
+    cut = S_ref[order[Kb - 4]]
+    band = TIE_BAND * max(cut, 1e-300)
+    bad = [b for b in diff if abs(S_ref[b] - cut) > band]
+    assert not bad, f"kept sets differ beyond the tie band: {sorted(diff)} cut={cut} " \
+                    f"scores={[S_ref[b] for b in sorted(diff)]}"
+
+
+def check_scores(S_gpu, S_ref):
+    S_gpu = np.asarray(S_gpu, dtype=np.float64)
+    floor = SCORE_FLOOR * max(S_ref.max(initial=0.0), 1e-300)
+    err = np.abs(S_gpu - S_ref)
+    ok_ = err <= SCORE_RTOL * np.abs(S_ref) + floor
+    assert ok_.all(), f"score mismatch at {np.nonzero(~ok_)[0][:10]}: " \
+                      f"gpu={S_gpu[~ok_][:5]} ref={S_ref[~ok_][:5]}"
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.linalg.norm(a - b, axis=-1) / np.maximum(np.linalg.norm(b, axis=-1), 1e-30)
+
+
+def check_unit(w, data, s, h, T, step, q_all, sel_all, nsel_all, out_all, lse_all, scores_all,
+               budget):
+    """Compare one unit's GPU results with the oracle's from-scratch step."""
+    G = w.G
+    u = s * w.H + h
+    q = q_all[s, h * G:(h + 1) * G]
+    ref = ok.decode_step(q, data["k"][s, h], data["v"][s, h], T, w.r, budget)
+    Kb = budget // 16
+    n = int(nsel_all[u])
+    check_selection(ref["S"], sel_all[u], n, Kb)
+    if scores_all is not None:
+        NB = ok.num_blocks(T)
+        check_scores(scores_all[s, h, :NB], ref["S"])
+    # output against the oracle evaluated on the GPU's (valid) kept set
+    o_ref = ok.decode_step(q, data["k"][s, h], data["v"][s, h], T, w.r, budget,
+                           sel=np.asarray(sel_all[u][:n]))
+    err = rel_l2(out_all[s, h * G:(h + 1) * G], o_ref["o"])
+    assert np.all(err <= OUT_RTOL_L2), f"unit {u}: output rel L2 {err}"
+    lse_err = np.abs(lse_all[s, h * G:(h + 1) * G] - o_ref["lse"])
+    assert np.all(lse_err <= 1e-3 * np.maximum(1.0, np.abs(o_ref["lse"]))), lse_err
+    return err.max()
+
+
+def summaries_equal(cache, data, w, s, h, T, rtol=1e-4, atol=2e-6):
+    """GPU summary store of one unit vs the oracle's from-scratch summaries."""
+    NB = ok.num_blocks(T)
+    ref = ok.block_summaries(ok.decode_bf16(data["k"][s, h][:T]), ok.decode_bf16(data["v"][s, h][:T]),
+                             T, w.r)
+    got = (cache.cnt[s, h, :NB].cpu().numpy(), cache.kbar[s, h, :NB].cpu().numpy(),
+           cache.dbar[s, h, :NB].cpu().numpy(), cache.vbar[s, h, :NB].cpu().numpy())
+    for name, g, r in zip(("cnt", "kbar", "dbar", "vbar"), got, ref):
+        np.testing.assert_allclose(g, r, rtol=rtol, atol=atol, err_msg=name)

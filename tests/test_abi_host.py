@@ -1,0 +1,126 @@
+"""Host-side checks of libcknv: it loads, exports every entry point that
+include/cknv.h declares, and rejects bad arguments before any HIP call.
+No kernel is launched (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_kv_stats_amd import cknv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cknv.h")
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cknv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = cknv.lib()
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert cknv.status_str(code).startswith("CKNV_")
+
+
+def shape(**kw):
+    base = dict(S=1, H=8, G=4, d=128, r=4, cap_blocks=2100)
+    base.update(kw)
+    return cknv.make_shape(**base)
+
+
+def wsize(sh, max_blocks=2048, budget=512):
+    n = ctypes.c_size_t(0)
+    st = cknv.lib().cknv_workspace_size(ctypes.byref(sh), max_blocks, budget, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_valid_and_monotone():
+    st, n1 = wsize(shape())
+    assert st == cknv.OK and n1 > 0 and n1 % 256 == 0
+    st, n2 = wsize(shape(), max_blocks=2100)
+    assert st == cknv.OK and n2 >= n1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), cknv.EUNSUPPORTED), (dict(G=3), cknv.EUNSUPPORTED), (dict(r=3), cknv.EUNSUPPORTED),
+    (dict(r=256), cknv.EUNSUPPORTED), (dict(S=0), cknv.EINVAL), (dict(H=-1), cknv.EINVAL),
+    (dict(flags=1), cknv.EUNSUPPORTED)])
+def test_bad_shapes(kw, code):
+    assert wsize(shape(**kw))[0] == code
+
+
+def test_block_size_must_be_16():
+    sh = shape()
+    sh.block = 32
+    assert wsize(sh)[0] == cknv.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("mb,budget,code", [(0, 512, cknv.EINVAL), (2101, 512, cknv.ENOSPACE),
+                                            (2048, 47, cknv.EINVAL)])
+def test_bad_sizes(mb, budget, code):
+    assert wsize(shape(), mb, budget)[0] == code
+
+
+def test_too_many_blocks_for_lds_is_unsupported():
+    assert wsize(shape(cap_blocks=1 << 16), 1 << 16, 512)[0] == cknv.EUNSUPPORTED
+
+
+def cache_struct(null=None):
+    c = cknv.Cache(*([FAKE] * 7))
+    if null:
+        setattr(c, null, None)
+    return c
+
+
+@pytest.mark.parametrize("null", ["k", "v", "kbar", "dbar", "cnt", "vbar", "seq_len"])
+def test_null_cache_pointer_rejected(null):
+    sh = shape()
+    c = cache_struct(null)
+    L = cknv.lib()
+    st = L.cknv_score_select(ctypes.byref(sh), ctypes.byref(c), FAKE, 512, 2048, None, FAKE, FAKE,
+                             FAKE, 1 << 30, None)
+    assert st == cknv.EINVAL
+    assert L.cknv_build_summaries(ctypes.byref(sh), ctypes.byref(c), 2048, None) == cknv.EINVAL
+
+
+def test_entry_points_reject_before_launch():
+    sh = shape()
+    c = cache_struct()
+    L = cknv.lib()
+    _, need = wsize(sh)
+    # null outputs / query / workspace
+    assert L.cknv_score_select(ctypes.byref(sh), ctypes.byref(c), None, 512, 2048, None, FAKE,
+                               FAKE, FAKE, need, None) == cknv.EINVAL
+    assert L.cknv_score_select(ctypes.byref(sh), ctypes.byref(c), FAKE, 512, 2048, None, None,
+                               FAKE, FAKE, need, None) == cknv.EINVAL
+    # workspace too small
+    assert L.cknv_score_select(ctypes.byref(sh), ctypes.byref(c), FAKE, 512, 2048, None, FAKE,
+                               FAKE, FAKE, need - 1, None) == cknv.ENOSPACE
+    assert L.cknv_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, FAKE, FAKE, 512, 2048, FAKE,
+                         None, FAKE, need - 1, None) == cknv.ENOSPACE
+    assert L.cknv_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, None, FAKE, 512, 2048, FAKE,
+                         None, FAKE, need, None) == cknv.EINVAL
+    assert L.cknv_dense_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, 2048, 512, None, None,
+                               FAKE, need, None) == cknv.EINVAL
+    assert L.cknv_append(ctypes.byref(sh), ctypes.byref(c), None, FAKE, 2048, 512, FAKE, need,
+                         None) == cknv.EINVAL
+    assert L.cknv_append(ctypes.byref(sh), ctypes.byref(c), FAKE, FAKE, 2048, 512, FAKE, 16,
+                         None) == cknv.ENOSPACE
+    assert L.cknv_workspace_init(ctypes.byref(sh), 2048, 512, None, need, None) == cknv.EINVAL
+    # budget below the forced set, max_blocks beyond capacity
+    assert L.cknv_score_select(ctypes.byref(sh), ctypes.byref(c), FAKE, 32, 2048, None, FAKE, FAKE,
+                               FAKE, need, None) == cknv.EINVAL
+    assert L.cknv_build_summaries(ctypes.byref(sh), ctypes.byref(c), 5000, None) == cknv.ENOSPACE
+    assert L.cknv_score_select(None, ctypes.byref(c), FAKE, 512, 2048, None, FAKE, FAKE, FAKE,
+                               need, None) == cknv.EINVAL
