@@ -1,0 +1,391 @@
+#!/usr/bin/env python3
+"""CompKV decode-step benchmark on one MI355X.
+
+One step = one layer's decode step for the workload's batch: append the new
+token (and refresh its block's summary), score + select, attend (exact kept
+blocks + Mean compensation). Inputs are the seeded synthetic workload,
+resident in HBM before timing. Steps rotate over R copies of the layer
+("layers") at distinct addresses so the per-step working set cannot stay in
+the 256 MB Infinity Cache.
+
+Prints ONE JSON line. `value` = steps/s from HIP-graph replay of whole
+layer sweeps (HIP events around the timed replays). `roofline` is for the
+dominant kernel (score + select), its duration measured with HIP events on
+the launch stream. `cpu_baseline` times the fp64 oracle's per-step path on a
+bounded sample on the host.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_32k]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/sec (1 layer, B=1) at 32K/128K ctx + achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+SCORE_SOURCES = ["block_sparse_kv_stats_amd/csrc/score_select.hip",
+                 "block_sparse_kv_stats_amd/csrc/cknv_internal.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(w, T: int):
+    """Algorithmic HBM bytes of one step over all units, split by kernel.
+    score: k̄ + D̄ + |b| of every block and v̄ of the unselected blocks;
+    attend: BF16 K and V of the kept blocks' tokens."""
+    U = w.S * w.H
+    NB = math.ceil(T / 16)
+    Kb = w.Kb
+    kept = min(Kb, NB)
+    score = U * (NB * (w.d + w.r + 1) * 4 + (NB - kept) * w.d * 4)
+    open_n = T - 16 * (NB - 1)
+    kept_tokens = (kept - 1) * 16 + open_n
+    attend = U * kept_tokens * 2 * w.d * 2
+    return score, attend
+
+
+def dense_bytes(w, T: int) -> int:
+    return w.S * w.H * T * 2 * w.d * 2
+
+
+class Bench:
+    def __init__(self, w, R, appends, stream):
+        import numpy as np
+        import torch
+        from block_sparse_kv_stats_amd import cknv, synth
+
+        self.w, self.R, self.stream = w, R, stream
+        wl = w.replace(steps=max(w.steps, 1), extra_cap=appends + 16)
+        log(f"generating {w.name}")
+        data = synth.gen_layer(wl)
+        T0 = w.prefill[0]
+        cap_blocks = wl.cap_blocks
+        self.max_blocks = math.ceil((T0 + appends) / 16)
+        shape = cknv.make_shape(w.S, w.H, w.G, w.d, w.r, cap_blocks)
+        self.shape = shape
+
+        def dev_bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+        base = cknv.LayerCache.allocate(shape)
+        kk = np.zeros((w.S, w.H, cap_blocks * 16, w.d), dtype=np.uint16)
+        vv = np.zeros_like(kk)
+        kk[:, :, :T0] = data["k"][:, :, :T0]
+        vv[:, :, :T0] = data["v"][:, :, :T0]
+        base.k.copy_(dev_bf16(kk))
+        base.v.copy_(dev_bf16(vv))
+        del kk, vv
+        base.seq_len.fill_(T0)
+        cknv.build_summaries(base, self.max_blocks)
+        torch.cuda.synchronize()
+        log(f"replicating {R} layers")
+        self.layers = [base] + [cknv.LayerCache(shape, *(t.clone() for t in (
+            base.k, base.v, base.kbar, base.dbar, base.cnt, base.vbar, base.seq_len)))
+            for _ in range(R - 1)]
+        nq = w.steps if w.steps > 1 else 1
+        self.q = [torch.from_numpy(data["q"][i % nq]).cuda() for i in range(R)]
+        self.new_k = dev_bf16(data["k"][:, :, T0])
+        self.new_v = dev_bf16(data["v"][:, :, T0])
+        self.ws = cknv.allocate_workspace(shape, self.max_blocks, w.budget, stream=stream)
+        U = w.S * w.H
+        self.sel = torch.zeros((U, w.Kb), dtype=torch.int32, device="cuda")
+        self.n_sel = torch.zeros((U,), dtype=torch.int32, device="cuda")
+        self.out = torch.zeros((w.S, w.H * w.G, w.d), dtype=torch.float32, device="cuda")
+        self.lse = torch.zeros((w.S, w.H * w.G), dtype=torch.float32, device="cuda")
+        self.bound = [cknv.BoundStep(L, self.max_blocks, w.budget, self.ws, self.sel, self.n_sel,
+                                     self.out, self.lse, self.q[i], self.new_k, self.new_v, stream)
+                      for i, L in enumerate(self.layers)]
+        torch.cuda.synchronize()
+
+    def seq_len(self):
+        return int(self.layers[0].seq_len[0].item())
+
+
+class Timer:
+    """HIP-event timing on the launch stream. Before each measured region a
+    spin kernel gives the host a head start, so the queued launches run back
+    to back and host launch latency does not enter the intervals."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        e0, e1 = self.event(), self.event()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(1000)
+            e0.record(stream)
+            torch.cuda._sleep(20_000_000)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        self.cycles_per_ms = 20_000_000 / max(e0.elapsed_time(e1), 1e-3)
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def head_start(self, ms):
+        self.torch.cuda._sleep(int(self.cycles_per_ms * ms))
+
+
+def capture(torch, stream, fn):
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph_steps(torch, timer, stream, bench, steps, which="step"):
+    """ms per step over exactly `steps` steps, replaying captured layer sweeps."""
+    R = bench.R
+    full = capture(torch, stream, lambda: [getattr(b, which)() for b in bench.bound])
+    rem = steps % R
+    part = capture(torch, stream, lambda: [getattr(b, which)() for b in bench.bound[:rem]]) if rem else None
+    e0, e1 = timer.event(), timer.event()
+    with torch.cuda.stream(stream):
+        timer.head_start(5.0 + 0.02 * (steps // R + 1))
+        e0.record(stream)
+        for _ in range(steps // R):
+            full.replay()
+        if part is not None:
+            part.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_eager_steps(torch, timer, stream, bench, n):
+    e0, e1 = timer.event(), timer.event()
+    with torch.cuda.stream(stream):
+        timer.head_start(5.0 + 0.08 * n)
+        e0.record(stream)
+        for i in range(n):
+            bench.bound[i % bench.R].step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def time_kernel_events(torch, timer, stream, bench, n, which):
+    """Average and median duration (ms) of one entry point's launch inside
+    full decode steps, bracketed by HIP events on the launch stream."""
+    evs = [(timer.event(), timer.event()) for _ in range(n)]
+    with torch.cuda.stream(stream):
+        timer.head_start(5.0 + 0.12 * n)
+        for i in range(n):
+            b = bench.bound[i % bench.R]
+            b.append()
+            if which == "attend":
+                b.score_select()
+            evs[i][0].record(stream)
+            getattr(b, which)()
+            evs[i][1].record(stream)
+            if which == "score_select":
+                b.attend()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(c) for a, c in evs)
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def cpu_baseline(w, seconds: float):
+    """The fp64 oracle's per-step path (open-block update, score, select,
+    attend) for one (sequence, KV head) unit, single thread, scaled to a step
+    over all units."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from block_sparse_kv_stats_amd import synth
+    from oracle import compkv as ok
+
+    n_max = 4000
+    u = synth.gen_unit(w.replace(steps=max(w.steps, 1), extra_cap=n_max), 0, 0,
+                       ntok=w.prefill[0] + n_max)
+    T0 = w.prefill[0]
+    q = u["q"][0]
+    with threadpool_limits(limits=1):
+        su = ok.StreamingUnit(u["k"], u["v"], T0, w.r, cap_tokens=T0 + n_max)
+        t0 = time.perf_counter()
+        n = 0
+        while n < n_max:
+            su.append(u["k"][T0 + n], u["v"][T0 + n])
+            su.step(q, w.budget)
+            n += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        dt = time.perf_counter() - t0
+    per_unit = dt / n
+    U = w.S * w.H
+    return {"value": 1.0 / (per_unit * U), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} consecutive steps of one (sequence, KV head) unit of {w.name} "
+                      f"({dt:.1f} s, fp64 NumPy, 1 thread), scaled x{U} units per step"}
+
+
+def traffic_from_profile(workload, launches_bytes):
+    """HBM bytes per score launch from a committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"score_select_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(SCORE_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_workload(torch, timer, wname, args, stream, want_dense=True):
+    from block_sparse_kv_stats_amd import synth
+
+    w = synth.WORKLOADS[wname]
+    sb, ab = step_bytes(w, w.prefill[0] + 1)
+    R = args.layers or max(4, math.ceil(2 * MALL_BYTES / (sb + ab)))
+    steps, warm = args.steps, args.warmup
+    n_e = min(steps, 256)
+    kernel_n = min(max(2 * R, 64), 256)
+    appends = (math.ceil(warm / R) + math.ceil(steps / R) + math.ceil(n_e / R)
+               + 2 * math.ceil(kernel_n / R) + 4)
+    bench = Bench(w, R, appends, stream)
+    log(f"{wname}: {R} layers, {warm} warm-up + {steps} timed steps")
+    with torch.cuda.stream(stream):
+        for i in range(warm):
+            bench.bound[i % R].step()
+    torch.cuda.synchronize()
+    ms_step = time_graph_steps(torch, timer, stream, bench, steps)
+    ms_eager = time_eager_steps(torch, timer, stream, bench, n_e)
+    k_avg, k_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "score_select")
+    a_avg, a_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "attend")
+    T = bench.seq_len()
+    sb, ab = step_bytes(w, T)
+    res = {"w": w, "R": R, "steps": steps, "warmup": warm, "ms_step": ms_step,
+           "ms_eager": ms_eager, "T": T, "score_bytes": sb, "attend_bytes": ab,
+           "score_ms": k_avg, "score_ms_median": k_med, "attend_ms": a_avg}
+    if want_dense:
+        res["dense_ms_step"] = time_graph_steps(torch, timer, stream, bench, max(R, steps // 4),
+                                                which="dense")
+        res["dense_bytes"] = dense_bytes(w, bench.seq_len())
+    del bench
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_probe(nbytes: int, reps: int):
+    """A plain device copy of known size (calibrates the rocprofv3 byte counters)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--also", default="qwen8b_128k", help="second workload reported beside ('' = none)")
+    ap.add_argument("--layers", type=int, default=0, help="layer copies to rotate over (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, help="run only a device copy of this many bytes")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 5)
+        return
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    timer = Timer(torch, stream)
+
+    main_res = run_workload(torch, timer, args.workload, args, stream, want_dense=not args.no_dense)
+    extra = None
+    if args.also and args.also != args.workload:
+        extra = run_workload(torch, timer, args.also, args, stream, want_dense=not args.no_dense)
+
+    w = main_res["w"]
+    value = 1000.0 / main_res["ms_step"]
+    score_gbps = main_res["score_bytes"] / (main_res["score_ms"] * 1e-3) / 1e9
+    step_gbps = (main_res["score_bytes"] + main_res["attend_bytes"]) / (main_res["ms_step"] * 1e-3) / 1e9
+    traffic = traffic_from_profile(args.workload, main_res["score_bytes"])
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": main_res["steps"],
+        "warmup": main_res["warmup"],
+        "ms_per_step": round(main_res["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 KV, fp32 summaries)",
+        "data": "synthetic (seeded generator: block-structured bf16 keys, 1% needles, N(0,1) values)",
+        "config": {"workload": w.name, "S": w.S, "H": w.H, "G": w.G, "d": w.d, "r": w.r,
+                   "context_tokens": main_res["T"], "budget_tokens": w.budget,
+                   "layers_rotated": main_res["R"], "launch": "hipGraph replay of layer sweeps"},
+        "step_GBps": round(step_gbps, 1),
+        "eager_ms_per_step": round(main_res["ms_eager"], 5),
+        "roofline": {"bound": "hbm", "kernel": "score_select",
+                     "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": main_res["score_bytes"],
+                     "avg_launch_us": round(main_res["score_ms"] * 1e3, 3)},
+        "attend_kernel": {"avg_launch_us": round(main_res["attend_ms"] * 1e3, 3),
+                          "algorithmic_bytes_per_launch": main_res["attend_bytes"]},
+    }
+    if "dense_ms_step" in main_res:
+        line["dense_baseline"] = {
+            "steps_per_s": round(1000.0 / main_res["dense_ms_step"], 2),
+            "GBps": round(main_res["dense_bytes"] / (main_res["dense_ms_step"] * 1e-3) / 1e9, 1),
+            "speedup_of_compkv": round(main_res["dense_ms_step"] / main_res["ms_step"], 3)}
+    if extra is not None:
+        we = extra["w"]
+        e_score = extra["score_bytes"] / (extra["score_ms"] * 1e-3) / 1e9
+        line["also"] = {
+            "workload": we.name, "steps_per_s": round(1000.0 / extra["ms_step"], 2),
+            "ms_per_step": round(extra["ms_step"], 5), "context_tokens": extra["T"],
+            "layers_rotated": extra["R"],
+            "step_GBps": round((extra["score_bytes"] + extra["attend_bytes"]) / (extra["ms_step"] * 1e-3) / 1e9, 1),
+            "score_kernel_GBps": round(e_score, 1), "score_frac": round(e_score / PEAK_HBM_GBPS, 4),
+            "score_avg_launch_us": round(extra["score_ms"] * 1e3, 3)}
+        if "dense_ms_step" in extra:
+            line["also"]["dense_steps_per_s"] = round(1000.0 / extra["dense_ms_step"], 2)
+            line["also"]["speedup_of_compkv"] = round(extra["dense_ms_step"] / extra["ms_step"], 3)
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,7 +44,7 @@ SZ = ctypes.c_size_t
 SIGNATURES = {
     "cknv_workspace_size": [ctypes.POINTER(Shape), I32, I32, ctypes.POINTER(SZ)],
     "cknv_workspace_init": [ctypes.POINTER(Shape), I32, I32, P, SZ, P],
-    "cknv_append": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, I32, I32, P, SZ, P],
+    "cknv_append": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P],
     "cknv_build_summaries": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), I32, P],
     "cknv_score_select": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, I32, I32, P, P, P, P,
                           SZ, P],
@@ -165,15 +165,14 @@ def allocate_workspace(shape: Shape, max_blocks: int, budget: int, device="cuda"
     return ws
 
 
-def append(cache: LayerCache, new_k, new_v, max_blocks: int, budget: int, ws, stream=None):
+def append(cache: LayerCache, new_k, new_v, stream=None):
     import torch
     s = cache.shape
     n = s.S * s.H * s.d
     bf = (torch.bfloat16, torch.int16, torch.uint16)
     c = cache.c_struct()
     _check(lib().cknv_append(ctypes.byref(s), ctypes.byref(c), _ptr(new_k, bf, n, "new_k"),
-                             _ptr(new_v, bf, n, "new_v"), max_blocks, budget,
-                             _ptr(ws, what="ws"), ws.numel(), _stream(stream)), "cknv_append")
+                             _ptr(new_v, bf, n, "new_v"), _stream(stream)), "cknv_append")
 
 
 def build_summaries(cache: LayerCache, max_blocks: int, stream=None):
@@ -248,7 +247,7 @@ class DecodeStep:
 
     def __call__(self, q, new_k=None, new_v=None, stream=None):
         if new_k is not None:
-            append(self.cache, new_k, new_v, self.max_blocks, self.budget, self.ws, stream)
+            append(self.cache, new_k, new_v, stream)
         score_select(self.cache, q, self.budget, self.max_blocks, self.sel, self.n_sel, self.ws,
                      self.scores, stream)
         attend(self.cache, q, self.sel, self.n_sel, self.budget, self.max_blocks, self.out,
@@ -258,3 +257,61 @@ class DecodeStep:
 
 def blocks_for(tokens: int) -> int:
     return int(math.ceil(tokens / BLOCK))
+
+
+class BoundStep:
+    """Pre-marshalled arguments of one layer's decode step (append, score/select,
+    attend) on a fixed stream, so that issuing a step is three foreign calls.
+    The tensors passed in must stay alive while this object is used."""
+
+    def __init__(self, cache: LayerCache, max_blocks: int, budget: int, ws, sel, n_sel, out,
+                 lse, q, new_k, new_v, stream, scores=None):
+        import torch
+        s = cache.shape
+        L = lib()
+        self._keep = (cache, ws, sel, n_sel, out, lse, q, new_k, new_v, scores)
+        self.shape = ctypes.byref(s)
+        self.cache_c = cache.c_struct()
+        cp = ctypes.byref(self.cache_c)
+        st = _stream(stream)
+        w, wn = _ptr(ws, what="ws"), ws.numel()
+        qp = _ptr(q, (torch.float32,), s.S * s.H * s.G * s.d, "q")
+        bf = (torch.bfloat16, torch.int16, torch.uint16)
+        self.append_args = (self.shape, cp, _ptr(new_k, bf, s.S * s.H * s.d, "new_k"),
+                            _ptr(new_v, bf, s.S * s.H * s.d, "new_v"), st)
+        self.score_args = (self.shape, cp, qp, budget, max_blocks,
+                           _ptr(scores, (torch.float32,), s.S * s.H * s.cap_blocks, "scores"),
+                           _ptr(sel, (torch.int32,), s.S * s.H * (budget // BLOCK), "sel"),
+                           _ptr(n_sel, (torch.int32,), s.S * s.H, "n_sel"), w, wn, st)
+        self.attend_args = (self.shape, cp, qp, self.score_args[6], self.score_args[7], budget,
+                            max_blocks, _ptr(out, (torch.float32,), s.S * s.H * s.G * s.d, "out"),
+                            _ptr(lse, (torch.float32,), s.S * s.H * s.G, "lse"), w, wn, st)
+        self.dense_args = (self.shape, cp, qp, max_blocks, budget, self.attend_args[7],
+                           self.attend_args[8], w, wn, st)
+        self._append, self._score = L.cknv_append, L.cknv_score_select
+        self._attend, self._dense = L.cknv_attend, L.cknv_dense_attend
+
+    def append(self):
+        st = self._append(*self.append_args)
+        if st:
+            raise CknvError(st, "cknv_append")
+
+    def score_select(self):
+        st = self._score(*self.score_args)
+        if st:
+            raise CknvError(st, "cknv_score_select")
+
+    def attend(self):
+        st = self._attend(*self.attend_args)
+        if st:
+            raise CknvError(st, "cknv_attend")
+
+    def dense(self):
+        st = self._dense(*self.dense_args)
+        if st:
+            raise CknvError(st, "cknv_dense_attend")
+
+    def step(self):
+        self.append()
+        self.score_select()
+        self.attend()

@@ -39,20 +39,19 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   q.NBmax = max_blocks;
   q.NG = (max_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
   q.Kb = budget_tokens / kBlock;
-  const int iters = (max_blocks + kBlocksPerIter - 1) / kBlocksPerIter;
-  q.C = iters < kMaxChunks ? iters : kMaxChunks;
-  const int ipc = (iters + q.C - 1) / q.C;
-  q.BPC = ipc * kBlocksPerIter;
-  q.C = (max_blocks + q.BPC - 1) / q.BPC;
-  q.P = (q.Kb + kWaves - 1) / kWaves;
-  const int want = (kDenseTargetWGs + q.U - 1) / q.U;
-  const int most = (max_blocks + kWaves - 1) / kWaves;
-  q.Pd = want < most ? want : most;
-  if (q.Pd < 1) q.Pd = 1;
-  const size_t W = (size_t)d + 2;
+  q.C = (max_blocks + kBlocksPerWG - 1) / kBlocksPerWG;
+  const int per_wg = kWaves * 2;  // kept blocks per attend workgroup
+  q.P = (q.Kb + per_wg - 1) / per_wg;
+  const int pc = (q.C + kMaxChunksPerAttendWG - 1) / kMaxChunksPerAttendWG;
+  q.P = q.P > pc ? q.P : pc;
+  int bpw = (max_blocks + kDenseMaxWGs - 1) / kDenseMaxWGs;
+  bpw = bpw > kDenseBlocksPerWG ? bpw : kDenseBlocksPerWG;
+  q.BPW = bpw;
+  q.Pd = (max_blocks + bpw - 1) / bpw;
+  const size_t W = (size_t)rec_words(d);
   size_t off = 0;
   q.off_ctr = off;
-  q.n_ctr = (size_t)kCtrRows * (size_t)(q.U > sh->S ? q.U : sh->S);
+  q.n_ctr = (size_t)kCtrRows * (size_t)q.U;
   off = align256(off + q.n_ctr * 4);
   q.off_grp = off;
   off = align256(off + (size_t)q.U * q.NG * G * 2 * 4);
@@ -65,10 +64,8 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   q.off_dense = off;
   off = align256(off + (size_t)q.U * q.Pd * G * W * 4);
   q.total = off;
-  const size_t main_lds = ((size_t)G * d + (size_t)G * r + (size_t)kWaves * 16 * G + (size_t)kWaves * G * W) * 4;
-  const size_t kp = (size_t)max_blocks + (size_t)max_blocks / 32 + 2;
-  const size_t tail_lds = kp * 4 + (size_t)q.NG * G * 4 + ((size_t)kWaves * G * 2 + G + 3) * 4 + 256 * 4 + 16 * 4;
-  q.score_lds = main_lds > tail_lds ? main_lds : tail_lds;
+  if (max_blocks > kThreads * kScoreKeysPerThread) return CKNV_EUNSUPPORTED;
+  q.score_lds = score_lds_bytes(d, G, max_blocks);
   if (q.score_lds > kMaxLds) return CKNV_EUNSUPPORTED;
   *p = q;
   return CKNV_OK;
@@ -108,18 +105,14 @@ int cknv_workspace_init(const cknv_shape* shape, int32_t max_blocks, int32_t bud
 }
 
 int cknv_append(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
-                const uint16_t* new_v, int32_t max_blocks, int32_t budget_tokens, void* ws,
-                size_t ws_bytes, void* stream) {
-  Plan p;
-  int st = make_plan(shape, max_blocks, budget_tokens, &p);
+                const uint16_t* new_v, void* stream) {
+  int st = check_shape(shape);
   if (st) return st;
   if ((st = check_cache(cache))) return st;
-  if (!new_k || !new_v || !ws) return CKNV_EINVAL;
-  if (ws_bytes < p.total) return CKNV_ENOSPACE;
+  if (!new_k || !new_v) return CKNV_EINVAL;
   AppendArgs a{cache->k, cache->v, cache->kbar, cache->dbar, cache->cnt, cache->vbar,
-               cache->seq_len, new_k, new_v, ctr_row(ws, p, kCtrAppend),
-               shape->S, shape->H, shape->r, shape->cap_blocks};
-  return hip_status(launch_append(shape->d, a, p.U, (hipStream_t)stream));
+               cache->seq_len, new_k, new_v, shape->S, shape->H, shape->r, shape->cap_blocks};
+  return hip_status(launch_append(shape->d, a, (hipStream_t)stream));
 }
 
 int cknv_build_summaries(const cknv_shape* shape, const cknv_cache* cache, int32_t max_blocks,
@@ -153,7 +146,7 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   a.u = reinterpret_cast<float*>(w + p.off_u);
   a.comp = reinterpret_cast<float*>(w + p.off_comp);
   a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
-  a.max_blocks = max_blocks; a.NG = p.NG; a.Kb = p.Kb; a.C = p.C; a.BPC = p.BPC;
+  a.max_blocks = max_blocks; a.NG = p.NG; a.Kb = p.Kb; a.C = p.C;
   a.xcd = (p.U % 8) == 0;
   a.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_score(shape->d, shape->G, a, p.U, p.score_lds, (hipStream_t)stream));
@@ -179,7 +172,7 @@ static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const
   a.comp = reinterpret_cast<const float*>(w + p.off_comp);
   a.part = reinterpret_cast<float*>(w + (dense ? p.off_dense : p.off_attp));
   a.S = shape->S; a.H = shape->H; a.cap_blocks = shape->cap_blocks; a.max_blocks = max_blocks;
-  a.Kb = p.Kb; a.C = p.C; a.P = dense ? p.Pd : p.P;
+  a.Kb = p.Kb; a.C = p.C; a.P = dense ? p.Pd : p.P; a.BPW = p.BPW;
   a.xcd = (p.U % 8) == 0;
   a.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_attend(shape->d, shape->G, dense, a, p.U, (hipStream_t)stream));

@@ -7,232 +7,452 @@
 // the normaliser and |b| e^{z̄_b} v̄_b to the value sum; kept blocks use
 // their tokens' exact terms, and both parts are normalised together.
 //
-// The score kernel already summed the compensation of ALL blocks per chunk;
-// here each workgroup p of a unit
-//   * adds the exact terms of its slice of the kept list (one wave per block:
-//     16 tokens x d BF16 keys and values, 4 tokens per wave instruction),
-//   * subtracts the kept blocks' own compensation terms |b| e^{z̄_b}(1, v̄_b),
-//   * folds in its share of the score kernel's chunk sums,
-// and the unit's last workgroup merges the P partials into out and lse.
+// The score kernel already summed the compensation of ALL blocks, per
+// 64-block chunk. Here workgroup p of a unit
+//   * adds the exact terms of its slice of the kept list (each wave two
+//     blocks: 16 tokens x d BF16 keys and values, 4 tokens per load),
+//   * subtracts those blocks' own compensation terms |b| e^{z̄_b}(1, v̄_b),
+//   * folds in up to 8 of the score kernel's chunk records,
+// and the unit's last workgroup merges the P records into out and lse.
 // Subtracting is safe in FP32: a kept block's exact mass sum_i e^{z_i} is at
 // least its compensation mass |b| e^{z̄_b} (Jensen), so the final normaliser
 // is at least the sum of all compensation masses and the rounding error of
 // the subtraction stays relative to the result.
 //
-// DENSE = true is the full-attention baseline: every block exact, no
-// compensation.
+// dense_kernel is the full-attention baseline: every block exact, no
+// compensation, a contiguous block range per workgroup.
 #include "cknv_internal.h"
 
 namespace cknv {
 
-template <int D, int G, bool DENSE>
+namespace {
+
+constexpr int kBlocksPerAttendWave = 2;
+
+// Running softmax state of one wave for the G query heads. Lane l owns value
+// coordinates [l*VPL, l*VPL+VPL) (VPL = d/64) summed over every token it has
+// absorbed; m and l are wave-uniform.
+template <int D, int G>
+struct WaveState {
+  static constexpr int VPL = D / 64;
+  float m[G], l[G], acc[G][VPL];
+  __device__ void init() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) acc[g][e] = 0.f;
+    }
+  }
+};
+
+// One block's BF16 tokens. Keys: token t = 4*m + tq, lane covers coordinates
+// [cc*EPL, +EPL) (16 lanes per token, 4 tokens per load). Values: every lane
+// loads its VPL coordinates of all 16 tokens. Tokens at or past T load as 0.
+template <int D>
+struct Tile {
+  static constexpr int EPL = D / 16, VPL = D / 64;
+  uint32_t k[4][EPL / 2];
+  uint32_t v[16];  // d=128: 2 bf16 (one word) per token; d=64: 1 bf16 in the low half
+  bool tv[4];
+  int nt;          // valid tokens
+  __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
+    const int tq = lane >> 4, cc = lane & 15;
+    const long left = T - tok0;
+    nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = 4 * m + tq;
+      tv[m] = t < nt;
+      const size_t off = (size_t)(tok0 + t) * D + cc * EPL;
+      if (EPL == 8) {
+        const uint4 kk = tv[m] ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
+        k[m][0] = kk.x; k[m][1] = kk.y; k[m][2] = kk.z; k[m][3] = kk.w;
+      } else {
+        const uint2 kk = tv[m] ? *reinterpret_cast<const uint2*>(kc + off) : make_uint2(0, 0);
+        k[m][0] = kk.x; k[m][1] = kk.y;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const size_t off = (size_t)(tok0 + t) * D + lane * VPL;
+      if (VPL == 2)
+        v[t] = t < nt ? *reinterpret_cast<const uint32_t*>(vc + off) : 0u;
+      else
+        v[t] = t < nt ? (uint32_t)vc[off] : 0u;
+    }
+  }
+};
+
+// Mean-compensation inputs of one kept block (to be subtracted): the lane's
+// VPL coordinates of k̄ and v̄, and |b|.
+template <int D>
+struct BlockMean {
+  static constexpr int VPL = D / 64;
+  float kb[VPL], vb[VPL], n;
+  __device__ void load(const float* kbar_row, const float* vbar_row, const float* cnt, int lane) {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) {
+      kb[e] = kbar_row[lane * VPL + e];
+      vb[e] = vbar_row[lane * VPL + e];
+    }
+    n = *cnt;
+  }
+};
+
+// p of token 4*m + R (held by the lanes of row R) for R = 0..3, in every lane.
+__device__ __forceinline__ void spread_rows(float x, float& r0, float& r1, float& r2, float& r3) {
+  float b;
+  const float a = swap16_lo(x, b);  // a: rows 0,0,2,2   b: rows 1,1,3,3
+  r0 = swap32_lo(a, r2);
+  r1 = swap32_lo(b, r3);
+}
+
+// Add one block's exact terms (and, with COMP, remove its compensation terms).
+template <int D, int G, bool COMP>
+__device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, const BlockMean<D>& bm,
+                                       const float* q_l, int lane, float isd) {
+  constexpr int EPL = D / 16, VPL = D / 64;
+  const int cc = lane & 15;
+  float zbar[G];
+  if (COMP) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float zp = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) zp += bm.kb[e] * q_l[g * D + lane * VPL + e];
+      zbar[g] = group_sum<64>(zp) * isd;
+    }
+  }
+  float z[4][G];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float kf[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL / 2; ++e) { kf[2 * e] = bf16_lo(t.k[m][e]); kf[2 * e + 1] = bf16_hi(t.k[m][e]); }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float zp = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) zp += kf[e] * q_l[g * D + cc * EPL + e];
+      zp = group_sum<16>(zp) * isd;
+      z[m][g] = t.tv[m] ? zp : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float bmax = fmaxf(fmaxf(z[0][g], z[1][g]), fmaxf(z[2][g], z[3][g]));
+    bmax = rows_max(bmax);
+    if (COMP) bmax = fmaxf(bmax, zbar[g]);
+    const float M = fmaxf(st.m[g], bmax);
+    const float sc = rescale(st.m[g], M);
+    float l = st.l[g] * sc;
+    float acc[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) acc[e] = st.acc[g][e] * sc;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float pz = t.tv[m] ? __expf(z[m][g] - M) : 0.f;
+      float p[4];
+      spread_rows(pz, p[0], p[1], p[2], p[3]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t vw = t.v[4 * m + q];
+        l += p[q];
+        if (VPL == 2) {
+          acc[0] += p[q] * bf16_lo(vw);
+          acc[1 % VPL] += p[q] * bf16_hi(vw);
+        } else {
+          acc[0] += p[q] * bf16_lo(vw);
+        }
+      }
+    }
+    if (COMP) {
+      const float w = bm.n * __expf(zbar[g] - M);
+      l -= w;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) acc[e] -= w * bm.vb[e];
+    }
+    st.m[g] = M;
+    st.l[g] = l;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) st.acc[g][e] = acc[e];
+  }
+}
+
+// Write the wave's record [m, l, 0, 0, acc[D]] per g.
+template <int D, int G>
+__device__ __forceinline__ void store_wave_record(const WaveState<D, G>& st, float* rec, int lane) {
+  constexpr int VPL = D / 64, W = rec_words(D);
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) rec[g * W + 4 + lane * VPL + e] = st.acc[g][e];
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      rec[g * W] = st.m[g];
+      rec[g * W + 1] = st.l[g];
+      rec[g * W + 2] = 0.f;
+      rec[g * W + 3] = 0.f;
+    }
+  }
+}
+
+// Per query head g of n records (LDS, G x W words each): M = max of m_i,
+// the factors e^{m_i - M} into scl[i*G + g], and L = sum_i l_i e^{m_i - M}
+// (starting from a running (M0, L0), whose factor goes to *s0).
+template <int D, int G>
+__device__ __forceinline__ void record_scales(const float* recs, int n, int g, float* scl, float& M,
+                                              float& L, float* s0) {
+  constexpr int W = rec_words(D);
+  float MM = M;
+  for (int i = 0; i < n; ++i) MM = fmaxf(MM, recs[(i * G + g) * W]);
+  const float so = rescale(M, MM);
+  float LL = L * so;
+  for (int i = 0; i < n; ++i) {
+    const float f = rescale(recs[(i * G + g) * W], MM);
+    scl[i * G + g] = f;
+    LL += recs[(i * G + g) * W + 1] * f;
+  }
+  if (s0) *s0 = so;
+  M = MM;
+  L = LL;
+}
+
+// sum_i recs[i][g][4 + c] * scl[i][g] over n records, four at a time.
+template <int D, int G>
+__device__ __forceinline__ float record_column(const float* recs, const float* scl, int n, int g, int c) {
+  constexpr int W = rec_words(D);
+  float A = 0.f;
+  int i = 0;
+#pragma unroll 1
+  for (; i + 4 <= n; i += 4) {
+    float x[4], f[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = recs[((i + k) * G + g) * W + 4 + c];
+      f[k] = scl[(i + k) * G + g];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) A += x[k] * f[k];
+  }
+  for (; i < n; ++i) A += recs[(i * G + g) * W + 4 + c] * scl[i * G + g];
+  return A;
+}
+
+// Merge n records of G x W words (LDS, consecutive) into one record at dst
+// (global). `scl` is LDS scratch of n*G floats.
+template <int D, int G>
+__device__ __forceinline__ void merge_records(const float* recs, int n, float* dst, float* scl) {
+  constexpr int W = rec_words(D);
+  const int tid = threadIdx.x;
+  if (tid < G) {
+    float M = -INFINITY, L = 0.f;
+    record_scales<D, G>(recs, n, tid, scl, M, L, nullptr);
+    dst[tid * W] = M;
+    dst[tid * W + 1] = L;
+    dst[tid * W + 2] = 0.f;
+    dst[tid * W + 3] = 0.f;
+  }
+  __syncthreads();
+  for (int col = tid; col < G * D; col += kThreads) {
+    const int g = col / D, c = col - g * D;
+    dst[g * W + 4 + c] = record_column<D, G>(recs, scl, n, g, c);
+  }
+}
+
+template <int G>
+constexpr int stage_cap() { return G <= 4 ? 24 : 12; }
+
+// Copy n <= stage_cap records (G x W words each, 16-byte aligned) from global
+// to LDS; every load is issued before the first LDS store.
+template <int D, int G>
+__device__ __forceinline__ void stage_records(const float* src, int n, float* lds_dst) {
+  constexpr int W4 = rec_words(D) / 4;
+  constexpr int NBUF = (stage_cap<G>() * G * W4 + kThreads - 1) / kThreads;
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+  float4* d4 = reinterpret_cast<float4*>(lds_dst);
+  const int total = n * G * W4;
+  float4 buf[NBUF];
+#pragma unroll
+  for (int k = 0; k < NBUF; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    buf[k] = i < total ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < NBUF; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    if (i < total) d4[i] = buf[k];
+  }
+}
+
+// The unit's last workgroup: merge its P part records into out and lse.
+// `stage` holds `cap` records of LDS, `scl` cap*G + 3*G floats.
+template <int D, int G>
+__device__ void finish_unit(const float* parts, int P, float* out, float* lse, float* stage,
+                            int cap, float* scl) {
+  constexpr int W = rec_words(D);
+  constexpr int COLS = (G * D + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  float* Mrun = scl + cap * G;  // [G] running max
+  float* Lrun = Mrun + G;       // [G] running normaliser
+  float* Srun = Lrun + G;       // [G] factor applied to the running sums this round
+  float Ar[COLS];
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) Ar[k] = 0.f;
+  if (tid < G) { Mrun[tid] = -INFINITY; Lrun[tid] = 0.f; }
+  for (int p0 = 0; p0 < P; p0 += cap) {
+    const int n = P - p0 < cap ? P - p0 : cap;
+    stage_records<D, G>(parts + (size_t)p0 * G * W, n, stage);
+    __syncthreads();
+    if (tid < G) {
+      float M = Mrun[tid], L = Lrun[tid];
+      record_scales<D, G>(stage, n, tid, scl, M, L, Srun + tid);
+      Mrun[tid] = M;
+      Lrun[tid] = L;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < COLS; ++k) {
+      const int col = tid + k * kThreads;
+      if (col < G * D) {
+        const int g = col / D, c = col - g * D;
+        Ar[k] = Ar[k] * Srun[g] + record_column<D, G>(stage, scl, n, g, c);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) {
+    const int col = tid + k * kThreads;
+    if (col < G * D) {
+      const int g = col / D, c = col - g * D;
+      const float L = Lrun[g];
+      const bool ok = L > 0.f;
+      out[col] = ok ? Ar[k] / L : 0.f;
+      if (c == 0 && lse) lse[g] = ok ? Mrun[g] + __logf(L) : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+template <int D, int G>
 __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
-  constexpr int EPL = D / 16;  // BF16 elements per lane per token (16 lanes per token)
-  constexpr int W = D + 2;
+  constexpr int W = rec_words(D);
+  constexpr int CAP = stage_cap<G>();
+  static_assert(CAP >= kWaves + kMaxChunksPerAttendWG, "record staging too small");
   __shared__ __align__(16) float q_l[G * D];
-  __shared__ float cmb[kWaves * G * W];
+  __shared__ __align__(16) float recs[CAP * G * W];
+  __shared__ float scl[CAP * G + 3 * G];
   __shared__ int last;
 
   int unit, p;
   map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
   const int s = unit / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // ---- round 1: context length, kept count, this wave's kept indices, the
+  // query, this workgroup's share of the score kernel's chunk records
   const int T = a.seq_len[s];
+  const int nk = a.n_sel[unit];
+  int bidx[kBlocksPerAttendWave];
+#pragma unroll
+  for (int i = 0; i < kBlocksPerAttendWave; ++i) {
+    const int it = (p * kWaves + wave) * kBlocksPerAttendWave + i;
+    bidx[i] = it < a.Kb ? a.sel[(size_t)unit * a.Kb + it] : -1;
+    bidx[i] = it < nk ? bidx[i] : -1;
+  }
+  static_assert(G * D / 4 <= kThreads, "one float4 of q per thread");
+  const float4 qv = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : G * D / 4 - 1];
+  const int c0 = (int)((long)p * a.C / a.P), c1 = (int)((long)(p + 1) * a.C / a.P);
+  stage_records<D, G>(a.comp + ((size_t)unit * a.C + c0) * G * W, c1 - c0, recs + kWaves * G * W);
+  if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
+  __syncthreads();
+
+  // ---- round 2: the kept blocks' tokens, mean key and value
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < a.max_blocks ? NB : a.max_blocks;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* qg = a.q + (size_t)unit * G * D;
-  for (int i = tid; i < G * D; i += kThreads) q_l[i] = qg[i];
-  __syncthreads();
-
-  const int tq = lane >> 4, cc = lane & 15;
   const long cap_tok = (long)a.cap_blocks * kBlock;
   const size_t ubase = (size_t)unit * a.cap_blocks;
-
-  int i0, i1;
-  if (DENSE) {
-    i0 = (int)((long)p * NB / a.P);
-    i1 = (int)((long)(p + 1) * NB / a.P);
-  } else {
-    int n = a.n_sel[unit];
-    n = n < a.Kb ? n : a.Kb;
-    i0 = (int)((long)p * n / a.P);
-    i1 = (int)((long)(p + 1) * n / a.P);
+  const uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
+  const uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
+  Tile<D> tile[kBlocksPerAttendWave];
+  BlockMean<D> bm[kBlocksPerAttendWave];
+  bool use[kBlocksPerAttendWave];
+#pragma unroll
+  for (int i = 0; i < kBlocksPerAttendWave; ++i) {
+    use[i] = bidx[i] >= 0 && bidx[i] < NB;
+    const int b = use[i] ? bidx[i] : 0;
+    tile[i].load(kc, vc, (long)b * kBlock, use[i] ? (long)T : 0, lane);
+    if (use[i]) bm[i].load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
   }
-
-  float mr[G], lr[G], acc[G][EPL];
+  WaveState<D, G> st;
+  st.init();
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    mr[g] = -INFINITY;
-    lr[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  }
-
-  for (int it = i0 + wave; it < i1; it += kWaves) {
-    const int b = DENSE ? it : a.sel[(size_t)unit * a.Kb + it];
-    if (b < 0 || b >= NB) continue;  // uniform over the wave
-    const long tok0 = (long)b * kBlock;
-    // ---- K and V tiles: token t = 4*m + tq, lane covers coordinates [cc*EPL, +EPL)
-    uint32_t kr[4][EPL / 2], vr[4][EPL / 2];
-    bool tv[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = 4 * m + tq;
-      tv[m] = tok0 + t < T;
-      const size_t off = ((size_t)unit * cap_tok + tok0 + t) * D + cc * EPL;
-      if (EPL == 8) {
-        const uint4 z4 = make_uint4(0, 0, 0, 0);
-        const uint4 kk = tv[m] ? *reinterpret_cast<const uint4*>(a.k + off) : z4;
-        const uint4 vv = tv[m] ? *reinterpret_cast<const uint4*>(a.v + off) : z4;
-        kr[m][0] = kk.x; kr[m][1] = kk.y; kr[m][2] = kk.z; kr[m][3] = kk.w;
-        vr[m][0] = vv.x; vr[m][1] = vv.y; vr[m][2] = vv.z; vr[m][3] = vv.w;
-      } else {
-        const uint2 z2 = make_uint2(0, 0);
-        const uint2 kk = tv[m] ? *reinterpret_cast<const uint2*>(a.k + off) : z2;
-        const uint2 vv = tv[m] ? *reinterpret_cast<const uint2*>(a.v + off) : z2;
-        kr[m][0] = kk.x; kr[m][1] = kk.y;
-        vr[m][0] = vv.x; vr[m][1] = vv.y;
-      }
-    }
-    float zbar[G], nb = 0.f;
-    float vb[EPL];
-    if (!DENSE) {
-      // block-mean logit from k̄ (D/64 floats per lane, whole-wave reduce)
-      constexpr int PL = D / 64;
-      float kb[PL];
-#pragma unroll
-      for (int e = 0; e < PL; ++e) kb[e] = a.kbar[(ubase + b) * D + lane * PL + e];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float zp = 0.f;
-#pragma unroll
-        for (int e = 0; e < PL; ++e) zp += kb[e] * q_l[g * D + lane * PL + e];
-        zbar[g] = xsum<1, 64>(zp) * a.isd;
-      }
-      nb = a.cnt[ubase + b];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) vb[e] = a.vbar[(ubase + b) * D + cc * EPL + e];
-    }
-    // ---- logits
-    float z[4][G];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      float kf[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL / 2; ++e) { kf[2 * e] = bf16_lo(kr[m][e]); kf[2 * e + 1] = bf16_hi(kr[m][e]); }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float zp = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) zp += kf[e] * q_l[g * D + cc * EPL + e];
-        zp = xsum<1, 16>(zp) * a.isd;
-        z[m][g] = tv[m] ? zp : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float bm = fmaxf(fmaxf(z[0][g], z[1][g]), fmaxf(z[2][g], z[3][g]));
-      bm = xmax<16, 64>(bm);
-      if (!DENSE) bm = fmaxf(bm, zbar[g]);
-      const float M = fmaxf(mr[g], bm);
-      const float sc = rescale(mr[g], M);
-      lr[g] *= sc;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= sc;
-      mr[g] = M;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float pz = tv[m] ? __expf(z[m][g] - M) : 0.f;
-        lr[g] += pz;
-#pragma unroll
-        for (int e = 0; e < EPL / 2; ++e) {
-          acc[g][2 * e] += pz * bf16_lo(vr[m][e]);
-          acc[g][2 * e + 1] += pz * bf16_hi(vr[m][e]);
-        }
-      }
-      if (!DENSE && tq == 0) {
-        const float w = nb * __expf(zbar[g] - M);
-        lr[g] -= w;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] -= w * vb[e];
-      }
-    }
-  }
-
-  // ---- sum the 4 token quarters, stage per-wave partials
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    lr[g] = xsum<16, 64>(lr[g]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = xsum<16, 64>(acc[g][e]);
-  }
-  if (tq == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) cmb[(wave * G + g) * W + 2 + cc * EPL + e] = acc[g][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      cmb[(wave * G + g) * W] = mr[g];
-      cmb[(wave * G + g) * W + 1] = lr[g];
-    }
-  }
+  for (int i = 0; i < kBlocksPerAttendWave; ++i)
+    if (use[i]) absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
+  store_wave_record<D, G>(st, recs + wave * G * W, lane);
   __syncthreads();
 
-  // ---- this workgroup's partial: its waves + its share of the chunk sums
-  int c0 = 0, c1 = 0;
-  if (!DENSE) {
-    c0 = (int)((long)p * a.C / a.P);
-    c1 = (int)((long)(p + 1) * a.C / a.P);
-  }
-  const float* comp = a.comp + (size_t)unit * a.C * G * W;
   float* po = a.part + ((size_t)unit * a.P + p) * G * W;
-  for (int idx = tid; idx < G * W; idx += kThreads) {
-    const int g = idx / W, e = idx - g * W;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cmb[(w * G + g) * W]);
-    for (int c = c0; c < c1; ++c) M = fmaxf(M, comp[((size_t)c * G + g) * W]);
-    float val;
-    if (e == 0) {
-      val = M;
-    } else {
-      val = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) val += cmb[(w * G + g) * W + e] * rescale(cmb[(w * G + g) * W], M);
-      for (int c = c0; c < c1; ++c)
-        val += comp[((size_t)c * G + g) * W + e] * rescale(comp[((size_t)c * G + g) * W], M);
-    }
-    po[idx] = val;
-  }
-
+  merge_records<D, G>(recs, kWaves + (c1 - c0), po, scl);
   if (!last_arriver(a.ctr + unit, a.P, &last)) return;
   if (tid == 0) a.ctr[unit] = 0u;
-  const float* pp = a.part + (size_t)unit * a.P * G * W;
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, c = idx - g * D;
-    float M = -INFINITY;
-    for (int q = 0; q < a.P; ++q) M = fmaxf(M, pp[((size_t)q * G + g) * W]);
-    float L = 0.f, A = 0.f;
-    for (int q = 0; q < a.P; ++q) {
-      const float f = rescale(pp[((size_t)q * G + g) * W], M);
-      L += pp[((size_t)q * G + g) * W + 1] * f;
-      A += pp[((size_t)q * G + g) * W + 2 + c] * f;
-    }
-    const bool ok = L > 0.f;
-    a.out[((size_t)unit * G + g) * D + c] = ok ? A / L : 0.f;
-    if (c == 0 && a.lse) a.lse[(size_t)unit * G + g] = ok ? M + __logf(L) : -INFINITY;
+  finish_unit<D, G>(a.part + (size_t)unit * a.P * G * W, a.P, a.out + (size_t)unit * G * D,
+                    a.lse ? a.lse + (size_t)unit * G : nullptr, recs, CAP, scl);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
+  constexpr int W = rec_words(D);
+  constexpr int CAP = stage_cap<G>();
+  __shared__ __align__(16) float q_l[G * D];
+  __shared__ __align__(16) float recs[CAP * G * W];
+  __shared__ float scl[CAP * G + 3 * G];
+  __shared__ int last;
+
+  int unit, p;
+  map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
+  const int s = unit / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.seq_len[s];
+  const float4 qv = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : G * D / 4 - 1];
+  if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
+  __syncthreads();
+  int NB = (T + kBlock - 1) / kBlock;
+  NB = NB < a.max_blocks ? NB : a.max_blocks;
+  const long cap_tok = (long)a.cap_blocks * kBlock;
+  const uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
+  const uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
+  const int lo = p * a.BPW, hi = min(lo + a.BPW, NB);
+  WaveState<D, G> st;
+  st.init();
+  BlockMean<D> none;
+  for (int b = lo + 2 * wave; b < hi; b += 2 * kWaves) {
+    Tile<D> t0, t1;
+    const bool u1 = b + 1 < hi;
+    t0.load(kc, vc, (long)b * kBlock, T, lane);
+    t1.load(kc, vc, (long)(b + 1) * kBlock, u1 ? (long)T : 0, lane);
+    absorb<D, G, false>(st, t0, none, q_l, lane, a.isd);
+    if (u1) absorb<D, G, false>(st, t1, none, q_l, lane, a.isd);
   }
+  store_wave_record<D, G>(st, recs + wave * G * W, lane);
+  __syncthreads();
+  merge_records<D, G>(recs, kWaves, a.part + ((size_t)unit * a.P + p) * G * W, scl);
+  if (!last_arriver(a.ctr + unit, a.P, &last)) return;
+  if (tid == 0) a.ctr[unit] = 0u;
+  finish_unit<D, G>(a.part + (size_t)unit * a.P * G * W, a.P, a.out + (size_t)unit * G * D,
+                    a.lse ? a.lse + (size_t)unit * G : nullptr, recs, CAP, scl);
 }
 
 hipError_t launch_attend(int d, int G, bool dense, const AttendArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const void* f = nullptr;
-#define CKNV_ATT_CASE(DD, GG)                                                         \
-  if (d == DD && G == GG)                                                             \
-    f = dense ? (const void*)attend_kernel<DD, GG, true> : (const void*)attend_kernel<DD, GG, false>;
+#define CKNV_ATT_CASE(DD, GG) \
+  if (d == DD && G == GG) f = dense ? (const void*)dense_kernel<DD, GG> : (const void*)attend_kernel<DD, GG>;
   CKNV_ATT_CASE(64, 1) CKNV_ATT_CASE(64, 2) CKNV_ATT_CASE(64, 4) CKNV_ATT_CASE(64, 8)
   CKNV_ATT_CASE(128, 1) CKNV_ATT_CASE(128, 2) CKNV_ATT_CASE(128, 4) CKNV_ATT_CASE(128, 8)
 #undef CKNV_ATT_CASE

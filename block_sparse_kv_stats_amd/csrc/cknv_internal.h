@@ -11,13 +11,22 @@
 namespace cknv {
 
 constexpr int kBlock = 16;          // tokens per block (CompKV page, "Assumptions and limits")
-constexpr int kThreads = 256;       // threads per workgroup of every streaming kernel
+constexpr int kThreads = 256;       // threads per workgroup of the score and attend kernels
 constexpr int kWaves = kThreads / 64;
-constexpr int kBlocksPerWave = 16;  // one 16-block score group per wave iteration
-constexpr int kBlocksPerIter = kWaves * kBlocksPerWave;
-constexpr int kMaxChunks = 64;      // score workgroups per unit, at most
-constexpr int kDenseTargetWGs = 1024;
+constexpr int kBlocksPerWave = 16;  // one 16-block score group per wave
+constexpr int kBlocksPerWG = kWaves * kBlocksPerWave;  // blocks per score workgroup (64)
+constexpr int kAppendThreads = 1024;
+constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
+constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
+constexpr int kDenseMaxWGs = 64;          // dense attention: workgroups per unit (at most)
 constexpr size_t kMaxLds = 64 * 1024;
+constexpr int kScoreKeysPerThread = 48;   // selection keys per thread: max_blocks <= 256*48
+constexpr int kScoreGroupsPerThread = 3;  // 16-block LSE partials per thread in the selection
+
+// A partial softmax record (per unit, part and query head): running max m,
+// normaliser l, two pad words, then the weighted value sum acc[d]; the pad
+// keeps acc 16-byte aligned.
+__host__ __device__ constexpr int rec_words(int d) { return d + 4; }
 
 // Workspace layout. All offsets in bytes from the workspace base, 256-aligned.
 struct Plan {
@@ -25,23 +34,39 @@ struct Plan {
   int NBmax;        // max_blocks
   int NG;           // 16-block score groups per unit = ceil(NBmax/16)
   int Kb;           // block slots of the budget
-  int C;            // score chunks (workgroups) per unit
-  int BPC;          // blocks per score chunk (multiple of 64)
+  int C;            // score workgroups per unit (64 blocks each)
   int P;            // attend workgroups per unit
   int Pd;           // dense-attend workgroups per unit
+  int BPW;          // dense-attend blocks per workgroup
   size_t off_ctr, off_grp, off_u, off_comp, off_attp, off_dense, total;
   size_t n_ctr;     // counters (uint32)
   size_t score_lds; // dynamic LDS of the score kernel
 };
 
-// Counter rows inside the counter region (uint32 each, row length = max(S, U)).
-enum { kCtrAppend = 0, kCtrScore = 1, kCtrAttend = 2, kCtrDense = 3, kCtrRows = 4 };
+// Counter rows inside the counter region (uint32 each, row length U).
+enum { kCtrScore = 0, kCtrAttend = 1, kCtrDense = 2, kCtrRows = 3 };
 
 int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p);
 
+// Dynamic LDS of the score kernel. The streaming phase stages the 4 waves'
+// compensation records; the selection keeps the normalisation factors
+// f[NG][G] and then, in the same words, the keys [48][256] ("big" region),
+// followed by reduction scratch, the radix histogram and tile counts.
+__host__ __device__ inline size_t score_big_words(int G, int max_blocks) {
+  const size_t NG = ((size_t)max_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
+  const size_t f = NG * G, keys = (size_t)kScoreKeysPerThread * kThreads;
+  return f > keys ? f : keys;
+}
+__host__ __device__ inline size_t score_lds_bytes(int d, int G, int max_blocks) {
+  const size_t main_lds = (size_t)kWaves * G * rec_words(d) * 4;
+  const size_t tail = score_big_words(G, max_blocks) * 4 + (size_t)kWaves * G * 2 * 4 + 256 * 4 +
+                      16 * 4 + (size_t)kWaves * 16 * 4;
+  return main_lds > tail ? main_lds : tail;
+}
+
 struct AppendArgs {
   uint16_t* k; uint16_t* v; float* kbar; float* dbar; float* cnt; float* vbar;
-  int32_t* seq_len; const uint16_t* new_k; const uint16_t* new_v; uint32_t* ctr;
+  int32_t* seq_len; const uint16_t* new_k; const uint16_t* new_v;
   int S, H, r, cap_blocks;
 };
 
@@ -55,7 +80,7 @@ struct ScoreArgs {
   const int32_t* seq_len; const float* q;
   float* scores; int32_t* sel; int32_t* n_sel;
   uint32_t* ctr; float* grp; float* u; float* comp;
-  int S, H, r, cap_blocks, max_blocks, NG, Kb, C, BPC, xcd;
+  int S, H, r, cap_blocks, max_blocks, NG, Kb, C, xcd;
   float isd;  // 1/sqrt(d)
 };
 
@@ -63,11 +88,11 @@ struct AttendArgs {
   const uint16_t* k; const uint16_t* v; const float* kbar; const float* vbar; const float* cnt;
   const int32_t* seq_len; const float* q; const int32_t* sel; const int32_t* n_sel;
   float* out; float* lse; uint32_t* ctr; const float* comp; float* part;
-  int S, H, cap_blocks, max_blocks, Kb, C, P, xcd;
+  int S, H, cap_blocks, max_blocks, Kb, C, P, BPW, xcd;  // BPW: dense blocks per workgroup
   float isd;
 };
 
-hipError_t launch_append(int d, const AppendArgs& a, int U, hipStream_t st);
+hipError_t launch_append(int d, const AppendArgs& a, hipStream_t st);
 hipError_t launch_build(int d, const BuildArgs& a, int U, hipStream_t st);
 hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, size_t lds, hipStream_t st);
 hipError_t launch_attend(int d, int G, bool dense, const AttendArgs& a, int U, hipStream_t st);
@@ -79,19 +104,69 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_1(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// Sum / max over the lanes whose index differs from this lane's in the bits
-// LO, 2*LO, ..., below HI (butterfly, every participating lane gets the result).
-template <int LO, int HI>
-__device__ __forceinline__ float xsum(float x) {
-#pragma unroll
-  for (int o = LO; o < HI; o <<= 1) x += __shfl_xor(x, o);
+// Cross-lane data movement without the LDS: DPP within 16-lane rows, the
+// gfx950 permlane swaps across rows. permlane16_swap(x, x) returns
+// (rows 0,0,2,2 ; rows 1,1,3,3) and permlane32_swap(x, x) returns
+// (lanes 0-31 twice ; lanes 32-63 twice), so adding the pair combines every
+// lane with its xor-16 (xor-32) partner. All reductions below give every lane
+// of the group the same bits (each step adds the same two operands).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+__device__ __forceinline__ float swap16_lo(float x, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  hi = __uint_as_float(r[1]);
+  return __uint_as_float(r[0]);
+}
+__device__ __forceinline__ float swap32_lo(float x, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  hi = __uint_as_float(r[1]);
+  return __uint_as_float(r[0]);
+}
+
+// Sum / max over aligned groups of N lanes (N = 2..64), starting at lane 0 of the group.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if (N >= 2) x += dpp<kDppXor1>(x);
+  if (N >= 4) x += dpp<kDppXor2>(x);
+  if (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if (N >= 16) x += dpp<kDppMirror>(x);
+  float h;
+  if (N >= 32) { const float l = swap16_lo(x, h); x = l + h; }
+  if (N >= 64) { const float l = swap32_lo(x, h); x = l + h; }
   return x;
 }
-template <int LO, int HI>
-__device__ __forceinline__ float xmax(float x) {
-#pragma unroll
-  for (int o = LO; o < HI; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+  if (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  if (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  float h;
+  if (N >= 32) { const float l = swap16_lo(x, h); x = fmaxf(l, h); }
+  if (N >= 64) { const float l = swap32_lo(x, h); x = fmaxf(l, h); }
   return x;
+}
+// Sum / max over the 4 rows of the wave (lanes i, i^16, i^32, i^48).
+__device__ __forceinline__ float rows_sum(float x) {
+  float h;
+  float l = swap16_lo(x, h);
+  x = l + h;
+  l = swap32_lo(x, h);
+  return l + h;
+}
+__device__ __forceinline__ float rows_max(float x) {
+  float h;
+  float l = swap16_lo(x, h);
+  x = fmaxf(l, h);
+  l = swap32_lo(x, h);
+  return fmaxf(l, h);
 }
 
 // exp(m - M) with exp(-inf - anything) = 0 (an empty partial contributes nothing).
@@ -113,20 +188,21 @@ __device__ __forceinline__ void map_wg(int L, int U, int parts, int xcd, int& un
   }
 }
 
-// Last-arriver election among the `expected` workgroups of one unit. Every
-// thread fences its own global writes (release) before the barrier; the
-// returned flag is uniform over the workgroup. The winner fences again
-// (acquire) before reading what the others wrote.
+// Last-arriver election among the `expected` workgroups of one unit. The
+// barrier makes every wave's global writes complete (workgroup release);
+// thread 0 then releases them at agent scope and counts the arrival. The
+// returned flag is uniform over the workgroup; the winner's waves acquire at
+// agent scope before reading what the others wrote.
 __device__ __forceinline__ bool last_arriver(uint32_t* ctr, int expected, int* flag_lds) {
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(ctr, 1u);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag_lds = (prev == (uint32_t)(expected - 1));
   }
   __syncthreads();
   const bool last = *flag_lds != 0;
-  if (last) __threadfence();
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return last;
 }
 #endif

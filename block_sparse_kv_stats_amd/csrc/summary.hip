@@ -36,53 +36,59 @@ __device__ __forceinline__ float group_mean(const float* cvar, int t, int gs) {
   return s / (float)gs;
 }
 
-// One workgroup per unit, one thread per key coordinate.
+// One workgroup per sequence: thread (h, c) handles key coordinate c of head
+// h (looping when H*D exceeds the workgroup). The token is written and the
+// block refreshed for every head before seq_len[s] advances, so no other
+// workgroup reads seq_len[s] concurrently.
 template <int D>
-__global__ __launch_bounds__(D) void append_kernel(AppendArgs a) {
-  __shared__ float cvar[D];
-  __shared__ int last;
-  const int unit = blockIdx.x, s = unit / a.H, c = threadIdx.x;
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+  __shared__ float cvar[kAppendThreads];
+  constexpr int HPI = kAppendThreads / D;  // heads per pass
+  const int s = blockIdx.x;
   const int T = a.seq_len[s];
   const long cap_tok = (long)a.cap_blocks * kBlock;
   const bool room = T < cap_tok;
-  int b = 0, n = 0;
-  if (room) {
-    b = T / kBlock;
-    n = T - b * kBlock + 1;  // tokens in the block once the new one is in
-    const size_t tok0 = (size_t)unit * cap_tok + (size_t)b * kBlock;
-    const uint16_t* kb = a.k + tok0 * D + c;
-    const uint16_t* vb = a.v + tok0 * D + c;
-    const uint16_t nk = a.new_k[(size_t)unit * D + c];
-    const uint16_t nv = a.new_v[(size_t)unit * D + c];
-    float kx[16], vx[16];
+  const int b = T / kBlock;
+  const int n = T - b * kBlock + 1;  // tokens in the block once the new one is in
+  const int hl = threadIdx.x / D, c = threadIdx.x % D;
+  for (int h0 = 0; h0 < a.H; h0 += HPI) {
+    const int h = h0 + hl;
+    const bool act = room && h < a.H;
+    const int unit = s * a.H + h;
+    if (act) {
+      const size_t tok0 = (size_t)unit * cap_tok + (size_t)b * kBlock;
+      const uint16_t* kb = a.k + tok0 * D + c;
+      const uint16_t* vb = a.v + tok0 * D + c;
+      const uint16_t nk = a.new_k[(size_t)unit * D + c];
+      const uint16_t nv = a.new_v[(size_t)unit * D + c];
+      float kx[16], vx[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const bool old = j < n - 1;
-      kx[j] = old ? bf16_1(kb[(size_t)j * D]) : (j == n - 1 ? bf16_1(nk) : 0.f);
-      vx[j] = old ? bf16_1(vb[(size_t)j * D]) : (j == n - 1 ? bf16_1(nv) : 0.f);
+      for (int j = 0; j < 16; ++j) {
+        const bool old = j < n - 1;
+        const uint16_t kj = old ? kb[(size_t)j * D] : nk;
+        const uint16_t vj = old ? vb[(size_t)j * D] : nv;
+        kx[j] = j < n ? bf16_1(kj) : 0.f;
+        vx[j] = j < n ? bf16_1(vj) : 0.f;
+      }
+      a.k[(tok0 + n - 1) * D + c] = nk;
+      a.v[(tok0 + n - 1) * D + c] = nv;
+      float km, kv, vm, vv;
+      mean_var16(kx, n, km, kv);
+      mean_var16(vx, n, vm, vv);
+      const size_t row = (size_t)unit * a.cap_blocks + b;
+      a.kbar[row * D + c] = km;
+      a.vbar[row * D + c] = vm;
+      cvar[threadIdx.x] = kv;
+      if (c == 0) a.cnt[row] = (float)n;
     }
-    a.k[(tok0 + n - 1) * D + c] = nk;
-    a.v[(tok0 + n - 1) * D + c] = nv;
-    float km, kv, vm, vv;
-    mean_var16(kx, n, km, kv);
-    mean_var16(vx, n, vm, vv);
-    const size_t row = (size_t)unit * a.cap_blocks + b;
-    a.kbar[row * D + c] = km;
-    a.vbar[row * D + c] = vm;
-    cvar[c] = kv;
-    if (c == 0) a.cnt[row] = (float)n;
+    __syncthreads();
+    if (act && c < a.r) {
+      const size_t row = (size_t)unit * a.cap_blocks + b;
+      a.dbar[row * a.r + c] = group_mean(cvar + hl * D, c, D / a.r);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (room && c < a.r) {
-    const size_t row = (size_t)unit * a.cap_blocks + b;
-    a.dbar[row * a.r + c] = group_mean(cvar, c, D / a.r);
-  }
-  // The last head of sequence s to finish advances seq_len[s]: every head has
-  // read it by then.
-  if (last_arriver(a.ctr + s, a.H, &last) && c == 0) {
-    a.ctr[s] = 0;
-    if (room) a.seq_len[s] = T + 1;
-  }
+  if (threadIdx.x == 0 && room) a.seq_len[s] = T + 1;
 }
 
 // Bulk build: 256 threads = 256/D blocks per workgroup, one thread per coordinate.
@@ -130,10 +136,10 @@ __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
   if (i < n) p[i] = 0u;
 }
 
-hipError_t launch_append(int d, const AppendArgs& a, int U, hipStream_t st) {
+hipError_t launch_append(int d, const AppendArgs& a, hipStream_t st) {
   void* args[] = {(void*)&a};
   const void* f = d == 128 ? (const void*)append_kernel<128> : (const void*)append_kernel<64>;
-  return hipLaunchKernel(f, dim3(U), dim3(d), args, 0, st);
+  return hipLaunchKernel(f, dim3(a.S), dim3(kAppendThreads), args, 0, st);
 }
 
 hipError_t launch_build(int d, const BuildArgs& a, int U, hipStream_t st) {

@@ -106,11 +106,9 @@ int cknv_workspace_init(const cknv_shape* shape, int32_t max_blocks, int32_t bud
  * recomputed from its (up to 16) tokens in FP32, two-pass (mean, then
  * population variance). Afterwards seq_len[s] += 1 for every sequence.
  * new_k, new_v: bfloat16 [S][H][d]. A sequence whose cache is full
- * (seq_len == 16*cap_blocks) is left unchanged.
- * The workspace is only used for its counters. */
+ * (seq_len == 16*cap_blocks) is left unchanged. Needs no workspace. */
 int cknv_append(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
-                const uint16_t* new_v, int32_t max_blocks, int32_t budget_tokens, void* ws,
-                size_t ws_bytes, void* stream);
+                const uint16_t* new_v, void* stream);
 
 /* Build the summary of every block of every unit from the cache (blocks
  * 0..NB-1, NB from seq_len). Same arithmetic as cknv_append. Used after a

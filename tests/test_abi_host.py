@@ -113,10 +113,8 @@ def test_entry_points_reject_before_launch():
                          None, FAKE, need, None) == cknv.EINVAL
     assert L.cknv_dense_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, 2048, 512, None, None,
                                FAKE, need, None) == cknv.EINVAL
-    assert L.cknv_append(ctypes.byref(sh), ctypes.byref(c), None, FAKE, 2048, 512, FAKE, need,
-                         None) == cknv.EINVAL
-    assert L.cknv_append(ctypes.byref(sh), ctypes.byref(c), FAKE, FAKE, 2048, 512, FAKE, 16,
-                         None) == cknv.ENOSPACE
+    assert L.cknv_append(ctypes.byref(sh), ctypes.byref(c), None, FAKE, None) == cknv.EINVAL
+    assert L.cknv_append(ctypes.byref(sh), None, FAKE, FAKE, None) == cknv.EINVAL
     assert L.cknv_workspace_init(ctypes.byref(sh), 2048, 512, None, need, None) == cknv.EINVAL
     # budget below the forced set, max_blocks beyond capacity
     assert L.cknv_score_select(ctypes.byref(sh), ctypes.byref(c), FAKE, 32, 2048, None, FAKE, FAKE,

@@ -267,9 +267,8 @@ def test_append_at_capacity_is_a_no_op():
     data = synth.gen_layer(w)
     cache = gu.upload(w, data, cap_blocks=4, max_blocks=4)
     before = [t.clone() for t in (cache.k, cache.v, cache.kbar, cache.cnt, cache.seq_len)]
-    ws = cknv.allocate_workspace(cache.shape, 4, 64)
     nk = torch.ones((1, 2, 64), dtype=torch.bfloat16, device="cuda")
-    cknv.append(cache, nk, nk, 4, 64, ws)
+    cknv.append(cache, nk, nk)
     torch.cuda.synchronize()
     for a, b in zip(before, (cache.k, cache.v, cache.kbar, cache.cnt, cache.seq_len)):
         assert torch.equal(a, b)
