@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode steps/sec (1 layer, B=1) at 32K/128K ctx + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
-SCORE_SOURCES = ["block_sparse_kv_stats_amd/csrc/score_select.hip",
+SCORE_SOURCES = ["block_sparse_kv_stats_amd/csrc/score.hip",
+                 "block_sparse_kv_stats_amd/csrc/select.hip",
                  "block_sparse_kv_stats_amd/csrc/cknv_internal.h"]
 
 

@@ -40,7 +40,7 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   q.NG = (max_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
   q.Kb = budget_tokens / kBlock;
   q.C = (max_blocks + kBlocksPerWG - 1) / kBlocksPerWG;
-  const int per_wg = kWaves * 2;  // kept blocks per attend workgroup
+  const int per_wg = kWaves;  // kept blocks per attend workgroup (one per wave)
   q.P = (q.Kb + per_wg - 1) / per_wg;
   const int pc = (q.C + kMaxChunksPerAttendWG - 1) / kMaxChunksPerAttendWG;
   q.P = q.P > pc ? q.P : pc;
@@ -50,9 +50,6 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   q.Pd = (max_blocks + bpw - 1) / bpw;
   const size_t W = (size_t)rec_words(d);
   size_t off = 0;
-  q.off_ctr = off;
-  q.n_ctr = (size_t)kCtrRows * (size_t)q.U;
-  off = align256(off + q.n_ctr * 4);
   q.off_grp = off;
   off = align256(off + (size_t)q.U * q.NG * G * 2 * 4);
   q.off_u = off;
@@ -64,16 +61,9 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   q.off_dense = off;
   off = align256(off + (size_t)q.U * q.Pd * G * W * 4);
   q.total = off;
-  if (max_blocks > kThreads * kScoreKeysPerThread) return CKNV_EUNSUPPORTED;
-  q.score_lds = score_lds_bytes(d, G, max_blocks);
-  if (q.score_lds > kMaxLds) return CKNV_EUNSUPPORTED;
+  if (max_blocks > kSelThreads * kSelKeysPerThread) return CKNV_EUNSUPPORTED;
   *p = q;
   return CKNV_OK;
-}
-
-static uint32_t* ctr_row(void* ws, const Plan& p, int row) {
-  const size_t rowlen = p.n_ctr / kCtrRows;
-  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.off_ctr) + (size_t)row * rowlen;
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? CKNV_OK : CKNV_EHIP; }
@@ -101,7 +91,7 @@ int cknv_workspace_init(const cknv_shape* shape, int32_t max_blocks, int32_t bud
   if (st) return st;
   if (!ws) return CKNV_EINVAL;
   if (ws_bytes < p.total) return CKNV_ENOSPACE;
-  return hip_status(launch_zero_u32(ctr_row(ws, p, 0), p.n_ctr, (hipStream_t)stream));
+  return hip_status(launch_zero_u32(static_cast<uint32_t*>(ws), p.total / 4, (hipStream_t)stream));
 }
 
 int cknv_append(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
@@ -140,16 +130,21 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   ScoreArgs a{};
   a.kbar = cache->kbar; a.dbar = cache->dbar; a.cnt = cache->cnt; a.vbar = cache->vbar;
   a.seq_len = cache->seq_len; a.q = q;
-  a.scores = scores; a.sel = sel; a.n_sel = n_sel;
-  a.ctr = ctr_row(ws, p, kCtrScore);
   a.grp = reinterpret_cast<float*>(w + p.off_grp);
   a.u = reinterpret_cast<float*>(w + p.off_u);
   a.comp = reinterpret_cast<float*>(w + p.off_comp);
   a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
-  a.max_blocks = max_blocks; a.NG = p.NG; a.Kb = p.Kb; a.C = p.C;
+  a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C;
   a.xcd = (p.U % 8) == 0;
   a.isd = 1.0f / sqrtf((float)shape->d);
-  return hip_status(launch_score(shape->d, shape->G, a, p.U, p.score_lds, (hipStream_t)stream));
+  hipError_t e = launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream);
+  if (e != hipSuccess) return CKNV_EHIP;
+  SelectArgs sa{};
+  sa.seq_len = cache->seq_len; sa.grp = a.grp; sa.u = a.u;
+  sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel;
+  sa.H = shape->H; sa.cap_blocks = shape->cap_blocks; sa.max_blocks = max_blocks; sa.NG = p.NG;
+  sa.Kb = p.Kb;
+  return hip_status(launch_select(shape->G, sa, p.U, (hipStream_t)stream));
 }
 
 static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const float* q,
@@ -168,7 +163,6 @@ static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const
   a.k = cache->k; a.v = cache->v; a.kbar = cache->kbar; a.vbar = cache->vbar; a.cnt = cache->cnt;
   a.seq_len = cache->seq_len; a.q = q; a.sel = sel; a.n_sel = n_sel;
   a.out = out; a.lse = lse;
-  a.ctr = ctr_row(ws, p, dense ? kCtrDense : kCtrAttend);
   a.comp = reinterpret_cast<const float*>(w + p.off_comp);
   a.part = reinterpret_cast<float*>(w + (dense ? p.off_dense : p.off_attp));
   a.S = shape->S; a.H = shape->H; a.cap_blocks = shape->cap_blocks; a.max_blocks = max_blocks;

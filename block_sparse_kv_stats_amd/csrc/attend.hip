@@ -13,7 +13,8 @@
 //     blocks: 16 tokens x d BF16 keys and values, 4 tokens per load),
 //   * subtracts those blocks' own compensation terms |b| e^{z̄_b}(1, v̄_b),
 //   * folds in up to 8 of the score kernel's chunk records,
-// and the unit's last workgroup merges the P records into out and lse.
+// and writes one record; merge_kernel then combines a unit's P records into
+// out and lse.
 // Subtracting is safe in FP32: a kept block's exact mass sum_i e^{z_i} is at
 // least its compensation mass |b| e^{z̄_b} (Jensen), so the final normaliser
 // is at least the sum of all compensation masses and the rounding error of
@@ -27,7 +28,7 @@ namespace cknv {
 
 namespace {
 
-constexpr int kBlocksPerAttendWave = 2;
+constexpr int kBlocksPerAttendWave = 1;
 
 // Running softmax state of one wave for the G query heads. Lane l owns value
 // coordinates [l*VPL, l*VPL+VPL) (VPL = d/64) summed over every token it has
@@ -347,7 +348,6 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   __shared__ __align__(16) float q_l[G * D];
   __shared__ __align__(16) float recs[CAP * G * W];
   __shared__ float scl[CAP * G + 3 * G];
-  __shared__ int last;
 
   int unit, p;
   map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
@@ -399,10 +399,6 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
 
   float* po = a.part + ((size_t)unit * a.P + p) * G * W;
   merge_records<D, G>(recs, kWaves + (c1 - c0), po, scl);
-  if (!last_arriver(a.ctr + unit, a.P, &last)) return;
-  if (tid == 0) a.ctr[unit] = 0u;
-  finish_unit<D, G>(a.part + (size_t)unit * a.P * G * W, a.P, a.out + (size_t)unit * G * D,
-                    a.lse ? a.lse + (size_t)unit * G : nullptr, recs, CAP, scl);
 }
 
 template <int D, int G>
@@ -412,7 +408,6 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
   __shared__ __align__(16) float q_l[G * D];
   __shared__ __align__(16) float recs[CAP * G * W];
   __shared__ float scl[CAP * G + 3 * G];
-  __shared__ int last;
 
   int unit, p;
   map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
@@ -442,8 +437,16 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
   __syncthreads();
   merge_records<D, G>(recs, kWaves, a.part + ((size_t)unit * a.P + p) * G * W, scl);
-  if (!last_arriver(a.ctr + unit, a.P, &last)) return;
-  if (tid == 0) a.ctr[unit] = 0u;
+}
+
+// One workgroup per unit: merge the unit's P part records into out and lse.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttendArgs a) {
+  constexpr int W = rec_words(D);
+  constexpr int CAP = stage_cap<G>();
+  __shared__ __align__(16) float recs[CAP * G * W];
+  __shared__ float scl[CAP * G + 3 * G];
+  const int unit = blockIdx.x;
   finish_unit<D, G>(a.part + (size_t)unit * a.P * G * W, a.P, a.out + (size_t)unit * G * D,
                     a.lse ? a.lse + (size_t)unit * G : nullptr, recs, CAP, scl);
 }
@@ -451,13 +454,19 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
 hipError_t launch_attend(int d, int G, bool dense, const AttendArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const void* f = nullptr;
-#define CKNV_ATT_CASE(DD, GG) \
-  if (d == DD && G == GG) f = dense ? (const void*)dense_kernel<DD, GG> : (const void*)attend_kernel<DD, GG>;
+  const void* m = nullptr;
+#define CKNV_ATT_CASE(DD, GG)                                                                  \
+  if (d == DD && G == GG) {                                                                    \
+    f = dense ? (const void*)dense_kernel<DD, GG> : (const void*)attend_kernel<DD, GG>;        \
+    m = (const void*)merge_kernel<DD, GG>;                                                     \
+  }
   CKNV_ATT_CASE(64, 1) CKNV_ATT_CASE(64, 2) CKNV_ATT_CASE(64, 4) CKNV_ATT_CASE(64, 8)
   CKNV_ATT_CASE(128, 1) CKNV_ATT_CASE(128, 2) CKNV_ATT_CASE(128, 4) CKNV_ATT_CASE(128, 8)
 #undef CKNV_ATT_CASE
-  if (!f) return hipErrorInvalidValue;
-  return hipLaunchKernel(f, dim3(U * a.P), dim3(kThreads), args, 0, st);
+  if (!f || !m) return hipErrorInvalidValue;
+  hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(kThreads), args, 0, st);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(m, dim3(U), dim3(kThreads), args, 0, st);
 }
 
 }  // namespace cknv

@@ -19,9 +19,9 @@ constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
 constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
 constexpr int kDenseMaxWGs = 64;          // dense attention: workgroups per unit (at most)
-constexpr size_t kMaxLds = 64 * 1024;
-constexpr int kScoreKeysPerThread = 48;   // selection keys per thread: max_blocks <= 256*48
-constexpr int kScoreGroupsPerThread = 3;  // 16-block LSE partials per thread in the selection
+constexpr int kSelThreads = 1024;       // selection: one workgroup per unit
+constexpr int kSelKeysPerThread = 12;   // blocks per selection thread: max_blocks <= 12288
+constexpr int kSelMaxGroups = 1024;     // 16-block groups the selection can normalise
 
 // A partial softmax record (per unit, part and query head): running max m,
 // normaliser l, two pad words, then the weighted value sum acc[d]; the pad
@@ -38,31 +38,10 @@ struct Plan {
   int P;            // attend workgroups per unit
   int Pd;           // dense-attend workgroups per unit
   int BPW;          // dense-attend blocks per workgroup
-  size_t off_ctr, off_grp, off_u, off_comp, off_attp, off_dense, total;
-  size_t n_ctr;     // counters (uint32)
-  size_t score_lds; // dynamic LDS of the score kernel
+  size_t off_grp, off_u, off_comp, off_attp, off_dense, total;
 };
 
-// Counter rows inside the counter region (uint32 each, row length U).
-enum { kCtrScore = 0, kCtrAttend = 1, kCtrDense = 2, kCtrRows = 3 };
-
 int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p);
-
-// Dynamic LDS of the score kernel. The streaming phase stages the 4 waves'
-// compensation records; the selection keeps the normalisation factors
-// f[NG][G] and then, in the same words, the keys [48][256] ("big" region),
-// followed by reduction scratch, the radix histogram and tile counts.
-__host__ __device__ inline size_t score_big_words(int G, int max_blocks) {
-  const size_t NG = ((size_t)max_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const size_t f = NG * G, keys = (size_t)kScoreKeysPerThread * kThreads;
-  return f > keys ? f : keys;
-}
-__host__ __device__ inline size_t score_lds_bytes(int d, int G, int max_blocks) {
-  const size_t main_lds = (size_t)kWaves * G * rec_words(d) * 4;
-  const size_t tail = score_big_words(G, max_blocks) * 4 + (size_t)kWaves * G * 2 * 4 + 256 * 4 +
-                      16 * 4 + (size_t)kWaves * 16 * 4;
-  return main_lds > tail ? main_lds : tail;
-}
 
 struct AppendArgs {
   uint16_t* k; uint16_t* v; float* kbar; float* dbar; float* cnt; float* vbar;
@@ -78,23 +57,29 @@ struct BuildArgs {
 struct ScoreArgs {
   const float* kbar; const float* dbar; const float* cnt; const float* vbar;
   const int32_t* seq_len; const float* q;
-  float* scores; int32_t* sel; int32_t* n_sel;
-  uint32_t* ctr; float* grp; float* u; float* comp;
-  int S, H, r, cap_blocks, max_blocks, NG, Kb, C, xcd;
+  float* grp; float* u; float* comp;
+  int S, H, r, cap_blocks, max_blocks, NG, C, xcd;
   float isd;  // 1/sqrt(d)
+};
+
+struct SelectArgs {
+  const int32_t* seq_len; const float* grp; const float* u;
+  float* scores; int32_t* sel; int32_t* n_sel;
+  int H, cap_blocks, max_blocks, NG, Kb;
 };
 
 struct AttendArgs {
   const uint16_t* k; const uint16_t* v; const float* kbar; const float* vbar; const float* cnt;
   const int32_t* seq_len; const float* q; const int32_t* sel; const int32_t* n_sel;
-  float* out; float* lse; uint32_t* ctr; const float* comp; float* part;
+  float* out; float* lse; const float* comp; float* part;
   int S, H, cap_blocks, max_blocks, Kb, C, P, BPW, xcd;  // BPW: dense blocks per workgroup
   float isd;
 };
 
 hipError_t launch_append(int d, const AppendArgs& a, hipStream_t st);
 hipError_t launch_build(int d, const BuildArgs& a, int U, hipStream_t st);
-hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, size_t lds, hipStream_t st);
+hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st);
+hipError_t launch_select(int G, const SelectArgs& a, int U, hipStream_t st);
 hipError_t launch_attend(int d, int G, bool dense, const AttendArgs& a, int U, hipStream_t st);
 hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 
@@ -188,23 +173,6 @@ __device__ __forceinline__ void map_wg(int L, int U, int parts, int xcd, int& un
   }
 }
 
-// Last-arriver election among the `expected` workgroups of one unit. The
-// barrier makes every wave's global writes complete (workgroup release);
-// thread 0 then releases them at agent scope and counts the arrival. The
-// returned flag is uniform over the workgroup; the winner's waves acquire at
-// agent scope before reading what the others wrote.
-__device__ __forceinline__ bool last_arriver(uint32_t* ctr, int expected, int* flag_lds) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_lds = (prev == (uint32_t)(expected - 1));
-  }
-  __syncthreads();
-  const bool last = *flag_lds != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
-}
 #endif
 
 }  // namespace cknv

@@ -1,4 +1,4 @@
-// Block scoring and selection, one streaming pass over the summary store.
+// Block scoring: one streaming pass over the summary store.
 //
 // CompKV page (onedev.kr/papers/157), "What differs": for the G query heads
 // of a KV head and every block b,
@@ -9,6 +9,7 @@
 // and the kept set is the first block, the two most recent blocks and the
 // Top-(Kb-3) of the rest by S_b. "How it works": an unselected block is
 // represented by Mean compensation, |b| e^{z̄} with mean value v̄_b.
+// This file computes every block's score ingredients in one streaming pass.
 //
 // σ̂² is evaluated per coordinate, (1/d) sum_i q_{g,i}^2 D̄_{b,t(i)} with t(i)
 // the group of coordinate i, which is the same sum regrouped.
@@ -22,10 +23,7 @@
 // chunk it writes the Mean-compensation sums of ALL its blocks,
 //   (m, l = sum |b| e^{z̄-m}, acc = sum |b| e^{z̄-m} v̄_b),
 // which the attend kernel corrects by removing the kept blocks' terms (the
-// kept set is not known yet). The last chunk of a unit to finish normalises
-// the scores (S_b = sum_g u_{g,b} e^{max - LSE_g}) and selects with an
-// MSB-first radix select on the fp32 bit patterns of S_b (S_b >= 0, so the bit
-// patterns order like the values), ties to the lower index.
+// kept set is not known yet). The selection kernel (select.hip) runs next.
 #include "cknv_internal.h"
 
 namespace cknv {
@@ -75,248 +73,11 @@ struct DbarTile<kDbarQuad, ROWS, KC> {
   }
 };
 
-// Running block-wide exclusive prefix over tiles of 256 consecutive items
-// (item order: tile-major, then thread). For each of NT tiles, before[m]
-// becomes the number of flagged items ahead of this thread's item, counting
-// from `run` (updated to the total). `cnt`: LDS scratch of kWaves*NT ints.
-template <int NT>
-__device__ __forceinline__ void tile_prefix(const bool (&flag)[NT], int (&before)[NT], int* cnt, int& run) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 0; m < NT; ++m) {
-    const unsigned long long bal = __ballot(flag[m]);
-    before[m] = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) cnt[wave * NT + m] = __popcll(bal);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < NT; ++m) {
-    int wsum = 0, mine = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = cnt[w * NT + m];
-      mine += w < wave ? c : 0;
-      wsum += c;
-    }
-    before[m] += run + mine;
-    run += wsum;
-  }
-  __syncthreads();
-}
-
-// The selection, run by the unit's last workgroup. LDS: the normalisation
-// factors f[NG][G], later overwritten by the keys [KPT][256]; reduction
-// scratch; the radix histogram; tile counts.
-template <int G>
-__device__ __forceinline__ void select_tail(const ScoreArgs& a, int unit, int NB, float* lds,
-                                            size_t big_words) {
-  constexpr int KPT = kScoreKeysPerThread;
-  constexpr int GPT = kScoreGroupsPerThread;
-  constexpr int CH = 16;  // keys per thread per LDS chunk
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* f = lds;                                                   // [NG][G]
-  uint32_t* keys = reinterpret_cast<uint32_t*>(lds);                // [KPT][256], after f
-  float* red = lds + big_words;                                     // [kWaves][G][2]
-  int* hist = reinterpret_cast<int*>(red + kWaves * G * 2);         // [256]
-  int* ctl = hist + 256;                                            // [16]
-  int* tcnt = ctl + 16;                                             // [kWaves][CH]
-  int32_t* sel = a.sel + (size_t)unit * a.Kb;
-
-  if (tid == 0) a.ctr[unit] = 0u;
-  if (NB == 0) {
-    if (tid == 0) a.n_sel[unit] = 0;
-    return;
-  }
-  const int NGu = (NB + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int nper = (NB + kThreads - 1) / kThreads;
-  const float* grp = a.grp + (size_t)unit * a.NG * G * 2;
-  const float* u = a.u + (size_t)unit * a.max_blocks * G;
-
-  // ---- group partials and the first batch of u, issued together
-  float gr[GPT][G], gl[GPT][G];
-#pragma unroll
-  for (int m = 0; m < GPT; ++m) {
-    const int gi = tid + m * kThreads;
-    const int gc = gi < NGu ? gi : NGu - 1;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float2 v = reinterpret_cast<const float2*>(grp)[(size_t)gc * G + g];
-      gr[m][g] = gi < NGu ? v.x : -INFINITY;
-      gl[m][g] = gi < NGu ? v.y : 0.f;
-    }
-  }
-  constexpr int UB = G <= 4 ? 16 : 8;  // blocks per thread per u batch
-  float ub[UB][G];
-#pragma unroll
-  for (int m = 0; m < UB; ++m) {
-    const int b = tid + m * kThreads;
-    const int bc = b < NB ? b : NB - 1;
-#pragma unroll
-    for (int g = 0; g < G; ++g) ub[m][g] = u[(size_t)bc * G + g];
-  }
-
-  // ---- LSE_g over all blocks
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float M = -INFINITY, L = 0.f;
-#pragma unroll
-    for (int m = 0; m < GPT; ++m) {
-      const float MM = fmaxf(M, gr[m][g]);
-      L = L * rescale(M, MM) + gl[m][g] * rescale(gr[m][g], MM);
-      M = MM;
-    }
-    const float Mw = group_max<64>(M);
-    const float Lw = group_sum<64>(L * rescale(M, Mw));
-    if (lane == 0) { red[(wave * G + g) * 2] = Mw; red[(wave * G + g) * 2 + 1] = Lw; }
-  }
-  __syncthreads();
-  float lse[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * G + g) * 2]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += red[(w * G + g) * 2 + 1] * rescale(red[(w * G + g) * 2], M);
-    lse[g] = M + __logf(L);
-  }
-  // f[gi][g] = exp(group max - LSE_g) turns u into p̂ σ̂²
-#pragma unroll
-  for (int m = 0; m < GPT; ++m) {
-    const int gi = tid + m * kThreads;
-    if (gi < NGu) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) f[gi * G + g] = __expf(gr[m][g] - lse[g]);
-    }
-  }
-  __syncthreads();
-
-  // ---- S_b into registers (thread owns blocks tid + 256*m), then the keys into LDS
-  uint32_t key[KPT];
-  float* scores = a.scores ? a.scores + (size_t)unit * a.cap_blocks : nullptr;
-#pragma unroll
-  for (int m0 = 0; m0 < KPT; m0 += UB) {
-    if (m0 > 0 && m0 < nper) {
-#pragma unroll
-      for (int m = 0; m < UB; ++m) {
-        const int b = tid + (m0 + m) * kThreads;
-        const int bc = b < NB ? b : NB - 1;
-#pragma unroll
-        for (int g = 0; g < G; ++g) ub[m][g] = u[(size_t)bc * G + g];
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < UB; ++m) {
-      const int b = tid + (m0 + m) * kThreads;
-      const int bc = b < NB ? b : NB - 1;
-      float S = 0.f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) S += ub[m][g] * f[(bc >> 4) * G + g];
-      key[m0 + m] = (b < NB && S > 0.f) ? __float_as_uint(S) : 0u;
-      if (scores && b < NB) scores[b] = S;
-    }
-  }
-  if (NB <= a.Kb) {
-    for (int b = tid; b < NB; b += kThreads) sel[b] = b;
-    if (tid == 0) a.n_sel[unit] = NB;
-    return;
-  }
-  __syncthreads();  // f is dead from here on; the keys take its place
-#pragma unroll
-  for (int m = 0; m < KPT; ++m) keys[m * kThreads + tid] = key[m];
-  __syncthreads();
-
-  // ---- radix select of the (Kb-3)-th largest key among candidates 1..NB-3
-  uint32_t prefix = 0u;
-  int krem = a.Kb - 3;
-  const int passes = krem > 0 ? 4 : 0;
-  if (krem == 0) prefix = 0xffffffffu;  // only the forced set is kept
-#pragma unroll 1
-  for (int pass = 0; pass < passes; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-    hist[tid] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int m0 = 0; m0 < KPT; m0 += CH) {
-      if (m0 < nper) {
-        uint32_t kc[CH];
-#pragma unroll
-        for (int m = 0; m < CH; ++m) kc[m] = keys[(m0 + m) * kThreads + tid];
-#pragma unroll
-        for (int m = 0; m < CH; ++m) {
-          const int b = tid + (m0 + m) * kThreads;
-          if (b >= 1 && b <= NB - 3 && (kc[m] & hmask) == prefix)
-            atomicAdd(&hist[(kc[m] >> shift) & 255u], 1);
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; find the bin holding the krem-th largest
-      int h[4], own = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { h[e] = hist[4 * lane + e]; own += h[e]; }
-      int above = own;  // inclusive suffix over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_down(above, o);
-        if (lane + o < 64) above += y;
-      }
-      int cum = above - own;
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        if (cum < krem && krem <= cum + h[e]) {
-          ctl[0] = 4 * lane + e;
-          ctl[1] = krem - cum;
-        }
-        cum += h[e];
-      }
-    }
-    __syncthreads();
-    prefix |= ((uint32_t)ctl[0]) << shift;
-    krem = ctl[1];
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;
-
-  // ---- ascending compaction: the forced set, keys > tau, the first krem keys == tau
-  int run_eq = 0, run_take = 0;
-#pragma unroll 1
-  for (int m0 = 0; m0 < nper; m0 += CH) {
-    uint32_t kc[CH];
-    bool eq[CH], take[CH];
-    int before[CH];
-#pragma unroll
-    for (int m = 0; m < CH; ++m) kc[m] = keys[(m0 + m) * kThreads + tid];
-#pragma unroll
-    for (int m = 0; m < CH; ++m) {
-      const int b = tid + (m0 + m) * kThreads;
-      eq[m] = b >= 1 && b <= NB - 3 && kc[m] == tau;
-    }
-    tile_prefix<CH>(eq, before, tcnt, run_eq);
-#pragma unroll
-    for (int m = 0; m < CH; ++m) {
-      const int b = tid + (m0 + m) * kThreads;
-      const bool cand = b >= 1 && b <= NB - 3;
-      const bool forced = b == 0 || (b >= NB - 2 && b < NB);
-      take[m] = forced || (cand && kc[m] > tau) || (eq[m] && before[m] < krem);
-    }
-    tile_prefix<CH>(take, before, tcnt, run_take);
-#pragma unroll
-    for (int m = 0; m < CH; ++m)
-      if (take[m]) sel[before[m]] = tid + (m0 + m) * kThreads;
-  }
-  if (tid == 0) a.n_sel[unit] = a.Kb;
-}
-
 }  // namespace
 
 template <int D, int G, int DM>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
-  extern __shared__ __align__(16) float lds[];
-  __shared__ int last;
+  __shared__ __align__(16) float cmb[kWaves * G * rec_words(D)];  // per-wave records
   constexpr int KC = D / 64;        // float4 chunks per lane per block (16 lanes per block)
   constexpr int ROWS = 4;           // blocks per lane: base + 4*row + (lane >> 4)
   constexpr int W = rec_words(D);
@@ -415,7 +176,6 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   }
 
   // ---- Mean compensation of every block of the group (kept ones removed later)
-  float* cmb = lds;  // [kWaves][G][W]
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float mx = -INFINITY;
@@ -467,12 +227,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     }
     co[idx] = val;
   }
-
-  if (!last_arriver(a.ctr + unit, a.C, &last)) return;
-  select_tail<G>(a, unit, NB, lds, score_big_words(G, MB));
 }
 
-hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, size_t lds, hipStream_t st) {
+hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const int gs = d / a.r;
   const int dm = gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
@@ -487,7 +244,7 @@ hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, size_t lds, hip
   CKNV_SCORE_CASE(128, 1) CKNV_SCORE_CASE(128, 2) CKNV_SCORE_CASE(128, 4) CKNV_SCORE_CASE(128, 8)
 #undef CKNV_SCORE_CASE
   if (!f) return hipErrorInvalidValue;
-  return hipLaunchKernel(f, dim3(U * a.C), dim3(kThreads), args, lds, st);
+  return hipLaunchKernel(f, dim3(U * a.C), dim3(kThreads), args, 0, st);
 }
 
 }  // namespace cknv

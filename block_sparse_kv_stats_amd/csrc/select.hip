@@ -1,0 +1,354 @@
+// Block selection: normalise the block scores and keep the forced set plus
+// the Top-(Kb-3) of the rest.
+//
+// CompKV page (onedev.kr/papers/157), "What differs": p̂_{g,b} is the
+// log-normal mass estimate normalised over all blocks,
+//   p̂_{g,b} = |b| exp(z̄ + σ̂²/2) / sum_c |c| exp(z̄_c + σ̂²_c/2),
+// S_b = sum_g p̂_{g,b} σ̂²_{g,b}; the first block and the two most recent
+// blocks are always kept and count against the budget; the remaining slots
+// go to the largest S_b (ties: lower block index).
+//
+// One 1024-thread workgroup per unit; thread t owns blocks t + 1024*m. The
+// score kernel left, per 16-block group, the partial (max, sum) of
+// a = ln|b| + z̄ + σ̂²/2 per query head and, per block,
+// u_{g,b} = exp(a - group max) σ̂². Here:
+//   1. LSE_g from the group partials; S_b = sum_g u_{g,b} exp(group max - LSE_g);
+//      the key of a block is the fp32 bit pattern of S_b (S_b >= 0, so keys
+//      order like values).
+//   2. A 2048-bin histogram of the candidates' (not forced) key top 11 bits;
+//      one wave finds the bin B holding the (Kb-3)-th largest key.
+//   3. Keys above B are kept. The keys inside B go to a short list that is
+//      ordered exactly by (key desc, index asc); its first `krem` are kept.
+//      If B holds more than kListMax keys (long runs of equal scores), two
+//      more radix passes (11 and 10 bits) pin the exact threshold key instead
+//      and equal keys are taken in index order.
+//   4. The kept blocks are written in ascending order (ballot prefix).
+#include "cknv_internal.h"
+
+namespace cknv {
+
+namespace {
+
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kListMax = 256;
+
+// Exclusive prefix over tiles of kSelThreads consecutive items (item order:
+// tile-major, then thread); bit m of `flags` is this thread's flag in tile m.
+// before[m] gets the number of flagged items ahead of this thread's item.
+// `cnt`: LDS scratch of NT*kSelWaves ints.
+template <int NT>
+__device__ __forceinline__ void tile_prefix(uint32_t flags, int (&before)[NT], int* cnt) {
+  constexpr int E = NT * kSelWaves;   // (tile, wave) entries in item order
+  constexpr int PER = (E + 63) / 64;  // entries per lane of wave 0
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < NT; ++m) {
+    const unsigned long long bal = __ballot((flags >> m) & 1u);
+    before[m] = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) cnt[m * kSelWaves + wave] = __popcll(bal);
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive scan of the E counts, in place
+    int v[PER], own = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = lane * PER + k;
+      v[k] = i < E ? cnt[i] : 0;
+      own += v[k];
+    }
+    int incl = own;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - own;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = lane * PER + k;
+      if (i < E) cnt[i] = run;
+      run += v[k];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < NT; ++m) before[m] += cnt[m * kSelWaves + wave];
+}
+
+// Wave 0: the bin of `hist` (NBINS bins, higher bin = larger keys) holding
+// the krem-th largest counted key; writes (bin, rank within the bin, count
+// in the bin) to ctl[0..2]. Lane l owns bins [l*PER, (l+1)*PER).
+template <int NBINS>
+__device__ __forceinline__ void find_bin(const int* hist, int krem, int* ctl) {
+  constexpr int PER = NBINS / 64, NC = PER / 4;
+  const int lane = threadIdx.x & 63;
+  const int4* h4 = reinterpret_cast<const int4*>(hist + lane * PER);
+  int cs[NC], own = 0;  // per int4 chunk of bins
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int4 v = h4[i];
+    cs[i] = v.x + v.y + v.z + v.w;
+    own += cs[i];
+  }
+  int above = own;  // inclusive suffix over lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(above, o);
+    if (lane + o < 64) above += y;
+  }
+  int cum = above - own;  // keys in bins of higher lanes
+  if (cum < krem && krem <= cum + own) {  // this lane holds the bin
+    int ci = 0, cb = cum;                  // chunk holding it, keys above that chunk
+    int c = cum;
+#pragma unroll
+    for (int i = NC - 1; i >= 0; --i) {
+      if (c < krem && krem <= c + cs[i]) { ci = i; cb = c; }
+      c += cs[i];
+    }
+    const int4 v = h4[ci];
+    const int hv[4] = {v.x, v.y, v.z, v.w};
+    c = cb;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      if (c < krem && krem <= c + hv[e]) {
+        ctl[0] = lane * PER + 4 * ci + e;
+        ctl[1] = krem - c;
+        ctl[2] = hv[e];
+      }
+      c += hv[e];
+    }
+  }
+}
+
+}  // namespace
+
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
+  constexpr int KPT = kSelKeysPerThread;
+  constexpr int NW = KPT * kSelThreads / 32;  // words of the kept-block bitmap
+  __shared__ float f[kSelMaxGroups * G];      // exp(group max - LSE_g)
+  __shared__ float red[kSelWaves * G * 2];
+  __shared__ __align__(16) int hist[2048];
+  __shared__ int cnt[KPT * kSelWaves];
+  __shared__ uint32_t lkey[kListMax];
+  __shared__ int lidx[kListMax];
+  __shared__ uint32_t keep_bits[NW];
+  __shared__ int ctl[8];
+
+  const int unit = blockIdx.x, s = unit / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int MB = a.max_blocks;
+  int32_t* sel = a.sel + (size_t)unit * a.Kb;
+  const float* grp = a.grp + (size_t)unit * a.NG * G * 2;
+  const float* u = a.u + (size_t)unit * MB * G;
+
+  // ---- loads, issued before the context length is known (clamped to max_blocks)
+  const int T = a.seq_len[s];
+  float gr[G], gl[G];
+  {
+    const int gc = tid < a.NG ? tid : a.NG - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float2 v = reinterpret_cast<const float2*>(grp)[(size_t)gc * G + g];
+      gr[g] = v.x;
+      gl[g] = v.y;
+    }
+  }
+  constexpr int UB0 = 4;  // blocks of u per thread per batch
+  float ub[UB0][G];
+#pragma unroll
+  for (int m = 0; m < UB0; ++m) {
+    const int b = tid + m * kSelThreads;
+    const int bc = b < MB ? b : MB - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) ub[m][g] = u[(size_t)bc * G + g];
+  }
+  hist[tid] = 0;
+  hist[tid + kSelThreads] = 0;
+  if (tid < NW) keep_bits[tid] = 0u;
+  if (tid == 0) ctl[3] = 0;  // list length
+
+  int NB = (T + kBlock - 1) / kBlock;
+  NB = NB < MB ? NB : MB;
+  if (NB == 0) {
+    if (tid == 0) a.n_sel[unit] = 0;
+    return;
+  }
+  const int NGu = (NB + kBlocksPerWave - 1) / kBlocksPerWave;
+  const int nper = (NB + kSelThreads - 1) / kSelThreads;
+  const int Kb = a.Kb;
+  const bool all = NB <= Kb;
+  int krem = Kb - 3;
+
+  // ---- LSE_g over all blocks, f = exp(group max - LSE_g)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float r = tid < NGu ? gr[g] : -INFINITY;
+    const float l = tid < NGu ? gl[g] : 0.f;
+    const float Mw = group_max<64>(r);
+    const float Lw = group_sum<64>(l * rescale(r, Mw));
+    if (lane == 0) { red[(wave * G + g) * 2] = Mw; red[(wave * G + g) * 2 + 1] = Lw; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) M = fmaxf(M, red[(w * G + g) * 2]);
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) L += red[(w * G + g) * 2 + 1] * rescale(red[(w * G + g) * 2], M);
+    if (tid < NGu) f[tid * G + g] = __expf(gr[g] - (M + __logf(L)));
+  }
+  __syncthreads();
+
+  // ---- S_b, its key, and the histogram of the candidates' key top 11 bits
+  uint32_t key[KPT];
+  uint32_t candm = 0u;  // bit m: block tid + 1024*m is a candidate (not forced, in range)
+  const bool count = !all && krem > 0;
+  float* scores = a.scores ? a.scores + (size_t)unit * a.cap_blocks : nullptr;
+#pragma unroll
+  for (int m0 = 0; m0 < KPT; m0 += UB0) {
+    if (m0 > 0 && m0 < nper) {
+#pragma unroll
+      for (int m = 0; m < UB0; ++m) {
+        const int b = tid + (m0 + m) * kSelThreads;
+        const int bc = b < NB ? b : NB - 1;
+#pragma unroll
+        for (int g = 0; g < G; ++g) ub[m][g] = u[(size_t)bc * G + g];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < UB0; ++m) {
+      const int b = tid + (m0 + m) * kSelThreads;
+      const int bc = b < NB ? b : NB - 1;
+      float S = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) S += ub[m][g] * f[(bc >> 4) * G + g];
+      key[m0 + m] = (b < NB && S > 0.f) ? __float_as_uint(S) : 0u;
+      const bool c = b >= 1 && b <= NB - 3;
+      candm |= (uint32_t)c << (m0 + m);
+      if (scores && b < NB) scores[b] = S;
+      if (c && count) atomicAdd(&hist[key[m0 + m] >> 21], 1);
+    }
+  }
+  if (all) {
+    for (int b = tid; b < NB; b += kSelThreads) sel[b] = b;
+    if (tid == 0) a.n_sel[unit] = NB;
+    return;
+  }
+
+  // ---- threshold bin: keys whose top 11 bits exceed tau_bin are kept
+  uint32_t tau_bin = 0xffffffffu;
+  bool use_list = true;
+  if (krem > 0) {
+    __syncthreads();
+    if (wave == 0) find_bin<2048>(hist, krem, ctl);
+    __syncthreads();
+    tau_bin = (uint32_t)ctl[0];
+    krem = ctl[1];
+    use_list = ctl[2] <= kListMax;
+  }
+
+  uint32_t exact_tau = 0u;  // long-tie path: exact threshold key, ties by index
+  if (krem > 0 && use_list) {
+    // the pivot bin's keys, ordered exactly; the first krem are kept
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      if (((candm >> m) & 1u) && (key[m] >> 21) == tau_bin) {
+        const int slot = atomicAdd(&ctl[3], 1);
+        lkey[slot] = key[m];
+        lidx[slot] = tid + m * kSelThreads;
+      }
+    }
+    __syncthreads();
+    const int n = ctl[3];
+    if (tid < n) {
+      const uint32_t ki = lkey[tid];
+      const int ii = lidx[tid];
+      int rank = 0;
+      for (int j0 = 0; j0 < n; j0 += 8) {
+        uint32_t kj[8];
+        int ij[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kj[e] = j0 + e < n ? lkey[j0 + e] : 0u;
+          ij[e] = j0 + e < n ? lidx[j0 + e] : 0x7fffffff;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rank += (kj[e] > ki) || (kj[e] == ki && ij[e] < ii);
+      }
+      if (rank < krem) atomicOr(&keep_bits[ii >> 5], 1u << (ii & 31));
+    }
+    __syncthreads();
+  } else if (krem > 0) {
+    uint32_t prefix = tau_bin << 21;
+    // bits 20..10 among the keys of the pivot bin
+    hist[tid] = 0;
+    hist[tid + kSelThreads] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < KPT; ++m)
+      if (((candm >> m) & 1u) && (key[m] >> 21) == (prefix >> 21)) atomicAdd(&hist[(key[m] >> 10) & 2047u], 1);
+    __syncthreads();
+    if (wave == 0) find_bin<2048>(hist, krem, ctl);
+    __syncthreads();
+    prefix |= ((uint32_t)ctl[0]) << 10;
+    krem = ctl[1];
+    // bits 9..0
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < KPT; ++m)
+      if (((candm >> m) & 1u) && (key[m] >> 10) == (prefix >> 10)) atomicAdd(&hist[key[m] & 1023u], 1);
+    __syncthreads();
+    if (wave == 0) find_bin<1024>(hist, krem, ctl);
+    __syncthreads();
+    prefix |= (uint32_t)ctl[0];
+    krem = ctl[1];
+    exact_tau = prefix;
+  }
+
+  // ---- ascending compaction of the kept blocks
+  int before[KPT];
+  uint32_t eqm = 0u;
+  const bool ties_by_index = !use_list && krem > 0;
+  if (ties_by_index) {
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) eqm |= (uint32_t)(((candm >> m) & 1u) && key[m] == exact_tau) << m;
+    __syncthreads();
+    tile_prefix<KPT>(eqm, before, cnt);
+    __syncthreads();
+  }
+  uint32_t takem = 0u;
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) {
+    const int b = tid + m * kSelThreads;
+    const bool forced = b == 0 || (b >= NB - 2 && b < NB);
+    const bool c = (candm >> m) & 1u;
+    bool t = forced;
+    if (ties_by_index || !use_list) {
+      t = t || (c && key[m] > exact_tau) || (((eqm >> m) & 1u) && before[m] < krem);
+    } else {
+      t = t || (c && (key[m] >> 21) > tau_bin) || ((keep_bits[b >> 5] >> (b & 31)) & 1u);
+    }
+    takem |= (uint32_t)t << m;
+  }
+  tile_prefix<KPT>(takem, before, cnt);
+#pragma unroll
+  for (int m = 0; m < KPT; ++m)
+    if ((takem >> m) & 1u) sel[before[m]] = tid + m * kSelThreads;
+  if (tid == 0) a.n_sel[unit] = Kb;
+}
+
+hipError_t launch_select(int G, const SelectArgs& a, int U, hipStream_t st) {
+  void* args[] = {(void*)&a};
+  const void* f = G == 1 ? (const void*)select_kernel<1>
+                : G == 2 ? (const void*)select_kernel<2>
+                : G == 4 ? (const void*)select_kernel<4>
+                : G == 8 ? (const void*)select_kernel<8> : nullptr;
+  if (!f) return hipErrorInvalidValue;
+  return hipLaunchKernel(f, dim3(U), dim3(kSelThreads), args, 0, st);
+}
+
+}  // namespace cknv

@@ -73,7 +73,8 @@ def test_bad_sizes(mb, budget, code):
 
 
 def test_too_many_blocks_for_lds_is_unsupported():
-    assert wsize(shape(cap_blocks=1 << 16), 1 << 16, 512)[0] == cknv.EUNSUPPORTED
+    assert wsize(shape(cap_blocks=1 << 16), 12289, 512)[0] == cknv.EUNSUPPORTED
+    assert wsize(shape(cap_blocks=1 << 16), 12288, 512)[0] == cknv.OK
 
 
 def cache_struct(null=None):

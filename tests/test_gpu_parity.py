@@ -182,6 +182,40 @@ def test_constant_blocks_tie_to_lower_index():
     assert torch.all(dec.scores[:, :, :50] == 0)
 
 
+def test_long_ties_take_lowest_indices():
+    """600 blocks of identical keys: every S_b is 0, far more tied candidates
+    than the exact-ranking list holds, so the selection pins the threshold
+    with extra radix passes and takes the tied blocks in index order."""
+    NBk = 600
+    w = synth.Workload("const-long", 82, S=1, H=2, G=4, d=64, r=4, budget=160,
+                       prefill=(16 * NBk - 1,), steps=1, needles=False)
+    data = synth.gen_layer(w)
+    k = data["k"]
+    for b in range(NBk):
+        k[:, :, 16 * b:16 * b + 16] = k[:, :, 16 * b:16 * b + 1]
+    cache = gu.upload(w, data, max_blocks=NBk)
+    dec = cknv.DecodeStep(cache, NBk, w.budget, want_scores=True)
+    step_and_check(w, data, cache, dec, 0, check_summaries=False)
+    sel = dec.sel.cpu().numpy()
+    for u in range(2):
+        assert sel[u].tolist() == list(range(8)) + [NBk - 2, NBk - 1]
+
+
+def test_mixed_ties_at_the_cut():
+    """Half the blocks constant (score 0), the rest noisy, with the budget
+    reaching into the zero-score run: the cut falls inside a long tie."""
+    NBk = 700
+    w = synth.Workload("mixed-ties", 83, S=1, H=2, G=4, d=64, r=4, budget=16 * 400,
+                       prefill=(16 * NBk - 1,), steps=1, needles=False)
+    data = synth.gen_layer(w)
+    k = data["k"]
+    for b in range(0, NBk, 2):
+        k[:, :, 16 * b:16 * b + 16] = k[:, :, 16 * b:16 * b + 1]
+    cache = gu.upload(w, data, max_blocks=NBk)
+    dec = cknv.DecodeStep(cache, NBk, w.budget, want_scores=True)
+    step_and_check(w, data, cache, dec, 0, check_summaries=False)
+
+
 @pytest.mark.parametrize("d,G,r", [(64, 1, 1), (64, 2, 16), (64, 8, 64), (128, 1, 8),
                                    (128, 2, 32), (128, 8, 4), (128, 4, 64), (64, 4, 2)])
 def test_shape_variants(d, G, r):
