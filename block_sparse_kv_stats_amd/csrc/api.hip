@@ -37,9 +37,9 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   Plan q{};
   q.U = sh->S * sh->H;
   q.NBmax = max_blocks;
-  q.NG = (max_blocks + kBlocksPerWave - 1) / kBlocksPerWave;
+  q.NG = (max_blocks + score_bpw(G) - 1) / score_bpw(G);
   q.Kb = budget_tokens / kBlock;
-  q.C = (max_blocks + kBlocksPerWG - 1) / kBlocksPerWG;
+  q.C = (max_blocks + score_bpwg(G) - 1) / score_bpwg(G);
   const int per_wg = kWaves;  // kept blocks per attend workgroup (one per wave)
   q.P = (q.Kb + per_wg - 1) / per_wg;
   const int pc = (q.C + kMaxChunksPerAttendWG - 1) / kMaxChunksPerAttendWG;

@@ -13,15 +13,18 @@ namespace cknv {
 constexpr int kBlock = 16;          // tokens per block (CompKV page, "Assumptions and limits")
 constexpr int kThreads = 256;       // threads per workgroup of the score and attend kernels
 constexpr int kWaves = kThreads / 64;
-constexpr int kBlocksPerWave = 16;  // one 16-block score group per wave
-constexpr int kBlocksPerWG = kWaves * kBlocksPerWave;  // blocks per score workgroup (64)
+// Score-kernel geometry: a wave covers 4 blocks per row (16 lanes each) and
+// score_rows(G) rows, so that rows x G = 16 (clamped to 2..4 rows) and the
+// transposed reduction leaves one (block, query head) per lane.
+__host__ __device__ constexpr int score_rows(int G) { return G >= 8 ? 2 : 4; }
+__host__ __device__ constexpr int score_bpw(int G) { return 4 * score_rows(G); }    // blocks per wave
+__host__ __device__ constexpr int score_bpwg(int G) { return 4 * score_bpw(G); }   // blocks per workgroup
 constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
 constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
 constexpr int kDenseMaxWGs = 64;          // dense attention: workgroups per unit (at most)
 constexpr int kSelThreads = 1024;       // selection: one workgroup per unit
 constexpr int kSelKeysPerThread = 12;   // blocks per selection thread: max_blocks <= 12288
-constexpr int kSelMaxGroups = 1024;     // 16-block groups the selection can normalise
 
 // A partial softmax record (per unit, part and query head): running max m,
 // normaliser l, two pad words, then the weighted value sum acc[d]; the pad
@@ -32,9 +35,9 @@ __host__ __device__ constexpr int rec_words(int d) { return d + 4; }
 struct Plan {
   int U;            // units = S*H
   int NBmax;        // max_blocks
-  int NG;           // 16-block score groups per unit = ceil(NBmax/16)
+  int NG;           // score groups per unit (one per score wave) = ceil(NBmax/score_bpw(G))
   int Kb;           // block slots of the budget
-  int C;            // score workgroups per unit (64 blocks each)
+  int C;            // score workgroups per unit = ceil(NBmax/score_bpwg(G))
   int P;            // attend workgroups per unit
   int Pd;           // dense-attend workgroups per unit
   int BPW;          // dense-attend blocks per workgroup
@@ -59,6 +62,7 @@ struct ScoreArgs {
   const int32_t* seq_len; const float* q;
   float* grp; float* u; float* comp;
   int S, H, r, cap_blocks, max_blocks, NG, C, xcd;
+  int closed_only;  // 1: score only blocks closed before this step's token (fused step)
   float isd;  // 1/sqrt(d)
 };
 
@@ -103,6 +107,9 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kDppQuadRev = 0x1B;     // quad_perm [3,2,1,0]
+constexpr int kDppRor8 = 0x128;       // row_ror:8, lane i <- lane (i+8)%16 (xor 8)
+constexpr int kDppBcast0 = 0x150;     // row_newbcast:k = kDppBcast0 + k, lane k of each row to the row
 
 __device__ __forceinline__ float swap16_lo(float x, float& hi) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -75,12 +75,76 @@ struct DbarTile<kDbarQuad, ROWS, KC> {
 
 }  // namespace
 
+// Partner across lane bit K (distance 2^K) inside a 16-lane row.
+template <int K>
+__device__ __forceinline__ float xlane(float x) {
+  if constexpr (K == 0) return dpp<kDppXor1>(x);
+  else if constexpr (K == 1) return dpp<kDppXor2>(x);
+  else if constexpr (K == 2) return dpp<kDppQuadRev>(dpp<kDppHalfMirror>(x));  // xor 7, then xor 3
+  else return dpp<kDppRor8>(x);
+}
+
+// One butterfly step over lane bit K on x[0..N): plain (every lane sums
+// every value with its partner) or transposed (pairs x[m], x[m+N/2]; lanes
+// with bit K clear keep the sum of the lower one, lanes with it set the
+// upper one, so the count halves).
+template <int K, int N, int CAP>
+__device__ __forceinline__ void plain_step(float (&x)[CAP]) {
+#pragma unroll
+  for (int m = 0; m < N; ++m) x[m] += xlane<K>(x[m]);
+}
+template <int K, int N, int CAP>
+__device__ __forceinline__ void transposed_step(float (&x)[CAP], bool hi) {
+#pragma unroll
+  for (int m = 0; m < N / 2; ++m) {
+    const float A = x[m], B = x[m + N / 2];
+    x[m] = (hi ? B : A) + xlane<K>(hi ? A : B);
+  }
+}
+
+// Sum over the 16 lanes of each row of 2*NP values per lane, value index
+// p + 2*i (p in {0,1}, i < NP). Afterwards x[0], x[1] of lane j hold the sums
+// for i = j & (NP-1).
+template <int NP, int CAP>
+__device__ __forceinline__ void reduce_rows16(float (&x)[CAP], int j) {
+  constexpr int N = 2 * NP;
+  if constexpr (NP < 16) plain_step<3, N>(x);
+  if constexpr (NP < 8) plain_step<2, N>(x);
+  if constexpr (NP < 4) plain_step<1, N>(x);
+  if constexpr (NP >= 16) transposed_step<3, N>(x, (j & 8) != 0);
+  if constexpr (NP >= 8) transposed_step<2, (NP >= 16 ? N / 2 : N)>(x, (j & 4) != 0);
+  if constexpr (NP >= 4) transposed_step<1, (NP >= 16 ? N / 4 : NP >= 8 ? N / 2 : N)>(x, (j & 2) != 0);
+  transposed_step<0, 4>(x, (j & 1) != 0);
+}
+
+// Max / sum over the SEG consecutive lanes (SEG = 2 or 4) of each aligned segment.
+template <int SEG>
+__device__ __forceinline__ float seg_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  if constexpr (SEG >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  return x;
+}
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  if constexpr (SEG >= 4) x += dpp<kDppXor2>(x);
+  return x;
+}
+
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) { return dpp<kDppBcast0 + L>(x); }
+
 template <int D, int G, int DM>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
-  __shared__ __align__(16) float cmb[kWaves * G * rec_words(D)];  // per-wave records
-  constexpr int KC = D / 64;        // float4 chunks per lane per block (16 lanes per block)
-  constexpr int ROWS = 4;           // blocks per lane: base + 4*row + (lane >> 4)
+  constexpr int KC = D / 64;              // float4 chunks per lane per block (16 lanes per block)
+  constexpr int E = 4 * KC;               // coordinates per lane
+  constexpr int ROWS = score_rows(G);     // blocks per lane: base + 4*row + (lane >> 4)
+  constexpr int NP = ROWS * G;            // (row, head) pairs of a 16-lane row
+  constexpr int BPW = score_bpw(G), BPWG = score_bpwg(G);
   constexpr int W = rec_words(D);
+  constexpr int NA = G * E;               // compensation sums per lane before the cross-row step
+  __shared__ __align__(16) float cacc[kWaves * G * D];  // per-wave compensation sums
+  __shared__ float cml[kWaves * G * 2];                 // per-wave (max, normaliser)
 
   int unit, chunk;
   map_wg(blockIdx.x, a.S * a.H, a.C, a.xcd, unit, chunk);
@@ -88,11 +152,15 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bg = lane >> 4, j = lane & 15;
   const int r = a.r, MB = a.max_blocks;
-  const int base = chunk * kBlocksPerWG + wave * kBlocksPerWave;
+  const int base = chunk * BPWG + wave * BPW;
   const size_t ubase = (size_t)unit * a.cap_blocks;
+  // After the transposed reduction this lane holds block tb, query head tg.
+  const int pj = j & (NP - 1);
+  const int trow = pj % ROWS, tg = pj / ROWS;
+  const int tb = base + 4 * trow + bg;
 
   // ---- every load of the workgroup, issued before any result is needed.
-  // Block indices are clamped into [0, MB); blocks past the context are
+  // Block indices are clamped into [0, MB); blocks past the scored range are
   // masked once seq_len has arrived.
   const int T = a.seq_len[s];
   float4 qv[G][KC];
@@ -103,16 +171,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
 #pragma unroll
       for (int i = 0; i < KC; ++i) qv[g][i] = q4[g * (D / 4) + j + 16 * i];
   }
-  int blk[ROWS];
   float4 kv[ROWS][KC], vv[ROWS][KC];
   DbarTile<DM, ROWS, KC> dt;
-  float n[ROWS];
   const float4* kbar4 = reinterpret_cast<const float4*>(a.kbar);
   const float4* vbar4 = reinterpret_cast<const float4*>(a.vbar);
 #pragma unroll
   for (int rw = 0; rw < ROWS; ++rw) {
-    blk[rw] = base + 4 * rw + bg;
-    const size_t row = ubase + (blk[rw] < MB ? blk[rw] : MB - 1);
+    const int b = base + 4 * rw + bg;
+    const size_t row = ubase + (b < MB ? b : MB - 1);
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const int c = j + 16 * i;  // float4 chunk: coordinates 4c..4c+3
@@ -120,19 +186,19 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
       vv[rw][i] = vbar4[row * (D / 4) + c];
       dt.load(a.dbar, row, c, r, D, rw, i);
     }
-    n[rw] = a.cnt[row];
   }
+  const float n = a.cnt[ubase + (tb < MB ? tb : MB - 1)];
+  // Keep the load block above: without this the scheduler sinks loads next
+  // to their uses and the wave pays several dependent memory round trips.
+  __builtin_amdgcn_sched_barrier(0);
 
-  int NB = (T + kBlock - 1) / kBlock;
+  int NB = a.closed_only ? T / kBlock : (T + kBlock - 1) / kBlock;
   NB = NB < MB ? NB : MB;
-  bool v[ROWS];
-#pragma unroll
-  for (int rw = 0; rw < ROWS; ++rw) v[rw] = blk[rw] < NB;
-  const bool any = base < NB;
   const float invd = 1.0f / (float)D;
 
-  // ---- z̄ and σ̂² per (row, g): partial over the lane's coordinates, then the 16 lanes
-  float z[ROWS][G], s2[ROWS][G];
+  // ---- z̄ and σ̂² partials over the lane's coordinates for every (row, head),
+  // then summed over the block's 16 lanes, transposed: lane j ends with (tb, tg).
+  float x[2 * NP];
 #pragma unroll
   for (int rw = 0; rw < ROWS; ++rw) {
 #pragma unroll
@@ -143,72 +209,79 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
         zp += dot4(kv[rw][i], qv[g][i]);
         sp += dt.qsq_dot(qv[g][i], rw, i);
       }
-      z[rw][g] = group_sum<16>(zp) * a.isd;
-      s2[rw][g] = group_sum<16>(sp) * invd;
+      x[2 * (rw + ROWS * g)] = zp;
+      x[2 * (rw + ROWS * g) + 1] = sp;
     }
   }
+  reduce_rows16<NP>(x, j);
+  const bool tv = tb < NB && j < NP;  // a valid block, and not a duplicate lane (NP < 16)
+  const float z = x[0] * a.isd, s2 = x[1] * invd;
 
-  // ---- scoring partials of this wave's 16-block group
-  const int gi = base / kBlocksPerWave;
-  float* uo = a.u + (size_t)unit * MB * G;
-  float* go = a.grp + (size_t)unit * a.NG * G * 2;
-  float ln[ROWS];
-#pragma unroll
-  for (int rw = 0; rw < ROWS; ++rw) ln[rw] = __logf(v[rw] ? n[rw] : 1.f);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float av[ROWS], mx = -INFINITY;
-#pragma unroll
-    for (int rw = 0; rw < ROWS; ++rw) {
-      av[rw] = v[rw] ? ln[rw] + z[rw][g] + 0.5f * s2[rw][g] : -INFINITY;
-      mx = fmaxf(mx, av[rw]);
-    }
-    const float ref = rows_max(mx);
-    float l = 0.f;
-#pragma unroll
-    for (int rw = 0; rw < ROWS; ++rw) {
-      const float e = v[rw] ? __expf(av[rw] - ref) : 0.f;
-      l += e;
-      if (j == g && v[rw]) uo[(size_t)blk[rw] * G + g] = e * s2[rw][g];
-    }
-    l = rows_sum(l);
-    if (any && lane == g) reinterpret_cast<float2*>(go)[(size_t)gi * G + g] = make_float2(ref, l);
+  // ---- scoring partials of this wave's group: a = ln|b| + z̄ + σ̂²/2
+  {
+    const float av = tv ? __logf(n) + z + 0.5f * s2 : -INFINITY;
+    const float ref = rows_max(seg_max<ROWS>(av));
+    const float e = tv ? __expf(av - ref) : 0.f;
+    const float l = rows_sum(seg_sum<ROWS>(e));
+    if (tv) a.u[((size_t)unit * MB + tb) * G + tg] = e * s2;
+    if (base < NB && lane < NP && trow == 0)
+      reinterpret_cast<float2*>(a.grp)[((size_t)unit * a.NG + base / BPW) * G + tg] = make_float2(ref, l);
   }
 
-  // ---- Mean compensation of every block of the group (kept ones removed later)
+  // ---- Mean compensation of every block of the wave (kept ones are removed later)
+  const float mz = rows_max(seg_max<ROWS>(tv ? z : -INFINITY));
+  const float w = tv ? n * __expf(z - mz) : 0.f;
+  const float lz = rows_sum(seg_sum<ROWS>(w));
+  float y[NA];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float mx = -INFINITY;
+  for (int m = 0; m < NA; ++m) y[m] = 0.f;
 #pragma unroll
-    for (int rw = 0; rw < ROWS; ++rw) mx = fmaxf(mx, v[rw] ? z[rw][g] : -INFINITY);
-    const float mz = rows_max(mx);
-    float w[ROWS], lz = 0.f;
+  for (int rw = 0; rw < ROWS; ++rw) {
+    const bool rv = base + 4 * rw + bg < NB;  // the mean value of an unscored block may be anything
 #pragma unroll
-    for (int rw = 0; rw < ROWS; ++rw) {
-      w[rw] = v[rw] ? n[rw] * __expf(z[rw][g] - mz) : 0.f;
-      lz += w[rw];
-    }
-    lz = rows_sum(lz);
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int rw = 0; rw < ROWS; ++rw) {
-        const float wr = w[rw];
-        acc.x += wr * (v[rw] ? vv[rw][i].x : 0.f);
-        acc.y += wr * (v[rw] ? vv[rw][i].y : 0.f);
-        acc.z += wr * (v[rw] ? vv[rw][i].z : 0.f);
-        acc.w += wr * (v[rw] ? vv[rw][i].w : 0.f);
+    for (int g = 0; g < G; ++g) {
+      float wb;
+      // w of (row rw, head g) lives in lane rw + ROWS*g of this 16-lane row
+#define CKNV_BC(L) case L: wb = row_bcast<(L < NP ? L : 0)>(w); break;
+      switch (rw + ROWS * g) {
+        CKNV_BC(0) CKNV_BC(1) CKNV_BC(2) CKNV_BC(3) CKNV_BC(4) CKNV_BC(5) CKNV_BC(6) CKNV_BC(7)
+        CKNV_BC(8) CKNV_BC(9) CKNV_BC(10) CKNV_BC(11) CKNV_BC(12) CKNV_BC(13) CKNV_BC(14) CKNV_BC(15)
+        default: wb = 0.f;
       }
-      acc.x = rows_sum(acc.x);
-      acc.y = rows_sum(acc.y);
-      acc.z = rows_sum(acc.z);
-      acc.w = rows_sum(acc.w);
-      if (bg == 0) reinterpret_cast<float4*>(cmb + (wave * G + g) * W + 4)[j + 16 * i] = acc;
+#undef CKNV_BC
+#pragma unroll
+      for (int i = 0; i < KC; ++i) {
+        const float4 v4 = vv[rw][i];
+        y[g * E + 4 * i + 0] += wb * (rv ? v4.x : 0.f);
+        y[g * E + 4 * i + 1] += wb * (rv ? v4.y : 0.f);
+        y[g * E + 4 * i + 2] += wb * (rv ? v4.z : 0.f);
+        y[g * E + 4 * i + 3] += wb * (rv ? v4.w : 0.f);
+      }
     }
-    if (lane == 0) {
-      cmb[(wave * G + g) * W] = mz;
-      cmb[(wave * G + g) * W + 1] = lz;
+  }
+  // Sum over the 4 rows of the wave, transposed: rows keep NA/4 values each.
+#pragma unroll
+  for (int m = 0; m < NA / 2; ++m) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[m]), __float_as_uint(y[m + NA / 2]), false, false);
+    y[m] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+#pragma unroll
+  for (int m = 0; m < NA / 4; ++m) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[m]), __float_as_uint(y[m + NA / 4]), false, false);
+    y[m] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  // Value m of this lane is index v = (bg&1)*NA/2 + (bg>>1)*NA/4 + m = g*E + e.
+  {
+    const int v0 = (bg & 1) * (NA / 2) + (bg >> 1) * (NA / 4);
+    float* cw = cacc + wave * G * D;
+#pragma unroll
+    for (int m = 0; m < NA / 4; ++m) {
+      const int v = v0 + m, g = v / E, e = v % E;
+      cw[g * D + 4 * (j + 16 * (e / 4)) + (e % 4)] = y[m];
+    }
+    if (bg == 0 && lane < NP && trow == 0) {
+      cml[(wave * G + tg) * 2] = mz;
+      cml[(wave * G + tg) * 2 + 1] = lz;
     }
   }
   __syncthreads();
@@ -217,13 +290,16 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     const int g = idx / W, e = idx - g * W;
     float mw[kWaves], M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) { mw[w] = cmb[(w * G + g) * W]; M = fmaxf(M, mw[w]); }
+    for (int q = 0; q < kWaves; ++q) { mw[q] = cml[(q * G + g) * 2]; M = fmaxf(M, mw[q]); }
     float val = 0.f;
     if (e == 0) {
       val = M;
-    } else if (e == 1 || e >= 4) {
+    } else if (e == 1) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) val += cmb[(w * G + g) * W + e] * rescale(mw[w], M);
+      for (int q = 0; q < kWaves; ++q) val += cml[(q * G + g) * 2 + 1] * rescale(mw[q], M);
+    } else if (e >= 4) {
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) val += cacc[(q * G + g) * D + e - 4] * rescale(mw[q], M);
     }
     co[idx] = val;
   }

@@ -126,7 +126,9 @@ template <int G>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   constexpr int KPT = kSelKeysPerThread;
   constexpr int NW = KPT * kSelThreads / 32;  // words of the kept-block bitmap
-  __shared__ float f[kSelMaxGroups * G];      // exp(group max - LSE_g)
+  constexpr int BPW = score_bpw(G);              // blocks per score group
+  constexpr int NGmax = kSelThreads * kSelKeysPerThread / BPW;
+  __shared__ float f[NGmax * G];                 // exp(group max - LSE_g)
   __shared__ float red[kSelWaves * G * 2];
   __shared__ __align__(16) int hist[2048];
   __shared__ int cnt[KPT * kSelWaves];
@@ -144,14 +146,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
   // ---- loads, issued before the context length is known (clamped to max_blocks)
   const int T = a.seq_len[s];
-  float gr[G], gl[G];
-  {
-    const int gc = tid < a.NG ? tid : a.NG - 1;
+  constexpr int GPT = (NGmax + kSelThreads - 1) / kSelThreads;  // score groups per thread
+  float gr[GPT][G], gl[GPT][G];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    const int gi = tid + k * kSelThreads;
+    const int gc = gi < a.NG ? gi : a.NG - 1;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float2 v = reinterpret_cast<const float2*>(grp)[(size_t)gc * G + g];
-      gr[g] = v.x;
-      gl[g] = v.y;
+      gr[k][g] = v.x;
+      gl[k][g] = v.y;
     }
   }
   constexpr int UB0 = 4;  // blocks of u per thread per batch
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     if (tid == 0) a.n_sel[unit] = 0;
     return;
   }
-  const int NGu = (NB + kBlocksPerWave - 1) / kBlocksPerWave;
+  const int NGu = (NB + BPW - 1) / BPW;
   const int nper = (NB + kSelThreads - 1) / kSelThreads;
   const int Kb = a.Kb;
   const bool all = NB <= Kb;
@@ -183,10 +188,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   // ---- LSE_g over all blocks, f = exp(group max - LSE_g)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float r = tid < NGu ? gr[g] : -INFINITY;
-    const float l = tid < NGu ? gl[g] : 0.f;
+    float r = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) r = fmaxf(r, tid + k * kSelThreads < NGu ? gr[k][g] : -INFINITY);
     const float Mw = group_max<64>(r);
-    const float Lw = group_sum<64>(l * rescale(r, Mw));
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+      l += tid + k * kSelThreads < NGu ? gl[k][g] * rescale(gr[k][g], Mw) : 0.f;
+    const float Lw = group_sum<64>(l);
     if (lane == 0) { red[(wave * G + g) * 2] = Mw; red[(wave * G + g) * 2 + 1] = Lw; }
   }
   __syncthreads();
@@ -198,7 +208,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) L += red[(w * G + g) * 2 + 1] * rescale(red[(w * G + g) * 2], M);
-    if (tid < NGu) f[tid * G + g] = __expf(gr[g] - (M + __logf(L)));
+    const float lse = M + __logf(L);
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+      if (tid + k * kSelThreads < NGu) f[(tid + k * kSelThreads) * G + g] = __expf(gr[k][g] - lse);
   }
   __syncthreads();
 
@@ -224,7 +237,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       const int bc = b < NB ? b : NB - 1;
       float S = 0.f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) S += ub[m][g] * f[(bc >> 4) * G + g];
+      for (int g = 0; g < G; ++g) S += ub[m][g] * f[(bc / BPW) * G + g];
       key[m0 + m] = (b < NB && S > 0.f) ? __float_as_uint(S) : 0u;
       const bool c = b >= 1 && b <= NB - 3;
       candm |= (uint32_t)c << (m0 + m);
