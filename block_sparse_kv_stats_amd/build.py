@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libcknv.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "summary.hip", "score.hip", "select.hip", "attend.hip"]
+SOURCES = ["api.hip", "summary.hip", "score.hip", "select.hip", "attend.hip", "step.hip"]
 ARCH = "gfx950"
 
 

@@ -52,6 +52,8 @@ SIGNATURES = {
                     P],
     "cknv_dense_attend": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, I32, I32, P, P, P, SZ,
                           P],
+    "cknv_decode_step": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P, I32, I32, P, P, P,
+                         P, P, P, SZ, P],
 }
 
 
@@ -224,6 +226,25 @@ def dense_attend(cache: LayerCache, q, max_blocks: int, budget: int, out, ws, ls
         _stream(stream)), "cknv_dense_attend")
 
 
+def decode_step(cache: LayerCache, new_k, new_v, q, budget: int, max_blocks: int, sel, n_sel,
+                out, ws, lse=None, scores=None, stream=None):
+    """cknv_decode_step: append + score/select + attend in one call."""
+    import torch
+    s = cache.shape
+    Kb = budget // BLOCK
+    nq = s.S * s.H * s.G
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    c = cache.c_struct()
+    _check(lib().cknv_decode_step(
+        ctypes.byref(s), ctypes.byref(c), _ptr(new_k, bf, s.S * s.H * s.d, "new_k"),
+        _ptr(new_v, bf, s.S * s.H * s.d, "new_v"), _ptr(q, (torch.float32,), nq * s.d, "q"),
+        budget, max_blocks, _ptr(scores, (torch.float32,), s.S * s.H * s.cap_blocks, "scores"),
+        _ptr(sel, (torch.int32,), s.S * s.H * Kb, "sel"),
+        _ptr(n_sel, (torch.int32,), s.S * s.H, "n_sel"),
+        _ptr(out, (torch.float32,), nq * s.d, "out"), _ptr(lse, (torch.float32,), nq, "lse"),
+        _ptr(ws, what="ws"), ws.numel(), _stream(stream)), "cknv_decode_step")
+
+
 class DecodeStep:
     """Buffers for one CompKV decode step of a layer: append, score/select, attend.
 
@@ -231,8 +252,9 @@ class DecodeStep:
     (max_blocks, budget)."""
 
     def __init__(self, cache: LayerCache, max_blocks: int, budget: int, want_scores=False,
-                 stream=None):
+                 stream=None, fused=False):
         import torch
+        self.fused = fused
         s = cache.shape
         dev = cache.k.device
         self.cache, self.max_blocks, self.budget = cache, max_blocks, budget
@@ -246,6 +268,10 @@ class DecodeStep:
                        if want_scores else None)
 
     def __call__(self, q, new_k=None, new_v=None, stream=None):
+        if self.fused and new_k is not None:
+            decode_step(self.cache, new_k, new_v, q, self.budget, self.max_blocks, self.sel,
+                        self.n_sel, self.out, self.ws, self.lse, self.scores, stream)
+            return self.out
         if new_k is not None:
             append(self.cache, new_k, new_v, stream)
         score_select(self.cache, q, self.budget, self.max_blocks, self.sel, self.n_sel, self.ws,
@@ -288,8 +314,12 @@ class BoundStep:
                             _ptr(lse, (torch.float32,), s.S * s.H * s.G, "lse"), w, wn, st)
         self.dense_args = (self.shape, cp, qp, max_blocks, budget, self.attend_args[7],
                            self.attend_args[8], w, wn, st)
+        self.fused_args = (self.shape, cp, self.append_args[2], self.append_args[3], qp, budget,
+                           max_blocks, self.score_args[5], self.score_args[6], self.score_args[7],
+                           self.attend_args[7], self.attend_args[8], w, wn, st)
         self._append, self._score = L.cknv_append, L.cknv_score_select
         self._attend, self._dense = L.cknv_attend, L.cknv_dense_attend
+        self._fused = L.cknv_decode_step
 
     def append(self):
         st = self._append(*self.append_args)
@@ -312,6 +342,13 @@ class BoundStep:
             raise CknvError(st, "cknv_dense_attend")
 
     def step(self):
+        """One decode step as three calls (append, score_select, attend)."""
         self.append()
         self.score_select()
         self.attend()
+
+    def fused_step(self):
+        """One decode step as one call (cknv_decode_step)."""
+        st = self._fused(*self.fused_args)
+        if st:
+            raise CknvError(st, "cknv_decode_step")

@@ -48,6 +48,7 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   bpw = bpw > kDenseBlocksPerWG ? bpw : kDenseBlocksPerWG;
   q.BPW = bpw;
   q.Pd = (max_blocks + bpw - 1) / bpw;
+  q.Pf = (q.Kb + step_kpart(G) - 1) / step_kpart(G);
   const size_t W = (size_t)rec_words(d);
   size_t off = 0;
   q.off_grp = off;
@@ -60,6 +61,10 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   off = align256(off + (size_t)q.U * q.P * G * W * 4);
   q.off_dense = off;
   off = align256(off + (size_t)q.U * q.Pd * G * W * 4);
+  q.off_t0 = off;
+  off = align256(off + (size_t)sh->S * 4);
+  q.off_fpart = off;
+  off = align256(off + (size_t)q.U * q.Pf * G * W * 4);
   q.total = off;
   if (max_blocks > kSelThreads * kSelKeysPerThread) return CKNV_EUNSUPPORTED;
   *p = q;
@@ -145,6 +150,44 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   sa.H = shape->H; sa.cap_blocks = shape->cap_blocks; sa.max_blocks = max_blocks; sa.NG = p.NG;
   sa.Kb = p.Kb;
   return hip_status(launch_select(shape->G, sa, p.U, (hipStream_t)stream));
+}
+
+int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                     const uint16_t* new_v, const float* q, int32_t budget_tokens,
+                     int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel, float* out,
+                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, max_blocks, budget_tokens, &p);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!new_k || !new_v || !q || !sel || !n_sel || !out || !ws) return CKNV_EINVAL;
+  if (ws_bytes < p.total) return CKNV_ENOSPACE;
+  char* w = static_cast<char*>(ws);
+  ScoreArgs a{};
+  a.kbar = cache->kbar; a.dbar = cache->dbar; a.cnt = cache->cnt; a.vbar = cache->vbar;
+  a.seq_len = cache->seq_len; a.q = q;
+  a.grp = reinterpret_cast<float*>(w + p.off_grp);
+  a.u = reinterpret_cast<float*>(w + p.off_u);
+  a.comp = reinterpret_cast<float*>(w + p.off_comp);
+  a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
+  a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C;
+  a.xcd = (p.U % 8) == 0;
+  a.closed_only = 1;
+  a.t0_out = reinterpret_cast<int32_t*>(w + p.off_t0);
+  a.isd = 1.0f / sqrtf((float)shape->d);
+  hipError_t e = launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream);
+  if (e != hipSuccess) return CKNV_EHIP;
+  StepArgs sa{};
+  sa.k = cache->k; sa.v = cache->v; sa.kbar = cache->kbar; sa.dbar = cache->dbar;
+  sa.cnt = cache->cnt; sa.vbar = cache->vbar; sa.seq_len = cache->seq_len; sa.t0 = a.t0_out;
+  sa.new_k = new_k; sa.new_v = new_v; sa.q = q;
+  sa.grp = a.grp; sa.u = a.u; sa.comp = a.comp;
+  sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel; sa.out = out; sa.lse = lse;
+  sa.part = reinterpret_cast<float*>(w + p.off_fpart);
+  sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
+  sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf;
+  sa.isd = a.isd;
+  return hip_status(launch_step(shape->d, shape->G, sa, p.U, (hipStream_t)stream));
 }
 
 static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const float* q,

@@ -22,321 +22,13 @@
 //
 // dense_kernel is the full-attention baseline: every block exact, no
 // compensation, a contiguous block range per workgroup.
-#include "cknv_internal.h"
+#include "attend_core.h"
 
 namespace cknv {
 
 namespace {
 
 constexpr int kBlocksPerAttendWave = 1;
-
-// Running softmax state of one wave for the G query heads. Lane l owns value
-// coordinates [l*VPL, l*VPL+VPL) (VPL = d/64) summed over every token it has
-// absorbed; m and l are wave-uniform.
-template <int D, int G>
-struct WaveState {
-  static constexpr int VPL = D / 64;
-  float m[G], l[G], acc[G][VPL];
-  __device__ void init() {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = -INFINITY;
-      l[g] = 0.f;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) acc[g][e] = 0.f;
-    }
-  }
-};
-
-// One block's BF16 tokens. Keys: token t = 4*m + tq, lane covers coordinates
-// [cc*EPL, +EPL) (16 lanes per token, 4 tokens per load). Values: every lane
-// loads its VPL coordinates of all 16 tokens. Tokens at or past T load as 0.
-template <int D>
-struct Tile {
-  static constexpr int EPL = D / 16, VPL = D / 64;
-  uint32_t k[4][EPL / 2];
-  uint32_t v[16];  // d=128: 2 bf16 (one word) per token; d=64: 1 bf16 in the low half
-  bool tv[4];
-  int nt;          // valid tokens
-  __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
-    const int tq = lane >> 4, cc = lane & 15;
-    const long left = T - tok0;
-    nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = 4 * m + tq;
-      tv[m] = t < nt;
-      const size_t off = (size_t)(tok0 + t) * D + cc * EPL;
-      if (EPL == 8) {
-        const uint4 kk = tv[m] ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
-        k[m][0] = kk.x; k[m][1] = kk.y; k[m][2] = kk.z; k[m][3] = kk.w;
-      } else {
-        const uint2 kk = tv[m] ? *reinterpret_cast<const uint2*>(kc + off) : make_uint2(0, 0);
-        k[m][0] = kk.x; k[m][1] = kk.y;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const size_t off = (size_t)(tok0 + t) * D + lane * VPL;
-      if (VPL == 2)
-        v[t] = t < nt ? *reinterpret_cast<const uint32_t*>(vc + off) : 0u;
-      else
-        v[t] = t < nt ? (uint32_t)vc[off] : 0u;
-    }
-  }
-};
-
-// Mean-compensation inputs of one kept block (to be subtracted): the lane's
-// VPL coordinates of k̄ and v̄, and |b|.
-template <int D>
-struct BlockMean {
-  static constexpr int VPL = D / 64;
-  float kb[VPL], vb[VPL], n;
-  __device__ void load(const float* kbar_row, const float* vbar_row, const float* cnt, int lane) {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) {
-      kb[e] = kbar_row[lane * VPL + e];
-      vb[e] = vbar_row[lane * VPL + e];
-    }
-    n = *cnt;
-  }
-};
-
-// p of token 4*m + R (held by the lanes of row R) for R = 0..3, in every lane.
-__device__ __forceinline__ void spread_rows(float x, float& r0, float& r1, float& r2, float& r3) {
-  float b;
-  const float a = swap16_lo(x, b);  // a: rows 0,0,2,2   b: rows 1,1,3,3
-  r0 = swap32_lo(a, r2);
-  r1 = swap32_lo(b, r3);
-}
-
-// Add one block's exact terms (and, with COMP, remove its compensation terms).
-template <int D, int G, bool COMP>
-__device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, const BlockMean<D>& bm,
-                                       const float* q_l, int lane, float isd) {
-  constexpr int EPL = D / 16, VPL = D / 64;
-  const int cc = lane & 15;
-  float zbar[G];
-  if (COMP) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float zp = 0.f;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) zp += bm.kb[e] * q_l[g * D + lane * VPL + e];
-      zbar[g] = group_sum<64>(zp) * isd;
-    }
-  }
-  float z[4][G];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    float kf[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL / 2; ++e) { kf[2 * e] = bf16_lo(t.k[m][e]); kf[2 * e + 1] = bf16_hi(t.k[m][e]); }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float zp = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) zp += kf[e] * q_l[g * D + cc * EPL + e];
-      zp = group_sum<16>(zp) * isd;
-      z[m][g] = t.tv[m] ? zp : -INFINITY;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float bmax = fmaxf(fmaxf(z[0][g], z[1][g]), fmaxf(z[2][g], z[3][g]));
-    bmax = rows_max(bmax);
-    if (COMP) bmax = fmaxf(bmax, zbar[g]);
-    const float M = fmaxf(st.m[g], bmax);
-    const float sc = rescale(st.m[g], M);
-    float l = st.l[g] * sc;
-    float acc[VPL];
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) acc[e] = st.acc[g][e] * sc;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float pz = t.tv[m] ? __expf(z[m][g] - M) : 0.f;
-      float p[4];
-      spread_rows(pz, p[0], p[1], p[2], p[3]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t vw = t.v[4 * m + q];
-        l += p[q];
-        if (VPL == 2) {
-          acc[0] += p[q] * bf16_lo(vw);
-          acc[1 % VPL] += p[q] * bf16_hi(vw);
-        } else {
-          acc[0] += p[q] * bf16_lo(vw);
-        }
-      }
-    }
-    if (COMP) {
-      const float w = bm.n * __expf(zbar[g] - M);
-      l -= w;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) acc[e] -= w * bm.vb[e];
-    }
-    st.m[g] = M;
-    st.l[g] = l;
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) st.acc[g][e] = acc[e];
-  }
-}
-
-// Write the wave's record [m, l, 0, 0, acc[D]] per g.
-template <int D, int G>
-__device__ __forceinline__ void store_wave_record(const WaveState<D, G>& st, float* rec, int lane) {
-  constexpr int VPL = D / 64, W = rec_words(D);
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) rec[g * W + 4 + lane * VPL + e] = st.acc[g][e];
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      rec[g * W] = st.m[g];
-      rec[g * W + 1] = st.l[g];
-      rec[g * W + 2] = 0.f;
-      rec[g * W + 3] = 0.f;
-    }
-  }
-}
-
-// Per query head g of n records (LDS, G x W words each): M = max of m_i,
-// the factors e^{m_i - M} into scl[i*G + g], and L = sum_i l_i e^{m_i - M}
-// (starting from a running (M0, L0), whose factor goes to *s0).
-template <int D, int G>
-__device__ __forceinline__ void record_scales(const float* recs, int n, int g, float* scl, float& M,
-                                              float& L, float* s0) {
-  constexpr int W = rec_words(D);
-  float MM = M;
-  for (int i = 0; i < n; ++i) MM = fmaxf(MM, recs[(i * G + g) * W]);
-  const float so = rescale(M, MM);
-  float LL = L * so;
-  for (int i = 0; i < n; ++i) {
-    const float f = rescale(recs[(i * G + g) * W], MM);
-    scl[i * G + g] = f;
-    LL += recs[(i * G + g) * W + 1] * f;
-  }
-  if (s0) *s0 = so;
-  M = MM;
-  L = LL;
-}
-
-// sum_i recs[i][g][4 + c] * scl[i][g] over n records, four at a time.
-template <int D, int G>
-__device__ __forceinline__ float record_column(const float* recs, const float* scl, int n, int g, int c) {
-  constexpr int W = rec_words(D);
-  float A = 0.f;
-  int i = 0;
-#pragma unroll 1
-  for (; i + 4 <= n; i += 4) {
-    float x[4], f[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[k] = recs[((i + k) * G + g) * W + 4 + c];
-      f[k] = scl[(i + k) * G + g];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) A += x[k] * f[k];
-  }
-  for (; i < n; ++i) A += recs[(i * G + g) * W + 4 + c] * scl[i * G + g];
-  return A;
-}
-
-// Merge n records of G x W words (LDS, consecutive) into one record at dst
-// (global). `scl` is LDS scratch of n*G floats.
-template <int D, int G>
-__device__ __forceinline__ void merge_records(const float* recs, int n, float* dst, float* scl) {
-  constexpr int W = rec_words(D);
-  const int tid = threadIdx.x;
-  if (tid < G) {
-    float M = -INFINITY, L = 0.f;
-    record_scales<D, G>(recs, n, tid, scl, M, L, nullptr);
-    dst[tid * W] = M;
-    dst[tid * W + 1] = L;
-    dst[tid * W + 2] = 0.f;
-    dst[tid * W + 3] = 0.f;
-  }
-  __syncthreads();
-  for (int col = tid; col < G * D; col += kThreads) {
-    const int g = col / D, c = col - g * D;
-    dst[g * W + 4 + c] = record_column<D, G>(recs, scl, n, g, c);
-  }
-}
-
-template <int G>
-constexpr int stage_cap() { return G <= 4 ? 24 : 12; }
-
-// Copy n <= stage_cap records (G x W words each, 16-byte aligned) from global
-// to LDS; every load is issued before the first LDS store.
-template <int D, int G>
-__device__ __forceinline__ void stage_records(const float* src, int n, float* lds_dst) {
-  constexpr int W4 = rec_words(D) / 4;
-  constexpr int NBUF = (stage_cap<G>() * G * W4 + kThreads - 1) / kThreads;
-  const float4* s4 = reinterpret_cast<const float4*>(src);
-  float4* d4 = reinterpret_cast<float4*>(lds_dst);
-  const int total = n * G * W4;
-  float4 buf[NBUF];
-#pragma unroll
-  for (int k = 0; k < NBUF; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    buf[k] = i < total ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-#pragma unroll
-  for (int k = 0; k < NBUF; ++k) {
-    const int i = threadIdx.x + k * kThreads;
-    if (i < total) d4[i] = buf[k];
-  }
-}
-
-// The unit's last workgroup: merge its P part records into out and lse.
-// `stage` holds `cap` records of LDS, `scl` cap*G + 3*G floats.
-template <int D, int G>
-__device__ void finish_unit(const float* parts, int P, float* out, float* lse, float* stage,
-                            int cap, float* scl) {
-  constexpr int W = rec_words(D);
-  constexpr int COLS = (G * D + kThreads - 1) / kThreads;
-  const int tid = threadIdx.x;
-  float* Mrun = scl + cap * G;  // [G] running max
-  float* Lrun = Mrun + G;       // [G] running normaliser
-  float* Srun = Lrun + G;       // [G] factor applied to the running sums this round
-  float Ar[COLS];
-#pragma unroll
-  for (int k = 0; k < COLS; ++k) Ar[k] = 0.f;
-  if (tid < G) { Mrun[tid] = -INFINITY; Lrun[tid] = 0.f; }
-  for (int p0 = 0; p0 < P; p0 += cap) {
-    const int n = P - p0 < cap ? P - p0 : cap;
-    stage_records<D, G>(parts + (size_t)p0 * G * W, n, stage);
-    __syncthreads();
-    if (tid < G) {
-      float M = Mrun[tid], L = Lrun[tid];
-      record_scales<D, G>(stage, n, tid, scl, M, L, Srun + tid);
-      Mrun[tid] = M;
-      Lrun[tid] = L;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < COLS; ++k) {
-      const int col = tid + k * kThreads;
-      if (col < G * D) {
-        const int g = col / D, c = col - g * D;
-        Ar[k] = Ar[k] * Srun[g] + record_column<D, G>(stage, scl, n, g, c);
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < COLS; ++k) {
-    const int col = tid + k * kThreads;
-    if (col < G * D) {
-      const int g = col / D, c = col - g * D;
-      const float L = Lrun[g];
-      const bool ok = L > 0.f;
-      out[col] = ok ? Ar[k] / L : 0.f;
-      if (c == 0 && lse) lse[g] = ok ? Mrun[g] + __logf(L) : -INFINITY;
-    }
-  }
-}
 
 }  // namespace
 

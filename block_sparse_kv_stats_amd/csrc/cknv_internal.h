@@ -23,6 +23,12 @@ constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
 constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
 constexpr int kDenseMaxWGs = 64;          // dense attention: workgroups per unit (at most)
+// Fused step kernel: threads per workgroup (the selection owns up to
+// kSelKeysPerThread * kSelThreads / step_threads blocks per thread). Half of
+// the waves attend one kept block each, so a workgroup attends step_kpart(G)
+// kept blocks; the other half fold the scoring pass's compensation records.
+__host__ __device__ constexpr int step_threads(int G) { return G <= 4 ? 1024 : 512; }
+__host__ __device__ constexpr int step_kpart(int G) { return step_threads(G) / 128; }
 constexpr int kSelThreads = 1024;       // selection: one workgroup per unit
 constexpr int kSelKeysPerThread = 12;   // blocks per selection thread: max_blocks <= 12288
 
@@ -39,9 +45,10 @@ struct Plan {
   int Kb;           // block slots of the budget
   int C;            // score workgroups per unit = ceil(NBmax/score_bpwg(G))
   int P;            // attend workgroups per unit
+  int Pf;           // fused-step workgroups per unit = ceil(Kb/step_kpart(G))
   int Pd;           // dense-attend workgroups per unit
   int BPW;          // dense-attend blocks per workgroup
-  size_t off_grp, off_u, off_comp, off_attp, off_dense, total;
+  size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, total;
 };
 
 int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p);
@@ -63,6 +70,7 @@ struct ScoreArgs {
   float* grp; float* u; float* comp;
   int S, H, r, cap_blocks, max_blocks, NG, C, xcd;
   int closed_only;  // 1: score only blocks closed before this step's token (fused step)
+  int32_t* t0_out;  // fused step: seq_len before the step, per sequence (or null)
   float isd;  // 1/sqrt(d)
 };
 
@@ -80,6 +88,17 @@ struct AttendArgs {
   float isd;
 };
 
+struct StepArgs {
+  uint16_t* k; uint16_t* v; float* kbar; float* dbar; float* cnt; float* vbar;
+  int32_t* seq_len; const int32_t* t0;
+  const uint16_t* new_k; const uint16_t* new_v; const float* q;
+  const float* grp; const float* u; const float* comp;
+  float* scores; int32_t* sel; int32_t* n_sel; float* out; float* lse; float* part;
+  int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P;
+  float isd;
+};
+
+hipError_t launch_step(int d, int G, const StepArgs& a, int U, hipStream_t st);
 hipError_t launch_append(int d, const AppendArgs& a, hipStream_t st);
 hipError_t launch_build(int d, const BuildArgs& a, int U, hipStream_t st);
 hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st);
@@ -164,6 +183,21 @@ __device__ __forceinline__ float rows_max(float x) {
 // exp(m - M) with exp(-inf - anything) = 0 (an empty partial contributes nothing).
 __device__ __forceinline__ float rescale(float m, float M) {
   return (m == -INFINITY) ? 0.f : __expf(m - M);
+}
+
+// Mean and population variance of x[0..n) (n in 1..16), x held in registers.
+__device__ __forceinline__ void mean_var16(const float (&x)[16], int n, float& mean, float& var) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += (j < n) ? x[j] : 0.f;
+  mean = s / (float)n;
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float dl = x[j] - mean;
+    q += (j < n) ? dl * dl : 0.f;
+  }
+  var = q / (float)n;
 }
 
 // Workgroup -> (unit, part). With U a multiple of 8, all parts of a unit land

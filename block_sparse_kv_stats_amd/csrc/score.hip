@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   // Block indices are clamped into [0, MB); blocks past the scored range are
   // masked once seq_len has arrived.
   const int T = a.seq_len[s];
+  if (a.t0_out && unit == s * a.H && chunk == 0 && tid == 0) a.t0_out[s] = T;
   float4 qv[G][KC];
   {
     const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D);
@@ -285,23 +286,36 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     }
   }
   __syncthreads();
-  float* co = a.comp + ((size_t)unit * a.C + chunk) * G * W;
-  for (int idx = tid; idx < G * W; idx += kThreads) {
-    const int g = idx / W, e = idx - g * W;
+  // ---- the workgroup's record: the waves' sums under their common max
+  constexpr int CPT = (G * D + kThreads - 1) / kThreads;  // coordinates per thread (1, 2 or 4)
+  const int f0 = tid * CPT;
+  if (f0 < G * D) {
+    const int g = f0 / D, c0 = f0 - g * D;
     float mw[kWaves], M = -INFINITY;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) { mw[q] = cml[(q * G + g) * 2]; M = fmaxf(M, mw[q]); }
-    float val = 0.f;
-    if (e == 0) {
-      val = M;
-    } else if (e == 1) {
+    float sc[kWaves];
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q) val += cml[(q * G + g) * 2 + 1] * rescale(mw[q], M);
-    } else if (e >= 4) {
+    for (int q = 0; q < kWaves; ++q) sc[q] = rescale(mw[q], M);
+    float acc[CPT];
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q) val += cacc[(q * G + g) * D + e - 4] * rescale(mw[q], M);
+    for (int e = 0; e < CPT; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q)
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) acc[e] += cacc[(q * G + g) * D + c0 + e] * sc[q];
+    float* co = a.comp + (((size_t)unit * a.C + chunk) * G + g) * W;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) co[4 + c0 + e] = acc[e];
+    if (c0 == 0) {
+      float l = 0.f;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) l += cml[(q * G + g) * 2 + 1] * sc[q];
+      co[0] = M;
+      co[1] = l;
+      co[2] = 0.f;
+      co[3] = 0.f;
     }
-    co[idx] = val;
   }
 }
 

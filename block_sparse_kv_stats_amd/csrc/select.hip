@@ -23,14 +23,13 @@
 //      more radix passes (11 and 10 bits) pin the exact threshold key instead
 //      and equal keys are taken in index order.
 //   4. The kept blocks are written in ascending order (ballot prefix).
-#include "cknv_internal.h"
+#include "select_core.h"
 
 namespace cknv {
 
 namespace {
 
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kListMax = 256;
 
 // Exclusive prefix over tiles of kSelThreads consecutive items (item order:
 // tile-major, then thread); bit m of `flags` is this thread's flag in tile m.
@@ -73,51 +72,6 @@ __device__ __forceinline__ void tile_prefix(uint32_t flags, int (&before)[NT], i
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < NT; ++m) before[m] += cnt[m * kSelWaves + wave];
-}
-
-// Wave 0: the bin of `hist` (NBINS bins, higher bin = larger keys) holding
-// the krem-th largest counted key; writes (bin, rank within the bin, count
-// in the bin) to ctl[0..2]. Lane l owns bins [l*PER, (l+1)*PER).
-template <int NBINS>
-__device__ __forceinline__ void find_bin(const int* hist, int krem, int* ctl) {
-  constexpr int PER = NBINS / 64, NC = PER / 4;
-  const int lane = threadIdx.x & 63;
-  const int4* h4 = reinterpret_cast<const int4*>(hist + lane * PER);
-  int cs[NC], own = 0;  // per int4 chunk of bins
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int4 v = h4[i];
-    cs[i] = v.x + v.y + v.z + v.w;
-    own += cs[i];
-  }
-  int above = own;  // inclusive suffix over lanes >= lane
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_down(above, o);
-    if (lane + o < 64) above += y;
-  }
-  int cum = above - own;  // keys in bins of higher lanes
-  if (cum < krem && krem <= cum + own) {  // this lane holds the bin
-    int ci = 0, cb = cum;                  // chunk holding it, keys above that chunk
-    int c = cum;
-#pragma unroll
-    for (int i = NC - 1; i >= 0; --i) {
-      if (c < krem && krem <= c + cs[i]) { ci = i; cb = c; }
-      c += cs[i];
-    }
-    const int4 v = h4[ci];
-    const int hv[4] = {v.x, v.y, v.z, v.w};
-    c = cb;
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      if (c < krem && krem <= c + hv[e]) {
-        ctl[0] = lane * PER + 4 * ci + e;
-        ctl[1] = krem - c;
-        ctl[2] = hv[e];
-      }
-      c += hv[e];
-    }
-  }
 }
 
 }  // namespace

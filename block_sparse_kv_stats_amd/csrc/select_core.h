@@ -1,0 +1,56 @@
+// Device helpers of the block selection shared by the selection kernels.
+// Internal to libcknv.
+#pragma once
+
+#include "cknv_internal.h"
+
+namespace cknv {
+
+constexpr int kListMax = 256;  // pivot-bin keys ranked exactly; more go to the radix fallback
+
+// Wave 0: the bin of `hist` (NBINS bins, higher bin = larger keys) holding
+// the krem-th largest counted key; writes (bin, rank within the bin, count
+// in the bin) to ctl[0..2]. Lane l owns bins [l*PER, (l+1)*PER).
+template <int NBINS>
+__device__ __forceinline__ void find_bin(const int* hist, int krem, int* ctl) {
+  constexpr int PER = NBINS / 64, NC = PER / 4;
+  const int lane = threadIdx.x & 63;
+  const int4* h4 = reinterpret_cast<const int4*>(hist + lane * PER);
+  int cs[NC], own = 0;  // per int4 chunk of bins
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int4 v = h4[i];
+    cs[i] = v.x + v.y + v.z + v.w;
+    own += cs[i];
+  }
+  int above = own;  // inclusive suffix over lanes >= lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(above, o);
+    if (lane + o < 64) above += y;
+  }
+  int cum = above - own;  // keys in bins of higher lanes
+  if (cum < krem && krem <= cum + own) {  // this lane holds the bin
+    int ci = 0, cb = cum;                  // chunk holding it, keys above that chunk
+    int c = cum;
+#pragma unroll
+    for (int i = NC - 1; i >= 0; --i) {
+      if (c < krem && krem <= c + cs[i]) { ci = i; cb = c; }
+      c += cs[i];
+    }
+    const int4 v = h4[ci];
+    const int hv[4] = {v.x, v.y, v.z, v.w};
+    c = cb;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      if (c < krem && krem <= c + hv[e]) {
+        ctl[0] = lane * PER + 4 * ci + e;
+        ctl[1] = krem - c;
+        ctl[2] = hv[e];
+      }
+      c += hv[e];
+    }
+  }
+}
+
+}  // namespace cknv

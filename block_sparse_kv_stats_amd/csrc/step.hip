@@ -1,0 +1,619 @@
+// The fused decode step after the scoring pass: append, selection and
+// attention of one unit in one workgroup (or in P workgroups that each
+// attend a slice of the kept list, merged by step_merge_kernel).
+//
+// CompKV page (onedev.kr/papers/157):
+//   "How to use it" -- every step stores the new token and refreshes the
+//     statistics of the block it lands in;
+//   "What differs"  -- p̂ is normalised over all blocks, S_b = sum_g p̂ σ̂²;
+//     the first block and the two most recent blocks are always kept and
+//     count against the budget, the rest of the budget goes to the largest
+//     S_b (ties: lower block index);
+//   "How it works"  -- kept blocks contribute their tokens' exact terms,
+//     every other block its Mean compensation |b| e^{z̄} (1, v̄), all under
+//     one normaliser.
+//
+// Inputs from the scoring pass (score_kernel with closed_only = 1), which
+// covered the NBa = T0/16 blocks that were closed before this step (T0 =
+// tokens before the step): per score group the (max, sum) of
+// a = ln|b| + z̄ + σ̂²/2, per block u_{g,b} = exp(a - group max) σ̂², per
+// chunk the Mean-compensation sums of all its blocks, and T0 per sequence.
+// The block the new token lands in (the fresh block, index T0/16) is not in
+// any of them: this kernel computes its summary from its tokens, folds its
+// a into the normalisers, and never removes compensation for it.
+//
+// Phases of a workgroup (NT threads; thread t owns blocks t*KPT.. of the
+// unit, in order):
+//   loads      score-group partials, the thread's u terms, the query, and
+//              (last wave) the fresh block's tokens;
+//   fresh      last wave: summary of the fresh block, its a and σ̂²; part 0
+//              writes the token and the summary to the cache;
+//   LSE        per query head over all blocks;
+//   keys       S_b per block (fp32 bits order like the values, S_b >= 0);
+//              scores; 2048-bin histogram of the candidates' top 11 bits;
+//   select     the bin holding the (Kb-3)-th largest candidate key; keys
+//              in that bin are ranked exactly (or, for long runs of equal
+//              keys, pinned by two more radix passes, ties by index);
+//   compact    kept blocks in ascending order -> sel, and this part's slice;
+//   attend     the first KPART waves: one kept block of this part's slice
+//              each (exact terms minus its compensation); the others: this
+//              part's share of the scoring pass's chunk records;
+//   merge      the waves' records -> out, lse (P == 1) or a part record.
+#include "attend_core.h"
+#include "select_core.h"
+
+namespace cknv {
+
+namespace {
+
+template <int G>
+struct StepCfg {
+  static constexpr int NT = step_threads(G);
+  static constexpr int NW = NT / 64;
+  static constexpr int KPT = kSelThreads * kSelKeysPerThread / NT;  // blocks per thread, at most
+  static constexpr int UB = (24 / G) < KPT ? (24 / G) : KPT;         // blocks per u load batch
+  static constexpr int NBATCH = (KPT + UB - 1) / UB;
+  static constexpr int BPW = score_bpw(G);                           // blocks per score group
+  static constexpr int NGT = (KPT - 1) / BPW + 2;                    // score groups of a thread's blocks
+  static constexpr int NGMAX = kSelThreads * kSelKeysPerThread / BPW;
+  static constexpr int GPT = (NGMAX + NT - 1) / NT;                  // score groups per thread (LSE)
+  static constexpr int KPART = step_kpart(G);                        // kept blocks per workgroup
+  static constexpr int RW = NW - KPART;                              // record-folding waves
+  static constexpr int RPW = 2;                                      // records per wave per batch
+};
+
+// Exclusive prefix sum over the workgroup of one int per thread (thread
+// order); also returns the total. `scan` is LDS scratch of NW ints.
+template <int NW>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scan, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) scan[wave] = incl;
+  __syncthreads();
+  int before = incl - v;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = scan[w];
+    before += w < wave ? c : 0;
+    total += c;
+  }
+  return before;
+}
+
+// out[g][c] = sum_i rec_i[g][c] e^{m_i - M} / L (and lse = M + ln L) over n
+// records in LDS.
+template <int D, int G, int NT>
+__device__ __forceinline__ void finalize_records(const float* recs, int n, float* out, float* lse,
+                                                 float* scl) {
+  constexpr int W = rec_words(D);
+  const int tid = threadIdx.x;
+  float* ML = scl + n * G;  // [G] (M, L)
+  if (tid < G) {
+    float M = -INFINITY, L = 0.f;
+    record_scales<D, G>(recs, n, tid, scl, M, L, nullptr);
+    ML[2 * tid] = M;
+    ML[2 * tid + 1] = L;
+  }
+  __syncthreads();
+  for (int col = tid; col < G * D; col += NT) {
+    const int g = col / D, c = col - g * D;
+    const float L = ML[2 * g + 1];
+    const bool ok = L > 0.f;
+    const float A = record_column<D, G>(recs, scl, n, g, c);
+    out[col] = ok ? A / L : 0.f;
+    if (c == 0 && lse) lse[g] = ok ? ML[2 * g] + __logf(L) : -INFINITY;
+  }
+}
+
+// Fold one compensation record (this lane's coordinates) into a wave state.
+template <int D, int G>
+__device__ __forceinline__ void fold_record(WaveState<D, G>& st, const float (&rm)[G], const float (&rl)[G],
+                                            const float (&racc)[G][D / 64]) {
+  constexpr int VPL = D / 64;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float M = fmaxf(st.m[g], rm[g]);
+    const float a = rescale(st.m[g], M), b = rescale(rm[g], M);
+    st.m[g] = M;
+    st.l[g] = st.l[g] * a + rl[g] * b;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) st.acc[g][e] = st.acc[g][e] * a + racc[g][e] * b;
+  }
+}
+
+}  // namespace
+
+template <int D, int G>
+__global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
+  using C = StepCfg<G>;
+  constexpr int NT = C::NT, NW = C::NW, KPT = C::KPT, UB = C::UB, BPW = C::BPW;
+  constexpr int NGT = C::NGT, GPT = C::GPT, KPART = C::KPART, RW = C::RW, RPW = C::RPW;
+  constexpr int W = rec_words(D), VPL = D / 64;
+  constexpr int OW = NW - 1;  // the wave that refreshes the fresh block
+  // Selection scratch and the waves' attention records share one LDS area.
+  constexpr int NBITS = KPT * NT / 32;
+  constexpr int SEL_WORDS = 2048 + 2 * kListMax + NBITS;
+  constexpr int REC_WORDS = NW * G * W;
+  constexpr int BIG = SEL_WORDS > REC_WORDS ? SEL_WORDS : REC_WORDS;
+  __shared__ __align__(16) float big[BIG];
+  __shared__ __align__(16) float q_l[G * D];
+  __shared__ float red[NW * G * 2];
+  __shared__ float scl[NW * G + 2 * G];
+  __shared__ float oinfo[2 * G];  // fresh block: a_g, σ̂²_g
+  __shared__ int scan[NW];
+  __shared__ int ctl[8];
+  __shared__ int klist[KPART];
+  int* hist = reinterpret_cast<int*>(big);
+  uint32_t* lkey = reinterpret_cast<uint32_t*>(big + 2048);
+  int* lidx = reinterpret_cast<int*>(big + 2048 + kListMax);
+  uint32_t* keep_bits = reinterpret_cast<uint32_t*>(big + 2048 + 2 * kListMax);
+  float* recs = big;
+
+  const int P = a.P;
+  const int unit = blockIdx.x / P, p = blockIdx.x - unit * P;
+  const int s = unit / a.H, h = unit - s * a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int MB = a.max_blocks, Kb = a.Kb;
+  const int KPTm = (MB + NT - 1) / NT;  // <= KPT (checked on the host)
+  const int b0 = tid * KPTm;
+  const long cap_tok = (long)a.cap_blocks * kBlock;
+  const size_t ubase = (size_t)unit * a.cap_blocks;
+  uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
+  uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
+  const float* u = a.u + (size_t)unit * MB * G;
+  const float2* grp = reinterpret_cast<const float2*>(a.grp) + (size_t)unit * a.NG * G;
+  const int NG = a.NG;
+
+  // ================================================================ loads
+  const int T0 = a.t0[s];
+  float2 gp[GPT][G];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    const int gi = tid + k * NT;
+    const int gc = gi < NG ? gi : NG - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) gp[k][g] = grp[(size_t)gc * G + g];
+  }
+  const int gA = b0 / BPW;
+  float gref[NGT][G];
+#pragma unroll
+  for (int k = 0; k < NGT; ++k) {
+    const int gc = gA + k < NG ? gA + k : NG - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) gref[k][g] = grp[(size_t)gc * G + g].x;
+  }
+  float uv[UB][G];
+#pragma unroll
+  for (int m = 0; m < UB; ++m) {
+    const int b = b0 + m;
+    const int bc = b < MB ? b : MB - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) uv[m][g] = u[(size_t)bc * G + g];
+  }
+  float4 q4[(G * D / 4 + NT - 1) / NT];
+#pragma unroll
+  for (int k = 0; k < (G * D / 4 + NT - 1) / NT; ++k) {
+    const int i = tid + k * NT;
+    q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
+  }
+  // Fresh-block tokens (wave OW): np = T0 % 16 cached tokens plus the new one.
+  const int fblk = T0 / kBlock;
+  const long ftok0 = (long)fblk * kBlock;
+  uint32_t fk[16], fv[16], nkw = 0u, nvw = 0u;
+  float fq[G][VPL];
+  if (wave == OW) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      long t = ftok0 + j;
+      t = t < T0 ? t : (T0 > 0 ? T0 - 1 : 0);  // clamp into written tokens
+      const size_t off = (size_t)t * D + lane * VPL;
+      fk[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(kc + off) : (uint32_t)kc[off];
+      fv[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(vc + off) : (uint32_t)vc[off];
+    }
+    const size_t noff = (size_t)unit * D + lane * VPL;
+    nkw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_k + noff) : (uint32_t)a.new_k[noff];
+    nvw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_v + noff) : (uint32_t)a.new_v[noff];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) fq[g][e] = a.q[((size_t)unit * G + g) * D + lane * VPL + e];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const bool room = T0 < cap_tok;
+  const int T = T0 + (room ? 1 : 0);
+  int NB = (T + kBlock - 1) / kBlock;
+  NB = NB < MB ? NB : MB;
+  int NBa = T0 / kBlock;
+  NBa = NBa < MB ? NBa : MB;
+  const int fb = (room && fblk < MB) ? fblk : -1;  // fresh block (always the last block)
+  const int NGa = (NBa + BPW - 1) / BPW;
+  const bool all = NB <= Kb;
+  int krem = Kb - 3;
+  const bool count = !all && krem > 0;
+#pragma unroll
+  for (int k = 0; k < (G * D / 4 + NT - 1) / NT; ++k) {
+    const int i = tid + k * NT;
+    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
+  }
+  for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+  for (int i = tid; i < NBITS; i += NT) keep_bits[i] = 0u;
+  if (tid == 0) ctl[3] = 0;
+
+  // ================================================================ fresh block
+  if (wave == OW && fb >= 0) {
+    const int np = T0 - fblk * kBlock;  // cached tokens of the block, 0..15
+    const int n = np + 1;
+    float km[VPL], kvr[VPL], vm[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) {
+      float kx[16], vx[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t wk = j < np ? fk[j] : nkw;
+        const uint32_t wv = j < np ? fv[j] : nvw;
+        kx[j] = e == 0 ? bf16_lo(wk) : bf16_hi(wk);
+        vx[j] = e == 0 ? bf16_lo(wv) : bf16_hi(wv);
+      }
+      float vvar;
+      mean_var16(kx, n, km[e], kvr[e]);
+      mean_var16(vx, n, vm[e], vvar);
+    }
+    // D̄: mean coordinate variance of each contiguous group of gs = D/r coordinates
+    const int gs = D / a.r;
+    float dl[VPL];
+    if (gs >= VPL) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) part += kvr[e];
+      for (int o = 1; o < gs / VPL; o <<= 1) part += __shfl_xor(part, o);
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) dl[e] = part / (float)gs;
+    } else {
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) dl[e] = kvr[e];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float zp = 0.f, sp = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) {
+        zp += fq[g][e] * km[e];
+        sp += fq[g][e] * fq[g][e] * dl[e];
+      }
+      const float z = group_sum<64>(zp) * a.isd;
+      const float s2 = group_sum<64>(sp) / (float)D;
+      if (lane == 0) {
+        oinfo[g] = __logf((float)n) + z + 0.5f * s2;
+        oinfo[G + g] = s2;
+      }
+    }
+    if (p == 0) {
+      const size_t toff = (size_t)T0 * D + lane * VPL;
+      const size_t row = ubase + fblk;
+      if (VPL == 2) {
+        *reinterpret_cast<uint32_t*>(kc + toff) = nkw;
+        *reinterpret_cast<uint32_t*>(vc + toff) = nvw;
+      } else {
+        kc[toff] = (uint16_t)nkw;
+        vc[toff] = (uint16_t)nvw;
+      }
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) {
+        a.kbar[row * D + lane * VPL + e] = km[e];
+        a.vbar[row * D + lane * VPL + e] = vm[e];
+      }
+      if (gs >= VPL) {
+        if ((lane * VPL) % gs == 0) a.dbar[row * a.r + (lane * VPL) / gs] = dl[0];
+      } else {
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) a.dbar[row * a.r + lane * VPL + e] = dl[e];
+      }
+      if (lane == 0) a.cnt[row] = (float)n;
+    }
+  }
+
+  // ================================================================ LSE
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float r = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) r = fmaxf(r, tid + k * NT < NGa ? gp[k][g].x : -INFINITY);
+    const float Mw = group_max<64>(r);
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) l += tid + k * NT < NGa ? gp[k][g].y * rescale(gp[k][g].x, Mw) : 0.f;
+    const float Lw = group_sum<64>(l);
+    if (lane == 0) {
+      red[(wave * G + g) * 2] = Mw;
+      red[(wave * G + g) * 2 + 1] = Lw;
+    }
+  }
+  __syncthreads();
+  float lse_g[G], fa[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float fa_g = fb >= 0 ? oinfo[g] : -INFINITY;
+    float M = fa_g;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[(w * G + g) * 2]);
+    float L = rescale(fa_g, M);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) L += red[(w * G + g) * 2 + 1] * rescale(red[(w * G + g) * 2], M);
+    lse_g[g] = L > 0.f ? M + __logf(L) : INFINITY;
+    fa[g] = fa_g;
+  }
+  float fg[NGT][G];
+#pragma unroll
+  for (int k = 0; k < NGT; ++k)
+#pragma unroll
+    for (int g = 0; g < G; ++g) fg[k][g] = __expf(gref[k][g] - lse_g[g]);
+
+  // ================================================================ keys
+  uint32_t key[KPT];
+  uint32_t candm = 0u;  // bit m: block b0 + m is a Top-K candidate
+  float* scores = (a.scores && p == 0) ? a.scores + ubase : nullptr;
+#pragma unroll
+  for (int bt = 0; bt < C::NBATCH; ++bt) {
+    if (bt > 0 && bt * UB < KPTm) {
+#pragma unroll
+      for (int m = 0; m < UB; ++m) {
+        const int b = b0 + bt * UB + m;
+        const int bc = b < MB ? b : MB - 1;
+#pragma unroll
+        for (int g = 0; g < G; ++g) uv[m][g] = u[(size_t)bc * G + g];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < UB; ++m) {
+      const int mm = bt * UB + m;
+      if (mm >= KPT) break;
+      const int b = b0 + mm;
+      const int k = b / BPW - gA;  // 0..NGT-1 for the thread's blocks
+      float S = 0.f;
+      if (b < NBa) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float f = fg[0][g];
+#pragma unroll
+          for (int kk = 1; kk < NGT; ++kk) f = k == kk ? fg[kk][g] : f;
+          S += uv[m][g] * f;
+        }
+      } else if (b == fb) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) S += __expf(fa[g] - lse_g[g]) * oinfo[G + g];
+      }
+      const bool inr = mm < KPTm && b < NB;
+      key[mm] = (inr && S > 0.f) ? __float_as_uint(S) : 0u;
+      const bool c = inr && b >= 1 && b <= NB - 3;
+      candm |= (uint32_t)c << mm;
+      if (scores && inr) scores[b] = S;
+      if (c && count) atomicAdd(&hist[key[mm] >> 21], 1);
+    }
+  }
+
+  // ================================================================ select
+  uint32_t tau_bin = 0xffffffffu;
+  bool use_list = true;
+  uint32_t exact_tau = 0u;
+  if (count) {
+    __syncthreads();
+    if (wave == 0) find_bin<2048>(hist, krem, ctl);
+    __syncthreads();
+    tau_bin = (uint32_t)ctl[0];
+    krem = ctl[1];
+    use_list = ctl[2] <= kListMax;
+    if (use_list) {
+      // the pivot bin's keys, ordered exactly by (key desc, index asc); the first krem are kept
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) {
+        if (((candm >> m) & 1u) && (key[m] >> 21) == tau_bin) {
+          const int slot = atomicAdd(&ctl[3], 1);
+          lkey[slot] = key[m];
+          lidx[slot] = b0 + m;
+        }
+      }
+      __syncthreads();
+      const int n = ctl[3];
+      if (tid < n) {
+        const uint32_t ki = lkey[tid];
+        const int ii = lidx[tid];
+        int rank = 0;
+        for (int j0 = 0; j0 < n; j0 += 8) {
+          uint32_t kj[8];
+          int ij[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kj[e] = j0 + e < n ? lkey[j0 + e] : 0u;
+            ij[e] = j0 + e < n ? lidx[j0 + e] : 0x7fffffff;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rank += (kj[e] > ki) || (kj[e] == ki && ij[e] < ii);
+        }
+        if (rank < krem) atomicOr(&keep_bits[ii >> 5], 1u << (ii & 31));
+      }
+      __syncthreads();
+    } else {
+      // long runs of equal keys: pin the exact threshold key with two more radix passes
+      uint32_t prefix = tau_bin << 21;
+      __syncthreads();
+      for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < KPT; ++m)
+        if (((candm >> m) & 1u) && (key[m] >> 21) == (prefix >> 21)) atomicAdd(&hist[(key[m] >> 10) & 2047u], 1);
+      __syncthreads();
+      if (wave == 0) find_bin<2048>(hist, krem, ctl);
+      __syncthreads();
+      prefix |= ((uint32_t)ctl[0]) << 10;
+      krem = ctl[1];
+      for (int i = tid; i < 1024; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < KPT; ++m)
+        if (((candm >> m) & 1u) && (key[m] >> 10) == (prefix >> 10)) atomicAdd(&hist[key[m] & 1023u], 1);
+      __syncthreads();
+      if (wave == 0) find_bin<1024>(hist, krem, ctl);
+      __syncthreads();
+      prefix |= (uint32_t)ctl[0];
+      krem = ctl[1];
+      exact_tau = prefix;
+    }
+  }
+
+  // ================================================================ compact
+  const bool ties_by_index = count && !use_list;
+  int eq_before = 0;
+  if (ties_by_index) {
+    int eqc = 0;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) eqc += (((candm >> m) & 1u) && key[m] == exact_tau) ? 1 : 0;
+    int tot;
+    eq_before = block_exclusive_scan<NW>(eqc, scan, tot);
+    __syncthreads();
+  }
+  uint32_t takem = 0u;
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) {
+    const int b = b0 + m;
+    const bool inr = m < KPTm && b < NB;
+    const bool c = (candm >> m) & 1u;
+    bool t;
+    if (all) {
+      t = inr;
+    } else {
+      t = inr && (b == 0 || b >= NB - 2);
+      if (krem > 0 || !count) {
+        if (ties_by_index) {
+          const bool eq = c && key[m] == exact_tau;
+          t = t || (c && key[m] > exact_tau) || (eq && eq_before < krem);
+          eq_before += eq ? 1 : 0;
+        } else if (count) {
+          t = t || (c && (key[m] >> 21) > tau_bin) || ((keep_bits[b >> 5] >> (b & 31)) & 1u);
+        }
+      } else if (count) {
+        t = t || (c && (key[m] >> 21) > tau_bin);
+      }
+    }
+    takem |= (uint32_t)(t && inr) << m;
+  }
+  int nk;
+  int pos = block_exclusive_scan<NW>(__popc(takem), scan, nk);
+  int32_t* sel = a.sel + (size_t)unit * Kb;
+  const int lo = p * KPART;
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) {
+    if ((takem >> m) & 1u) {
+      if (p == 0 && pos < Kb) sel[pos] = b0 + m;
+      if (pos >= lo && pos < lo + KPART) klist[pos - lo] = b0 + m;
+      ++pos;
+    }
+  }
+  nk = nk < Kb ? nk : Kb;  // the selection keeps exactly min(Kb, NB); never index past sel
+  if (p == 0 && tid == 0) a.n_sel[unit] = nk;
+  __syncthreads();
+
+  // ================================================================ attend
+  // Waves 0..KPART-1: one kept block of this part's slice each (exact terms,
+  // minus its compensation if the scoring pass counted it). Waves KPART..:
+  // this part's share of the scoring pass's chunk records.
+  WaveState<D, G> st;
+  st.init();
+  if (wave < KPART) {
+    const int e = lo + wave;
+    const int b = e < nk ? klist[wave] : -1;
+    if (b >= 0) {
+      Tile<D> tile;
+      BlockMean<D> bm;
+      if (b == fb) {
+        tile.load_fresh(kc, vc, (long)b * kBlock, T0 - b * kBlock, a.new_k + (size_t)unit * D,
+                        a.new_v + (size_t)unit * D, lane);
+        absorb<D, G, false>(st, tile, bm, q_l, lane, a.isd);
+      } else {
+        tile.load(kc, vc, (long)b * kBlock, (long)T0, lane);
+        bm.load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
+        if (b < NBa)
+          absorb<D, G, true>(st, tile, bm, q_l, lane, a.isd);
+        else
+          absorb<D, G, false>(st, tile, bm, q_l, lane, a.isd);
+      }
+    }
+  } else {
+    const int c0 = (int)((long)p * a.C / P), c1 = (int)((long)(p + 1) * a.C / P);
+    const float* crec = a.comp + (size_t)unit * a.C * G * W;
+    for (int cb = c0 + wave - KPART; cb < c1; cb += RPW * RW) {
+      float rm[RPW][G], rl[RPW][G], racc[RPW][G][VPL];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int c = cb + i * RW;
+        const int cc = c < c1 ? c : c1 - 1;
+        const float* rp = crec + (size_t)cc * G * W;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float2 ml = *reinterpret_cast<const float2*>(rp + g * W);
+          rm[i][g] = c < c1 ? ml.x : -INFINITY;
+          rl[i][g] = ml.y;
+#pragma unroll
+          for (int e = 0; e < VPL; ++e) racc[i][g][e] = rp[g * W + 4 + lane * VPL + e];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) fold_record<D, G>(st, rm[i], rl[i], racc[i]);
+    }
+  }
+  store_wave_record<D, G>(st, recs + wave * G * W, lane);
+  __syncthreads();
+
+  // ================================================================ merge
+  if (P == 1) {
+    finalize_records<D, G, NT>(recs, NW, a.out + (size_t)unit * G * D,
+                               a.lse ? a.lse + (size_t)unit * G : nullptr, scl);
+    if (h == 0 && tid == 0 && room) a.seq_len[s] = T;
+  } else {
+    merge_records<D, G, NT>(recs, NW, a.part + ((size_t)unit * P + p) * G * W, scl);
+  }
+}
+
+// P > 1: one workgroup per unit merges the parts; the unit's first head
+// advances seq_len.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void step_merge_kernel(StepArgs a) {
+  constexpr int W = rec_words(D);
+  constexpr int CAP = stage_cap<G>();
+  __shared__ __align__(16) float recs[CAP * G * W];
+  __shared__ float scl[CAP * G + 3 * G];
+  const int unit = blockIdx.x;
+  const int s = unit / a.H, h = unit - s * a.H;
+  finish_unit<D, G>(a.part + (size_t)unit * a.P * G * W, a.P, a.out + (size_t)unit * G * D,
+                    a.lse ? a.lse + (size_t)unit * G : nullptr, recs, CAP, scl);
+  if (h == 0 && threadIdx.x == 0) {
+    const int T0 = a.t0[s];
+    if (T0 < (long)a.cap_blocks * kBlock) a.seq_len[s] = T0 + 1;
+  }
+}
+
+hipError_t launch_step(int d, int G, const StepArgs& a, int U, hipStream_t st) {
+  void* args[] = {(void*)&a};
+  const void* f = nullptr;
+  const void* m = nullptr;
+#define CKNV_STEP_CASE(DD, GG)                          \
+  if (d == DD && G == GG) {                             \
+    f = (const void*)step_kernel<DD, GG>;               \
+    m = (const void*)step_merge_kernel<DD, GG>;         \
+  }
+  CKNV_STEP_CASE(64, 1) CKNV_STEP_CASE(64, 2) CKNV_STEP_CASE(64, 4) CKNV_STEP_CASE(64, 8)
+  CKNV_STEP_CASE(128, 1) CKNV_STEP_CASE(128, 2) CKNV_STEP_CASE(128, 4) CKNV_STEP_CASE(128, 8)
+#undef CKNV_STEP_CASE
+  if (!f || !m) return hipErrorInvalidValue;
+  hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(step_threads(G)), args, 0, st);
+  if (e != hipSuccess || a.P == 1) return e;
+  return hipLaunchKernel(m, dim3(U), dim3(kThreads), args, 0, st);
+}
+
+}  // namespace cknv

@@ -14,26 +14,21 @@
 
 namespace cknv {
 
-// Mean and population variance of x[0..n) (n in 1..16), x held in registers.
-__device__ __forceinline__ void mean_var16(const float (&x)[16], int n, float& mean, float& var) {
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) s += (j < n) ? x[j] : 0.f;
-  mean = s / (float)n;
-  float q = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float dl = x[j] - mean;
-    q += (j < n) ? dl * dl : 0.f;
-  }
-  var = q / (float)n;
-}
-
 // D̄_t = mean of the coordinate variances of group t = [t*gs, (t+1)*gs).
-__device__ __forceinline__ float group_mean(const float* cvar, int t, int gs) {
-  float s = 0.f;
-  for (int m = 0; m < gs; ++m) s += cvar[t * gs + m];
-  return s / (float)gs;
+// The D coordinate variances of `nslot` blocks sit in cvar[slot*D + c]; the
+// workgroup sums each group as a balanced pairwise tree (each node = left +
+// right, the order a lane butterfly gives), leaving the sum in cvar[t*gs].
+// Every thread of the workgroup must call this.
+template <int D, int NTH>
+__device__ __forceinline__ void group_tree_sums(float* cvar, int nslot, int gs) {
+  for (int len = 1; len < gs; len <<= 1) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nslot * D; i += NTH) {
+      const int c = i % D;
+      if (c % (2 * len) == 0) cvar[i] += cvar[i + len];
+    }
+  }
+  __syncthreads();
 }
 
 // One workgroup per sequence: thread (h, c) handles key coordinate c of head
@@ -51,10 +46,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int b = T / kBlock;
   const int n = T - b * kBlock + 1;  // tokens in the block once the new one is in
   const int hl = threadIdx.x / D, c = threadIdx.x % D;
+  const int gs = D / a.r;
   for (int h0 = 0; h0 < a.H; h0 += HPI) {
     const int h = h0 + hl;
     const bool act = room && h < a.H;
     const int unit = s * a.H + h;
+    const size_t row = (size_t)unit * a.cap_blocks + b;
+    float kv = 0.f;
     if (act) {
       const size_t tok0 = (size_t)unit * cap_tok + (size_t)b * kBlock;
       const uint16_t* kb = a.k + tok0 * D + c;
@@ -72,20 +70,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
       a.k[(tok0 + n - 1) * D + c] = nk;
       a.v[(tok0 + n - 1) * D + c] = nv;
-      float km, kv, vm, vv;
+      float km, vm, vv;
       mean_var16(kx, n, km, kv);
       mean_var16(vx, n, vm, vv);
-      const size_t row = (size_t)unit * a.cap_blocks + b;
       a.kbar[row * D + c] = km;
       a.vbar[row * D + c] = vm;
-      cvar[threadIdx.x] = kv;
       if (c == 0) a.cnt[row] = (float)n;
     }
     __syncthreads();
-    if (act && c < a.r) {
-      const size_t row = (size_t)unit * a.cap_blocks + b;
-      a.dbar[row * a.r + c] = group_mean(cvar + hl * D, c, D / a.r);
-    }
+    cvar[threadIdx.x] = kv;
+    group_tree_sums<D, kAppendThreads>(cvar, HPI, gs);
+    if (act && c % gs == 0) a.dbar[row * a.r + c / gs] = cvar[threadIdx.x] / (float)gs;
     __syncthreads();
   }
   if (threadIdx.x == 0 && room) a.seq_len[s] = T + 1;
@@ -104,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
   NB = NB < a.max_blocks ? NB : a.max_blocks;
   const int b = blockIdx.x * SLOTS + slot;
   const bool valid = b < NB;
+  float kv = 0.f;
   if (valid) {
     const int n = (T - b * kBlock) < kBlock ? (T - b * kBlock) : kBlock;
     const size_t tok0 = (size_t)unit * cap_tok + (size_t)b * kBlock;
@@ -115,19 +111,20 @@ __global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
       kx[j] = (j < n) ? bf16_1(kb[(size_t)j * D]) : 0.f;
       vx[j] = (j < n) ? bf16_1(vb[(size_t)j * D]) : 0.f;
     }
-    float km, kv, vm, vv;
+    float km, vm, vv;
     mean_var16(kx, n, km, kv);
     mean_var16(vx, n, vm, vv);
     const size_t row = (size_t)unit * a.cap_blocks + b;
     a.kbar[row * D + c] = km;
     a.vbar[row * D + c] = vm;
-    cvar[threadIdx.x] = kv;
     if (c == 0) a.cnt[row] = (float)n;
   }
-  __syncthreads();
-  if (valid && c < a.r) {
+  cvar[threadIdx.x] = kv;
+  const int gs = D / a.r;
+  group_tree_sums<D, kThreads>(cvar, SLOTS, gs);
+  if (valid && c % gs == 0) {
     const size_t row = (size_t)unit * a.cap_blocks + b;
-    a.dbar[row * a.r + c] = group_mean(cvar + slot * D, c, D / a.r);
+    a.dbar[row * a.r + c / gs] = cvar[threadIdx.x] / (float)gs;
   }
 }
 

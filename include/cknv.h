@@ -8,6 +8,8 @@
  *   cknv_score_select  score every block, keep the forced set + Top-K
  *   cknv_attend        exact attention over kept blocks + Mean compensation
  *
+ * or as one call, cknv_decode_step, which fuses the three.
+ *
  * Method: the CompKV page (onedev.kr/papers/157). Section names cited below:
  *   "How it works"  -- Mean compensation, GQA group, budget of K blocks;
  *   "What differs"  -- block summary, estimators z̄, σ̂², p̂, S_b, forced set,
@@ -94,9 +96,9 @@ typedef struct cknv_cache {
 int cknv_workspace_size(const cknv_shape* shape, int32_t max_blocks, int32_t budget_tokens,
                         size_t* bytes);
 
-/* Zero the workspace's synchronisation counters. Call once after allocating
- * a workspace (the library returns them to zero after every call). Enqueues
- * a kernel (no memset), so it may be captured in a graph. */
+/* Zero-fill the workspace. Optional: every call writes the workspace
+ * regions it reads before reading them. Enqueues a kernel (no memset), so
+ * it may be captured in a graph. */
 int cknv_workspace_init(const cknv_shape* shape, int32_t max_blocks, int32_t budget_tokens,
                         void* ws, size_t ws_bytes, void* stream);
 
@@ -152,6 +154,22 @@ int cknv_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q
                 const int32_t* sel, const int32_t* n_sel, int32_t budget_tokens,
                 int32_t max_blocks, float* out, float* lse, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* One whole decode step, fused: the same results as cknv_append, then
+ * cknv_score_select, then cknv_attend on the same arguments, in two or three
+ * kernel launches instead of five or six.
+ *   - new_k, new_v: bfloat16 [S][H][d], the step's token ("How to use it":
+ *     the new K/V are stored and the current block's statistics refreshed);
+ *   - q, budget_tokens, scores, sel, n_sel: as for cknv_score_select, with
+ *     NB counted after the append; out, lse: as for cknv_attend.
+ * max_blocks bounds NB after the append. seq_len[s] advances by one for
+ * every sequence whose cache has room (a full cache is left unchanged and
+ * the step attends its existing tokens). The workspace regions are those of
+ * cknv_score_select / cknv_attend plus the step's own. */
+int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                     const uint16_t* new_v, const float* q, int32_t budget_tokens,
+                     int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel, float* out,
+                     float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Full (dense) softmax attention over every cached token, the baseline the
  * page compares CompKV with ("Assumptions and limits"). Same q/out/lse

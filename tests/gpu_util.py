@@ -119,3 +119,28 @@ def summaries_equal(cache, data, w, s, h, T, rtol=1e-4, atol=2e-6):
            cache.dbar[s, h, :NB].cpu().numpy(), cache.vbar[s, h, :NB].cpu().numpy())
     for name, g, r in zip(("cnt", "kbar", "dbar", "vbar"), got, ref):
         np.testing.assert_allclose(g, r, rtol=rtol, atol=atol, err_msg=name)
+
+
+def step_and_check(w, data, cache, dec, step, units=None, check_summaries=False):
+    """Append token prefill+step, score/select, attend; compare the listed units."""
+    t_idx = [p + step for p in data["prefill"]]
+    nk, nv = new_token(data, t_idx)
+    import torch
+    q = torch.from_numpy(data["q"][step]).cuda()
+    dec(q, nk, nv)
+    torch.cuda.synchronize()
+    sel, nsel = dec.sel.cpu().numpy(), dec.n_sel.cpu().numpy()
+    out, lse = dec.out.cpu().numpy(), dec.lse.cpu().numpy()
+    scores = dec.scores.cpu().numpy() if dec.scores is not None else None
+    assert np.all(cache.seq_len.cpu().numpy() == np.asarray(t_idx) + 1)
+    worst = 0.0
+    for s in range(w.S):
+        for h in range(w.H):
+            if units is not None and (s, h) not in units:
+                continue
+            T = t_idx[s] + 1
+            worst = max(worst, check_unit(w, data, s, h, T, step, data["q"][step], sel, nsel,
+                                             out, lse, scores, w.budget))
+            if check_summaries:
+                summaries_equal(cache, data, w, s, h, T)
+    return worst

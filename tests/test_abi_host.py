@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = cknv.lib()
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
 
@@ -123,3 +123,24 @@ def test_entry_points_reject_before_launch():
     assert L.cknv_build_summaries(ctypes.byref(sh), ctypes.byref(c), 5000, None) == cknv.ENOSPACE
     assert L.cknv_score_select(None, ctypes.byref(c), FAKE, 512, 2048, None, FAKE, FAKE, FAKE,
                                need, None) == cknv.EINVAL
+
+
+def test_decode_step_rejects_before_launch():
+    sh = shape()
+    c = cache_struct()
+    L = cknv.lib()
+    _, need = wsize(sh)
+
+    def call(new_k=FAKE, new_v=FAKE, q=FAKE, budget=512, mb=2048, sel=FAKE, n_sel=FAKE, out=FAKE,
+             ws=FAKE, ws_bytes=need, cache=c, shp=sh):
+        return L.cknv_decode_step(ctypes.byref(shp) if shp is not None else None,
+                                  ctypes.byref(cache) if cache is not None else None, new_k, new_v,
+                                  q, budget, mb, None, sel, n_sel, out, None, ws, ws_bytes, None)
+
+    for kw in (dict(new_k=None), dict(new_v=None), dict(q=None), dict(sel=None),
+               dict(n_sel=None), dict(out=None), dict(ws=None), dict(cache=None), dict(shp=None),
+               dict(budget=47), dict(mb=0)):
+        assert call(**kw) == cknv.EINVAL, kw
+    assert call(ws_bytes=need - 1) == cknv.ENOSPACE
+    assert call(mb=2101) == cknv.ENOSPACE
+    assert call(cache=cache_struct("seq_len")) == cknv.EINVAL

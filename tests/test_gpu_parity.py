@@ -24,30 +24,6 @@ def say(msg):
     sys.stdout.flush()
 
 
-def step_and_check(w, data, cache, dec, step, units=None, check_summaries=False):
-    """Append token prefill+step, score/select, attend; compare the listed units."""
-    t_idx = [p + step for p in data["prefill"]]
-    nk, nv = gu.new_token(data, t_idx)
-    q = torch.from_numpy(data["q"][step]).cuda()
-    dec(q, nk, nv)
-    torch.cuda.synchronize()
-    sel, nsel = dec.sel.cpu().numpy(), dec.n_sel.cpu().numpy()
-    out, lse = dec.out.cpu().numpy(), dec.lse.cpu().numpy()
-    scores = dec.scores.cpu().numpy() if dec.scores is not None else None
-    assert np.all(cache.seq_len.cpu().numpy() == np.asarray(t_idx) + 1)
-    worst = 0.0
-    for s in range(w.S):
-        for h in range(w.H):
-            if units is not None and (s, h) not in units:
-                continue
-            T = t_idx[s] + 1
-            worst = max(worst, gu.check_unit(w, data, s, h, T, step, data["q"][step], sel, nsel,
-                                             out, lse, scores, w.budget))
-            if check_summaries:
-                gu.summaries_equal(cache, data, w, s, h, T)
-    return worst
-
-
 def run_single_step(w, units=None, check_summaries=True):
     say(f"workload {w.name}: S={w.S} H={w.H} G={w.G} d={w.d} r={w.r} budget={w.budget} "
         f"prefill={w.prefill[:4]}")
@@ -55,7 +31,7 @@ def run_single_step(w, units=None, check_summaries=True):
     mb = w.max_blocks_after(0)
     cache = gu.upload(w, data, max_blocks=mb)
     dec = cknv.DecodeStep(cache, mb, w.budget, want_scores=True)
-    return step_and_check(w, data, cache, dec, 0, units, check_summaries)
+    return gu.step_and_check(w, data, cache, dec, 0, units, check_summaries)
 
 
 def test_tiny_step():
@@ -85,7 +61,7 @@ def test_streaming_with_block_closes_shortened():
     cache = gu.upload(w, data, max_blocks=mb)
     dec = cknv.DecodeStep(cache, mb, w.budget, want_scores=True)
     for step in range(w.steps):
-        step_and_check(w, data, cache, dec, step, check_summaries=(step % 13 == 0))
+        gu.step_and_check(w, data, cache, dec, step, check_summaries=(step % 13 == 0))
     T = w.prefill[0] + w.steps
     for h in range(w.H):
         gu.summaries_equal(cache, data, w, 0, h, T)
@@ -109,7 +85,7 @@ def test_streaming_qwen8b_128k_full():
     for step in range(w.steps):
         if step in (0, 15, 16, 47, 63):
             say(f"  step {step} checked")
-            step_and_check(w, data, cache, dec, step, check_summaries=(step == 63))
+            gu.step_and_check(w, data, cache, dec, step, check_summaries=(step == 63))
         else:
             t_idx = [p + step for p in data["prefill"]]
             nk, nv = gu.new_token(data, t_idx)
@@ -129,7 +105,7 @@ def test_ragged_batch_shortened():
     cache = gu.upload(w, data, max_blocks=mb)
     dec = cknv.DecodeStep(cache, mb, w.budget, want_scores=True)
     for step in range(w.steps):
-        step_and_check(w, data, cache, dec, step, check_summaries=(step == w.steps - 1))
+        gu.step_and_check(w, data, cache, dec, step, check_summaries=(step == w.steps - 1))
 
 
 @pytest.mark.parametrize("budget", [48, 128])
@@ -142,7 +118,7 @@ def test_short_contexts_keep_everything(budget):
     cache = gu.upload(w, data, max_blocks=mb)
     dec = cknv.DecodeStep(cache, mb, w.budget, want_scores=True)
     for step in range(w.steps):
-        step_and_check(w, data, cache, dec, step, check_summaries=True)
+        gu.step_and_check(w, data, cache, dec, step, check_summaries=True)
 
 
 def test_empty_sequence_outputs_zero():
@@ -175,7 +151,7 @@ def test_constant_blocks_tie_to_lower_index():
         k[:, :, 16 * b:16 * b + 16] = k[:, :, 16 * b:16 * b + 1]
     cache = gu.upload(w, data, max_blocks=50)
     dec = cknv.DecodeStep(cache, 50, w.budget, want_scores=True)
-    step_and_check(w, data, cache, dec, 0, check_summaries=True)
+    gu.step_and_check(w, data, cache, dec, 0, check_summaries=True)
     sel = dec.sel.cpu().numpy()
     for u in range(2):
         assert sel[u].tolist() == list(range(8)) + [48, 49]
@@ -195,7 +171,7 @@ def test_long_ties_take_lowest_indices():
         k[:, :, 16 * b:16 * b + 16] = k[:, :, 16 * b:16 * b + 1]
     cache = gu.upload(w, data, max_blocks=NBk)
     dec = cknv.DecodeStep(cache, NBk, w.budget, want_scores=True)
-    step_and_check(w, data, cache, dec, 0, check_summaries=False)
+    gu.step_and_check(w, data, cache, dec, 0, check_summaries=False)
     sel = dec.sel.cpu().numpy()
     for u in range(2):
         assert sel[u].tolist() == list(range(8)) + [NBk - 2, NBk - 1]
@@ -213,7 +189,7 @@ def test_mixed_ties_at_the_cut():
         k[:, :, 16 * b:16 * b + 16] = k[:, :, 16 * b:16 * b + 1]
     cache = gu.upload(w, data, max_blocks=NBk)
     dec = cknv.DecodeStep(cache, NBk, w.budget, want_scores=True)
-    step_and_check(w, data, cache, dec, 0, check_summaries=False)
+    gu.step_and_check(w, data, cache, dec, 0, check_summaries=False)
 
 
 @pytest.mark.parametrize("d,G,r", [(64, 1, 1), (64, 2, 16), (64, 8, 64), (128, 1, 8),
@@ -226,7 +202,7 @@ def test_shape_variants(d, G, r):
     cache = gu.upload(w, data, max_blocks=mb)
     dec = cknv.DecodeStep(cache, mb, w.budget, want_scores=True)
     for step in range(w.steps):
-        step_and_check(w, data, cache, dec, step, check_summaries=True)
+        gu.step_and_check(w, data, cache, dec, step, check_summaries=True)
 
 
 def test_determinism_bitwise():
