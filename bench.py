@@ -1,18 +1,24 @@
 #!/usr/bin/env python3
 """CompKV decode-step benchmark on one MI355X.
 
-One step = one layer's decode step for the workload's batch: append the new
-token (and refresh its block's summary), score + select, attend (exact kept
-blocks + Mean compensation). Inputs are the seeded synthetic workload,
-resident in HBM before timing. Steps rotate over R copies of the layer
-("layers") at distinct addresses so the per-step working set cannot stay in
-the 256 MB Infinity Cache.
+One step = one layer's decode step for the workload's batch, through the
+fused entry point cknv_decode_step: the streaming scoring pass over the
+summaries (score_kernel), then append + refresh of the block the token lands
+in + normalisers + selection + exact attention with Mean compensation
+(step_kernel, and step_merge_kernel when a unit's kept blocks are split over
+several workgroups). Inputs are the seeded synthetic workload, resident in
+HBM before timing. Steps rotate over R copies of the layer ("layers") at
+distinct addresses so the per-step working set cannot stay in the 256 MB
+Infinity Cache.
 
-Prints ONE JSON line. `value` = steps/s from HIP-graph replay of whole
-layer sweeps (HIP events around the timed replays). `roofline` is for the
-dominant kernel (score + select), its duration measured with HIP events on
-the launch stream. `cpu_baseline` times the fp64 oracle's per-step path on a
-bounded sample on the host.
+Prints ONE JSON line. `value` = steps/s from HIP-graph replay of whole layer
+sweeps (HIP events around exactly K timed steps). `roofline` is for the
+dominant kernel, the streaming score_kernel (issued alone by
+cknv_decode_score): its algorithmic bytes per launch over its average
+duration, measured with HIP events on the launch stream inside eager full
+steps. `cpu_baseline` times the fp64 oracle's per-step path on a bounded
+sample on the host. The three-call path (cknv_append, cknv_score_select,
+cknv_attend) and the dense baseline are reported beside it.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_32k]
 """
@@ -33,7 +39,6 @@ METRIC = "decode steps/sec (1 layer, B=1) at 32K/128K ctx + achieved HBM GB/s vs
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 SCORE_SOURCES = ["block_sparse_kv_stats_amd/csrc/score.hip",
-                 "block_sparse_kv_stats_amd/csrc/select.hip",
                  "block_sparse_kv_stats_amd/csrc/cknv_internal.h"]
 
 
@@ -50,14 +55,17 @@ def kernel_source_hash(paths) -> str:
 
 
 def step_bytes(w, T: int):
-    """Algorithmic HBM bytes of one step over all units, split by kernel.
-    score: k̄ + D̄ + |b| of every block and v̄ of the unselected blocks;
-    attend: BF16 K and V of the kept blocks' tokens."""
+    """Algorithmic HBM bytes of one fused step over all units, split by
+    kernel (T = tokens after the step's append).
+    score_kernel: k̄ + D̄ + |b| of every block closed before the step and v̄
+    of those of them that are not kept;
+    step_kernel: BF16 K and V of the kept blocks' tokens."""
     U = w.S * w.H
     NB = math.ceil(T / 16)
-    Kb = w.Kb
-    kept = min(Kb, NB)
-    score = U * (NB * (w.d + w.r + 1) * 4 + (NB - kept) * w.d * 4)
+    closed = (T - 1) // 16
+    kept = min(w.Kb, NB)
+    kept_closed = kept - (NB - closed)  # the block holding the new token is always kept
+    score = U * (closed * (w.d + w.r + 1) * 4 + (closed - kept_closed) * w.d * 4)
     open_n = T - 16 * (NB - 1)
     kept_tokens = (kept - 1) * 16 + open_n
     attend = U * kept_tokens * 2 * w.d * 2
@@ -178,28 +186,30 @@ def time_eager_steps(torch, timer, stream, bench, n):
         timer.head_start(5.0 + 0.08 * n)
         e0.record(stream)
         for i in range(n):
-            bench.bound[i % bench.R].step()
+            bench.bound[i % bench.R].fused_step()
         e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
 
 
 def time_kernel_events(torch, timer, stream, bench, n, which):
-    """Average and median duration (ms) of one entry point's launch inside
-    full decode steps, bracketed by HIP events on the launch stream."""
+    """Average and median duration (ms) of one half of the fused step inside
+    full eager steps, bracketed by HIP events on the launch stream."""
     evs = [(timer.event(), timer.event()) for _ in range(n)]
     with torch.cuda.stream(stream):
         timer.head_start(5.0 + 0.12 * n)
         for i in range(n):
             b = bench.bound[i % bench.R]
-            b.append()
-            if which == "attend":
-                b.score_select()
-            evs[i][0].record(stream)
-            getattr(b, which)()
-            evs[i][1].record(stream)
-            if which == "score_select":
-                b.attend()
+            if which == "decode_score":
+                evs[i][0].record(stream)
+                b.decode_score()
+                evs[i][1].record(stream)
+                b.decode_finish()
+            else:
+                b.decode_score()
+                evs[i][0].record(stream)
+                b.decode_finish()
+                evs[i][1].record(stream)
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(c) for a, c in evs)
     return sum(ts) / len(ts), ts[len(ts) // 2]
@@ -238,10 +248,10 @@ def cpu_baseline(w, seconds: float):
                       f"({dt:.1f} s, fp64 NumPy, 1 thread), scaled x{U} units per step"}
 
 
-def traffic_from_profile(workload, launches_bytes):
-    """HBM bytes per score launch from a committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"score_select_{workload}_pmc.json")
+def traffic_from_profile(workload):
+    """HBM bytes per score_kernel launch from a committed rocprofv3 PMC
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"score_kernel_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -261,22 +271,24 @@ def run_workload(torch, timer, wname, args, stream, want_dense=True):
     n_e = min(steps, 256)
     kernel_n = min(max(2 * R, 64), 256)
     appends = (math.ceil(warm / R) + math.ceil(steps / R) + math.ceil(n_e / R)
-               + 2 * math.ceil(kernel_n / R) + 4)
+               + 2 * math.ceil(kernel_n / R) + math.ceil(max(R, steps // 4) / R) + 4)
     bench = Bench(w, R, appends, stream)
     log(f"{wname}: {R} layers, {warm} warm-up + {steps} timed steps")
     with torch.cuda.stream(stream):
         for i in range(warm):
-            bench.bound[i % R].step()
+            bench.bound[i % R].fused_step()
     torch.cuda.synchronize()
-    ms_step = time_graph_steps(torch, timer, stream, bench, steps)
+    ms_step = time_graph_steps(torch, timer, stream, bench, steps, which="fused_step")
     ms_eager = time_eager_steps(torch, timer, stream, bench, n_e)
-    k_avg, k_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "score_select")
-    a_avg, a_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "attend")
+    k_avg, k_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "decode_score")
+    f_avg, f_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "decode_finish")
+    ms_three = time_graph_steps(torch, timer, stream, bench, max(R, steps // 4), which="step")
     T = bench.seq_len()
     sb, ab = step_bytes(w, T)
     res = {"w": w, "R": R, "steps": steps, "warmup": warm, "ms_step": ms_step,
            "ms_eager": ms_eager, "T": T, "score_bytes": sb, "attend_bytes": ab,
-           "score_ms": k_avg, "score_ms_median": k_med, "attend_ms": a_avg}
+           "score_ms": k_avg, "score_ms_median": k_med, "finish_ms": f_avg,
+           "ms_three_calls": ms_three}
     if want_dense:
         res["dense_ms_step"] = time_graph_steps(torch, timer, stream, bench, max(R, steps // 4),
                                                 which="dense")
@@ -336,7 +348,7 @@ def main():
     value = 1000.0 / main_res["ms_step"]
     score_gbps = main_res["score_bytes"] / (main_res["score_ms"] * 1e-3) / 1e9
     step_gbps = (main_res["score_bytes"] + main_res["attend_bytes"]) / (main_res["ms_step"] * 1e-3) / 1e9
-    traffic = traffic_from_profile(args.workload, main_res["score_bytes"])
+    traffic = traffic_from_profile(args.workload)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -352,17 +364,22 @@ def main():
         "data": "synthetic (seeded generator: block-structured bf16 keys, 1% needles, N(0,1) values)",
         "config": {"workload": w.name, "S": w.S, "H": w.H, "G": w.G, "d": w.d, "r": w.r,
                    "context_tokens": main_res["T"], "budget_tokens": w.budget,
-                   "layers_rotated": main_res["R"], "launch": "hipGraph replay of layer sweeps"},
+                   "layers_rotated": main_res["R"],
+                   "launch": "hipGraph replay of layer sweeps of cknv_decode_step"},
         "step_GBps": round(step_gbps, 1),
         "eager_ms_per_step": round(main_res["ms_eager"], 5),
-        "roofline": {"bound": "hbm", "kernel": "score_select",
+        "roofline": {"bound": "hbm", "kernel": "score_kernel (cknv_decode_score)",
                      "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": main_res["score_bytes"],
-                     "avg_launch_us": round(main_res["score_ms"] * 1e3, 3)},
-        "attend_kernel": {"avg_launch_us": round(main_res["attend_ms"] * 1e3, 3),
-                          "algorithmic_bytes_per_launch": main_res["attend_bytes"]},
+                     "avg_launch_us": round(main_res["score_ms"] * 1e3, 3),
+                     "median_launch_us": round(main_res["score_ms_median"] * 1e3, 3)},
+        "finish_kernels": {"kernels": "step_kernel + step_merge_kernel (cknv_decode_finish)",
+                           "avg_us": round(main_res["finish_ms"] * 1e3, 3),
+                           "algorithmic_bytes": main_res["attend_bytes"]},
+        "three_call_path": {"steps_per_s": round(1000.0 / main_res["ms_three_calls"], 2),
+                            "calls": "cknv_append + cknv_score_select + cknv_attend"},
     }
     if "dense_ms_step" in main_res:
         line["dense_baseline"] = {
@@ -378,7 +395,9 @@ def main():
             "layers_rotated": extra["R"],
             "step_GBps": round((extra["score_bytes"] + extra["attend_bytes"]) / (extra["ms_step"] * 1e-3) / 1e9, 1),
             "score_kernel_GBps": round(e_score, 1), "score_frac": round(e_score / PEAK_HBM_GBPS, 4),
-            "score_avg_launch_us": round(extra["score_ms"] * 1e3, 3)}
+            "score_avg_launch_us": round(extra["score_ms"] * 1e3, 3),
+            "finish_avg_us": round(extra["finish_ms"] * 1e3, 3),
+            "three_call_steps_per_s": round(1000.0 / extra["ms_three_calls"], 2)}
         if "dense_ms_step" in extra:
             line["also"]["dense_steps_per_s"] = round(1000.0 / extra["dense_ms_step"], 2)
             line["also"]["speedup_of_compkv"] = round(extra["dense_ms_step"] / extra["ms_step"], 3)

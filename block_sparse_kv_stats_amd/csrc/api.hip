@@ -48,7 +48,7 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   bpw = bpw > kDenseBlocksPerWG ? bpw : kDenseBlocksPerWG;
   q.BPW = bpw;
   q.Pd = (max_blocks + bpw - 1) / bpw;
-  q.Pf = (q.Kb + step_kpart(G) - 1) / step_kpart(G);
+  q.Pf = (q.Kb + kStepKeptPerPart - 1) / kStepKeptPerPart;
   const size_t W = (size_t)rec_words(d);
   size_t off = 0;
   q.off_grp = off;
@@ -152,17 +152,8 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   return hip_status(launch_select(shape->G, sa, p.U, (hipStream_t)stream));
 }
 
-int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
-                     const uint16_t* new_v, const float* q, int32_t budget_tokens,
-                     int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel, float* out,
-                     float* lse, void* ws, size_t ws_bytes, void* stream) {
-  Plan p;
-  int st = make_plan(shape, max_blocks, budget_tokens, &p);
-  if (st) return st;
-  if ((st = check_cache(cache))) return st;
-  if (!new_k || !new_v || !q || !sel || !n_sel || !out || !ws) return CKNV_EINVAL;
-  if (ws_bytes < p.total) return CKNV_ENOSPACE;
-  char* w = static_cast<char*>(ws);
+static int decode_score_impl(const Plan& p, const cknv_shape* shape, const cknv_cache* cache,
+                             const float* q, int32_t max_blocks, char* w, void* stream) {
   ScoreArgs a{};
   a.kbar = cache->kbar; a.dbar = cache->dbar; a.cnt = cache->cnt; a.vbar = cache->vbar;
   a.seq_len = cache->seq_len; a.q = q;
@@ -175,19 +166,73 @@ int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uin
   a.closed_only = 1;
   a.t0_out = reinterpret_cast<int32_t*>(w + p.off_t0);
   a.isd = 1.0f / sqrtf((float)shape->d);
-  hipError_t e = launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream);
-  if (e != hipSuccess) return CKNV_EHIP;
+  return hip_status(launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream));
+}
+
+static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv_cache* cache,
+                              const uint16_t* new_k, const uint16_t* new_v, const float* q,
+                              int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel,
+                              float* out, float* lse, char* w, void* stream) {
   StepArgs sa{};
   sa.k = cache->k; sa.v = cache->v; sa.kbar = cache->kbar; sa.dbar = cache->dbar;
-  sa.cnt = cache->cnt; sa.vbar = cache->vbar; sa.seq_len = cache->seq_len; sa.t0 = a.t0_out;
+  sa.cnt = cache->cnt; sa.vbar = cache->vbar; sa.seq_len = cache->seq_len;
+  sa.t0 = reinterpret_cast<const int32_t*>(w + p.off_t0);
   sa.new_k = new_k; sa.new_v = new_v; sa.q = q;
-  sa.grp = a.grp; sa.u = a.u; sa.comp = a.comp;
+  sa.grp = reinterpret_cast<const float*>(w + p.off_grp);
+  sa.u = reinterpret_cast<const float*>(w + p.off_u);
+  sa.comp = reinterpret_cast<const float*>(w + p.off_comp);
   sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel; sa.out = out; sa.lse = lse;
   sa.part = reinterpret_cast<float*>(w + p.off_fpart);
   sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
   sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf;
-  sa.isd = a.isd;
+  sa.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_step(shape->d, shape->G, sa, p.U, (hipStream_t)stream));
+}
+
+static int decode_check(const cknv_shape* shape, const cknv_cache* cache, int32_t max_blocks,
+                        int32_t budget_tokens, const void* ws, size_t ws_bytes, Plan* p) {
+  int st = make_plan(shape, max_blocks, budget_tokens, p);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!ws) return CKNV_EINVAL;
+  if (ws_bytes < p->total) return CKNV_ENOSPACE;
+  return CKNV_OK;
+}
+
+int cknv_decode_score(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                      int32_t budget_tokens, int32_t max_blocks, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Plan p;
+  int st = decode_check(shape, cache, max_blocks, budget_tokens, ws, ws_bytes, &p);
+  if (st) return st;
+  if (!q) return CKNV_EINVAL;
+  return decode_score_impl(p, shape, cache, q, max_blocks, static_cast<char*>(ws), stream);
+}
+
+int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                       const uint16_t* new_v, const float* q, int32_t budget_tokens,
+                       int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel,
+                       float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = decode_check(shape, cache, max_blocks, budget_tokens, ws, ws_bytes, &p);
+  if (st) return st;
+  if (!new_k || !new_v || !q || !sel || !n_sel || !out) return CKNV_EINVAL;
+  return decode_finish_impl(p, shape, cache, new_k, new_v, q, max_blocks, scores, sel, n_sel, out,
+                            lse, static_cast<char*>(ws), stream);
+}
+
+int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                     const uint16_t* new_v, const float* q, int32_t budget_tokens,
+                     int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel, float* out,
+                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = decode_check(shape, cache, max_blocks, budget_tokens, ws, ws_bytes, &p);
+  if (st) return st;
+  if (!new_k || !new_v || !q || !sel || !n_sel || !out) return CKNV_EINVAL;
+  char* w = static_cast<char*>(ws);
+  if ((st = decode_score_impl(p, shape, cache, q, max_blocks, w, stream))) return st;
+  return decode_finish_impl(p, shape, cache, new_k, new_v, q, max_blocks, scores, sel, n_sel, out,
+                            lse, w, stream);
 }
 
 static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const float* q,

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   const int c0 = (int)((long)p * a.C / a.P), c1 = (int)((long)(p + 1) * a.C / a.P);
   stage_records<D, G>(a.comp + ((size_t)unit * a.C + c0) * G * W, c1 - c0, recs + kWaves * G * W);
   if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
-  __syncthreads();
+  lds_barrier();
 
   // ---- round 2: the kept blocks' tokens, mean key and value
   int NB = (T + kBlock - 1) / kBlock;
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   for (int i = 0; i < kBlocksPerAttendWave; ++i)
     if (use[i]) absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
-  __syncthreads();
+  lds_barrier();
 
   float* po = a.part + ((size_t)unit * a.P + p) * G * W;
   merge_records<D, G>(recs, kWaves + (c1 - c0), po, scl);
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
   const int T = a.seq_len[s];
   const float4 qv = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : G * D / 4 - 1];
   if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
-  __syncthreads();
+  lds_barrier();
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < a.max_blocks ? NB : a.max_blocks;
   const long cap_tok = (long)a.cap_blocks * kBlock;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
     if (u1) absorb<D, G, false>(st, t1, none, q_l, lane, a.isd);
   }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
-  __syncthreads();
+  lds_barrier();
   merge_records<D, G>(recs, kWaves, a.part + ((size_t)unit * a.P + p) * G * W, scl);
 }
 

@@ -264,7 +264,7 @@ __device__ __forceinline__ void merge_records(const float* recs, int n, float* d
     dst[tid * W + 2] = 0.f;
     dst[tid * W + 3] = 0.f;
   }
-  __syncthreads();
+  lds_barrier();
   for (int col = tid; col < G * D; col += NT) {
     const int g = col / D, c = col - g * D;
     dst[g * W + 4 + c] = record_column<D, G>(recs, scl, n, g, c);
@@ -314,14 +314,14 @@ __device__ void finish_unit(const float* parts, int P, float* out, float* lse, f
   for (int p0 = 0; p0 < P; p0 += cap) {
     const int n = P - p0 < cap ? P - p0 : cap;
     stage_records<D, G, NT>(parts + (size_t)p0 * G * W, n, stage);
-    __syncthreads();
+    lds_barrier();
     if (tid < G) {
       float M = Mrun[tid], L = Lrun[tid];
       record_scales<D, G>(stage, n, tid, scl, M, L, Srun + tid);
       Mrun[tid] = M;
       Lrun[tid] = L;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int k = 0; k < COLS; ++k) {
       const int col = tid + k * NT;
@@ -330,7 +330,7 @@ __device__ void finish_unit(const float* parts, int P, float* out, float* lse, f
         Ar[k] = Ar[k] * Srun[g] + record_column<D, G>(stage, scl, n, g, c);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 #pragma unroll
   for (int k = 0; k < COLS; ++k) {

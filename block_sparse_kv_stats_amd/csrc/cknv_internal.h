@@ -23,12 +23,17 @@ constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
 constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
 constexpr int kDenseMaxWGs = 64;          // dense attention: workgroups per unit (at most)
-// Fused step kernel: threads per workgroup (the selection owns up to
-// kSelKeysPerThread * kSelThreads / step_threads blocks per thread). Half of
-// the waves attend one kept block each, so a workgroup attends step_kpart(G)
-// kept blocks; the other half fold the scoring pass's compensation records.
-__host__ __device__ constexpr int step_threads(int G) { return G <= 4 ? 1024 : 512; }
-__host__ __device__ constexpr int step_kpart(int G) { return step_threads(G) / 128; }
+// Fused step kernel: one wave per SIMD (256 threads); thread t owns blocks
+// t + 256*j for j < KPTB, KPTB the smallest bucket that covers max_blocks;
+// each wave attends one kept block, so a workgroup attends kStepKeptPerPart
+// of them.
+constexpr int kStepThreads = 256;
+constexpr int kStepKeptPerPart = kStepThreads / 64;
+__host__ __device__ constexpr int step_kptb(int max_blocks) {
+  return max_blocks <= 4 * kStepThreads ? 4 : max_blocks <= 8 * kStepThreads ? 8
+       : max_blocks <= 12 * kStepThreads ? 12 : max_blocks <= 16 * kStepThreads ? 16
+       : max_blocks <= 24 * kStepThreads ? 24 : max_blocks <= 32 * kStepThreads ? 32 : 48;
+}
 constexpr int kSelThreads = 1024;       // selection: one workgroup per unit
 constexpr int kSelKeysPerThread = 12;   // blocks per selection thread: max_blocks <= 12288
 
@@ -45,7 +50,7 @@ struct Plan {
   int Kb;           // block slots of the budget
   int C;            // score workgroups per unit = ceil(NBmax/score_bpwg(G))
   int P;            // attend workgroups per unit
-  int Pf;           // fused-step workgroups per unit = ceil(Kb/step_kpart(G))
+  int Pf;           // fused-step workgroups per unit = ceil(Kb/kStepKeptPerPart)
   int Pd;           // dense-attend workgroups per unit
   int BPW;          // dense-attend blocks per workgroup
   size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, total;
@@ -178,6 +183,15 @@ __device__ __forceinline__ float rows_max(float x) {
   x = fmaxf(l, h);
   l = swap32_lo(x, h);
   return fmaxf(l, h);
+}
+
+// Workgroup barrier for data exchanged through LDS only. __syncthreads()
+// also orders global memory, so it first waits for every outstanding global
+// load and store of the wave; kernels here never read in one wave what
+// another wave of the workgroup wrote to global memory, so waiting for the
+// wave's LDS operations is enough and in-flight global traffic keeps going.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // exp(m - M) with exp(-inf - anything) = 0 (an empty partial contributes nothing).

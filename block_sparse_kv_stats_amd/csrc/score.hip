@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
       cml[(wave * G + tg) * 2 + 1] = lz;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // ---- the workgroup's record: the waves' sums under their common max
   constexpr int CPT = (G * D + kThreads - 1) / kThreads;  // coordinates per thread (1, 2 or 4)
   const int f0 = tid * CPT;

@@ -31,49 +31,6 @@ namespace {
 
 constexpr int kSelWaves = kSelThreads / 64;
 
-// Exclusive prefix over tiles of kSelThreads consecutive items (item order:
-// tile-major, then thread); bit m of `flags` is this thread's flag in tile m.
-// before[m] gets the number of flagged items ahead of this thread's item.
-// `cnt`: LDS scratch of NT*kSelWaves ints.
-template <int NT>
-__device__ __forceinline__ void tile_prefix(uint32_t flags, int (&before)[NT], int* cnt) {
-  constexpr int E = NT * kSelWaves;   // (tile, wave) entries in item order
-  constexpr int PER = (E + 63) / 64;  // entries per lane of wave 0
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 0; m < NT; ++m) {
-    const unsigned long long bal = __ballot((flags >> m) & 1u);
-    before[m] = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) cnt[m * kSelWaves + wave] = __popcll(bal);
-  }
-  __syncthreads();
-  if (wave == 0) {  // exclusive scan of the E counts, in place
-    int v[PER], own = 0;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = lane * PER + k;
-      v[k] = i < E ? cnt[i] : 0;
-      own += v[k];
-    }
-    int incl = own;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    int run = incl - own;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = lane * PER + k;
-      if (i < E) cnt[i] = run;
-      run += v[k];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < NT; ++m) before[m] += cnt[m * kSelWaves + wave];
-}
-
 }  // namespace
 
 template <int G>
@@ -85,7 +42,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ float f[NGmax * G];                 // exp(group max - LSE_g)
   __shared__ float red[kSelWaves * G * 2];
   __shared__ __align__(16) int hist[2048];
-  __shared__ int cnt[KPT * kSelWaves];
+  __shared__ int cnt[KPT * kSelWaves + 1];
   __shared__ uint32_t lkey[kListMax];
   __shared__ int lidx[kListMax];
   __shared__ uint32_t keep_bits[NW];
@@ -153,7 +110,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     const float Lw = group_sum<64>(l);
     if (lane == 0) { red[(wave * G + g) * 2] = Mw; red[(wave * G + g) * 2 + 1] = Lw; }
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float M = -INFINITY;
@@ -167,7 +124,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     for (int k = 0; k < GPT; ++k)
       if (tid + k * kSelThreads < NGu) f[(tid + k * kSelThreads) * G + g] = __expf(gr[k][g] - lse);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- S_b, its key, and the histogram of the candidates' key top 11 bits
   uint32_t key[KPT];
@@ -209,9 +166,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   uint32_t tau_bin = 0xffffffffu;
   bool use_list = true;
   if (krem > 0) {
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) find_bin<2048>(hist, krem, ctl);
-    __syncthreads();
+    lds_barrier();
     tau_bin = (uint32_t)ctl[0];
     krem = ctl[1];
     use_list = ctl[2] <= kListMax;
@@ -228,7 +185,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
         lidx[slot] = tid + m * kSelThreads;
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int n = ctl[3];
     if (tid < n) {
       const uint32_t ki = lkey[tid];
@@ -247,30 +204,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       }
       if (rank < krem) atomicOr(&keep_bits[ii >> 5], 1u << (ii & 31));
     }
-    __syncthreads();
+    lds_barrier();
   } else if (krem > 0) {
     uint32_t prefix = tau_bin << 21;
     // bits 20..10 among the keys of the pivot bin
     hist[tid] = 0;
     hist[tid + kSelThreads] = 0;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int m = 0; m < KPT; ++m)
       if (((candm >> m) & 1u) && (key[m] >> 21) == (prefix >> 21)) atomicAdd(&hist[(key[m] >> 10) & 2047u], 1);
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) find_bin<2048>(hist, krem, ctl);
-    __syncthreads();
+    lds_barrier();
     prefix |= ((uint32_t)ctl[0]) << 10;
     krem = ctl[1];
     // bits 9..0
     hist[tid] = 0;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int m = 0; m < KPT; ++m)
       if (((candm >> m) & 1u) && (key[m] >> 10) == (prefix >> 10)) atomicAdd(&hist[key[m] & 1023u], 1);
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) find_bin<1024>(hist, krem, ctl);
-    __syncthreads();
+    lds_barrier();
     prefix |= (uint32_t)ctl[0];
     krem = ctl[1];
     exact_tau = prefix;
@@ -283,9 +240,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   if (ties_by_index) {
 #pragma unroll
     for (int m = 0; m < KPT; ++m) eqm |= (uint32_t)(((candm >> m) & 1u) && key[m] == exact_tau) << m;
-    __syncthreads();
-    tile_prefix<KPT>(eqm, before, cnt);
-    __syncthreads();
+    lds_barrier();
+    int tot_eq;
+    tile_prefix<KPT, kSelWaves>(eqm, before, cnt, tot_eq);
+    lds_barrier();
   }
   uint32_t takem = 0u;
 #pragma unroll
@@ -301,7 +259,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     }
     takem |= (uint32_t)t << m;
   }
-  tile_prefix<KPT>(takem, before, cnt);
+  int tot_take;
+  tile_prefix<KPT, kSelWaves>(takem, before, cnt, tot_take);
 #pragma unroll
   for (int m = 0; m < KPT; ++m)
     if ((takem >> m) & 1u) sel[before[m]] = tid + m * kSelThreads;

@@ -53,4 +53,51 @@ __device__ __forceinline__ void find_bin(const int* hist, int krem, int* ctl) {
   }
 }
 
+// Exclusive prefix over items in tile-major order: tile m holds items
+// m*NT .. m*NT+NT-1 (thread t's item of tile m is m*NT + t); bit m of
+// `flags` is this thread's flag in tile m. before[m] gets the number of
+// flagged items ahead of this thread's item of tile m; the total goes to
+// *total. `cnt`: LDS scratch of NTILE*NW + 1 ints. Every thread calls this.
+template <int NTILE, int NW>
+__device__ __forceinline__ void tile_prefix(uint64_t flags, int (&before)[NTILE], int* cnt,
+                                            int& total) {
+  constexpr int E = NTILE * NW;       // (tile, wave) entries in item order
+  constexpr int PER = (E + 63) / 64;  // entries per lane of wave 0
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < NTILE; ++m) {
+    const unsigned long long bal = __ballot((flags >> m) & 1u);
+    before[m] = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) cnt[m * NW + wave] = __popcll(bal);
+  }
+  lds_barrier();
+  if (wave == 0) {  // exclusive scan of the E counts, in place; total after them
+    int v[PER], own = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = lane * PER + k;
+      v[k] = i < E ? cnt[i] : 0;
+      own += v[k];
+    }
+    int incl = own;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - own;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = lane * PER + k;
+      if (i < E) cnt[i] = run;
+      run += v[k];
+    }
+    if (lane == 63) cnt[E] = incl;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int m = 0; m < NTILE; ++m) before[m] += cnt[m * NW + wave];
+  total = cnt[E];
+}
+
 }  // namespace cknv

@@ -46,45 +46,20 @@ namespace cknv {
 
 namespace {
 
-template <int G>
+template <int G, int KPTB>
 struct StepCfg {
-  static constexpr int NT = step_threads(G);
+  static constexpr int NT = kStepThreads;
   static constexpr int NW = NT / 64;
-  static constexpr int KPT = kSelThreads * kSelKeysPerThread / NT;  // blocks per thread, at most
-  static constexpr int UB = (24 / G) < KPT ? (24 / G) : KPT;         // blocks per u load batch
+  static constexpr int KPT = KPTB;                                 // blocks per thread
+  static constexpr int BPW = score_bpw(G);                         // blocks per score group
+  static constexpr int NGMAX = (NT * KPT + BPW - 1) / BPW;         // score groups covered
+  static constexpr int GPT = (NGMAX + NT - 1) / NT;                // score groups per thread
+  static constexpr int UB = KPT < 128 / G ? KPT : 128 / G;         // blocks per u load batch
   static constexpr int NBATCH = (KPT + UB - 1) / UB;
-  static constexpr int BPW = score_bpw(G);                           // blocks per score group
-  static constexpr int NGT = (KPT - 1) / BPW + 2;                    // score groups of a thread's blocks
-  static constexpr int NGMAX = kSelThreads * kSelKeysPerThread / BPW;
-  static constexpr int GPT = (NGMAX + NT - 1) / NT;                  // score groups per thread (LSE)
-  static constexpr int KPART = step_kpart(G);                        // kept blocks per workgroup
-  static constexpr int RW = NW - KPART;                              // record-folding waves
-  static constexpr int RPW = 2;                                      // records per wave per batch
+  static constexpr int KPART = kStepKeptPerPart;                   // kept blocks per workgroup
+  static constexpr int RPW = 2;                                    // records per wave per batch
+  static_assert(KPART == NW, "one kept block per wave");
 };
-
-// Exclusive prefix sum over the workgroup of one int per thread (thread
-// order); also returns the total. `scan` is LDS scratch of NW ints.
-template <int NW>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* scan, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) scan[wave] = incl;
-  __syncthreads();
-  int before = incl - v;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int c = scan[w];
-    before += w < wave ? c : 0;
-    total += c;
-  }
-  return before;
-}
 
 // out[g][c] = sum_i rec_i[g][c] e^{m_i - M} / L (and lse = M + ln L) over n
 // records in LDS.
@@ -100,7 +75,7 @@ __device__ __forceinline__ void finalize_records(const float* recs, int n, float
     ML[2 * tid] = M;
     ML[2 * tid + 1] = L;
   }
-  __syncthreads();
+  lds_barrier();
   for (int col = tid; col < G * D; col += NT) {
     const int g = col / D, c = col - g * D;
     const float L = ML[2 * g + 1];
@@ -129,39 +104,37 @@ __device__ __forceinline__ void fold_record(WaveState<D, G>& st, const float (&r
 
 }  // namespace
 
-template <int D, int G>
-__global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
-  using C = StepCfg<G>;
+template <int D, int G, int KPTB>
+__global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
+  using C = StepCfg<G, KPTB>;
   constexpr int NT = C::NT, NW = C::NW, KPT = C::KPT, UB = C::UB, BPW = C::BPW;
-  constexpr int NGT = C::NGT, GPT = C::GPT, KPART = C::KPART, RW = C::RW, RPW = C::RPW;
+  constexpr int GPT = C::GPT, NGMAX = C::NGMAX, KPART = C::KPART, RPW = C::RPW;
   constexpr int W = rec_words(D), VPL = D / 64;
   constexpr int OW = NW - 1;  // the wave that refreshes the fresh block
-  // Selection scratch and the waves' attention records share one LDS area.
-  constexpr int NBITS = KPT * NT / 32;
-  constexpr int SEL_WORDS = 2048 + 2 * kListMax + NBITS;
-  constexpr int REC_WORDS = NW * G * W;
-  constexpr int BIG = SEL_WORDS > REC_WORDS ? SEL_WORDS : REC_WORDS;
-  __shared__ __align__(16) float big[BIG];
-  __shared__ __align__(16) float q_l[G * D];
+  // LDS: area A holds the score-group factors during the keys, then the
+  // query and the waves' attention records; area B the selection scratch.
+  constexpr int NBITS = (KPT * NT + 31) / 32;  // kept-block bitmap of the pivot-bin path
+  constexpr int A_WORDS = NGMAX * G > NW * G * W + G * D ? NGMAX * G : NW * G * W + G * D;
+  __shared__ __align__(16) float areaA[A_WORDS];
+  __shared__ __align__(16) int hist[2048];
+  __shared__ uint32_t lkey[kListMax];
+  __shared__ int lidx[kListMax];
+  __shared__ uint32_t keep_bits[NBITS];
+  __shared__ int cnt[KPT * NW + 1];
   __shared__ float red[NW * G * 2];
   __shared__ float scl[NW * G + 2 * G];
   __shared__ float oinfo[2 * G];  // fresh block: a_g, σ̂²_g
-  __shared__ int scan[NW];
   __shared__ int ctl[8];
   __shared__ int klist[KPART];
-  int* hist = reinterpret_cast<int*>(big);
-  uint32_t* lkey = reinterpret_cast<uint32_t*>(big + 2048);
-  int* lidx = reinterpret_cast<int*>(big + 2048 + kListMax);
-  uint32_t* keep_bits = reinterpret_cast<uint32_t*>(big + 2048 + 2 * kListMax);
-  float* recs = big;
+  float* fgrp = areaA;                   // [NGMAX][G] exp(group max - LSE_g)
+  float* recs = areaA;                   // [NW][G][W] after the selection
+  float* q_l = areaA + NW * G * W;       // [G][D] after the selection
 
   const int P = a.P;
   const int unit = blockIdx.x / P, p = blockIdx.x - unit * P;
   const int s = unit / a.H, h = unit - s * a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int MB = a.max_blocks, Kb = a.Kb;
-  const int KPTm = (MB + NT - 1) / NT;  // <= KPT (checked on the host)
-  const int b0 = tid * KPTm;
   const long cap_tok = (long)a.cap_blocks * kBlock;
   const size_t ubase = (size_t)unit * a.cap_blocks;
   uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
@@ -169,6 +142,8 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
   const float* u = a.u + (size_t)unit * MB * G;
   const float2* grp = reinterpret_cast<const float2*>(a.grp) + (size_t)unit * a.NG * G;
   const int NG = a.NG;
+  // thread tid owns blocks tid + NT*j, j < KPT (NT*KPT >= MB), and score
+  // groups tid + NT*k, k < GPT
 
   // ================================================================ loads
   const int T0 = a.t0[s];
@@ -180,25 +155,18 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) gp[k][g] = grp[(size_t)gc * G + g];
   }
-  const int gA = b0 / BPW;
-  float gref[NGT][G];
-#pragma unroll
-  for (int k = 0; k < NGT; ++k) {
-    const int gc = gA + k < NG ? gA + k : NG - 1;
-#pragma unroll
-    for (int g = 0; g < G; ++g) gref[k][g] = grp[(size_t)gc * G + g].x;
-  }
   float uv[UB][G];
 #pragma unroll
-  for (int m = 0; m < UB; ++m) {
-    const int b = b0 + m;
+  for (int j = 0; j < UB; ++j) {
+    const int b = tid + j * NT;
     const int bc = b < MB ? b : MB - 1;
 #pragma unroll
-    for (int g = 0; g < G; ++g) uv[m][g] = u[(size_t)bc * G + g];
+    for (int g = 0; g < G; ++g) uv[j][g] = u[(size_t)bc * G + g];
   }
-  float4 q4[(G * D / 4 + NT - 1) / NT];
+  constexpr int NQ4 = (G * D / 4 + NT - 1) / NT;
+  float4 q4[NQ4];
 #pragma unroll
-  for (int k = 0; k < (G * D / 4 + NT - 1) / NT; ++k) {
+  for (int k = 0; k < NQ4; ++k) {
     const int i = tid + k * NT;
     q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
   }
@@ -237,11 +205,6 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
   const bool all = NB <= Kb;
   int krem = Kb - 3;
   const bool count = !all && krem > 0;
-#pragma unroll
-  for (int k = 0; k < (G * D / 4 + NT - 1) / NT; ++k) {
-    const int i = tid + k * NT;
-    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
-  }
   for (int i = tid; i < 2048; i += NT) hist[i] = 0;
   for (int i = tid; i < NBITS; i += NT) keep_bits[i] = 0u;
   if (tid == 0) ctl[3] = 0;
@@ -265,7 +228,8 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
       mean_var16(kx, n, km[e], kvr[e]);
       mean_var16(vx, n, vm[e], vvar);
     }
-    // D̄: mean coordinate variance of each contiguous group of gs = D/r coordinates
+    // D̄: mean coordinate variance of each contiguous group of gs = D/r
+    // coordinates, summed as a pairwise tree (the order of the summary kernels)
     const int gs = D / a.r;
     float dl[VPL];
     if (gs >= VPL) {
@@ -335,7 +299,7 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
       red[(wave * G + g) * 2 + 1] = Lw;
     }
   }
-  __syncthreads();
+  lds_barrier();
   float lse_g[G], fa[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -349,52 +313,63 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
     lse_g[g] = L > 0.f ? M + __logf(L) : INFINITY;
     fa[g] = fa_g;
   }
-  float fg[NGT][G];
 #pragma unroll
-  for (int k = 0; k < NGT; ++k)
+  for (int k = 0; k < GPT; ++k) {
+    const int gi = tid + k * NT;
+    if (gi < NGa && gi < NGMAX) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) fg[k][g] = __expf(gref[k][g] - lse_g[g]);
+      for (int g = 0; g < G; ++g) fgrp[gi * G + g] = __expf(gp[k][g].x - lse_g[g]);
+    }
+  }
+  lds_barrier();
 
   // ================================================================ keys
+  // S of the fresh block is the same for every thread; the factor rows of
+  // the thread's blocks are read from LDS up front (group index clamped, the
+  // value is used only for scored blocks).
+  float Sfresh = 0.f;
+  if (fb >= 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) Sfresh += __expf(fa[g] - lse_g[g]) * oinfo[G + g];
+  }
   uint32_t key[KPT];
-  uint32_t candm = 0u;  // bit m: block b0 + m is a Top-K candidate
+  uint64_t candm = 0u;  // bit j: block tid + NT*j is a Top-K candidate
   float* scores = (a.scores && p == 0) ? a.scores + ubase : nullptr;
 #pragma unroll
   for (int bt = 0; bt < C::NBATCH; ++bt) {
-    if (bt > 0 && bt * UB < KPTm) {
+    if (bt > 0) {
 #pragma unroll
       for (int m = 0; m < UB; ++m) {
-        const int b = b0 + bt * UB + m;
+        const int b = tid + (bt * UB + m) * NT;
         const int bc = b < MB ? b : MB - 1;
 #pragma unroll
         for (int g = 0; g < G; ++g) uv[m][g] = u[(size_t)bc * G + g];
       }
     }
+    float fr[UB][G];
 #pragma unroll
     for (int m = 0; m < UB; ++m) {
-      const int mm = bt * UB + m;
-      if (mm >= KPT) break;
-      const int b = b0 + mm;
-      const int k = b / BPW - gA;  // 0..NGT-1 for the thread's blocks
-      float S = 0.f;
-      if (b < NBa) {
+      const int b = tid + (bt * UB + m) * NT;
+      int gi = b / BPW;
+      gi = gi < NGa ? gi : (NGa > 0 ? NGa - 1 : 0);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float f = fg[0][g];
+      for (int g = 0; g < G; ++g) fr[m][g] = fgrp[gi * G + g];
+    }
 #pragma unroll
-          for (int kk = 1; kk < NGT; ++kk) f = k == kk ? fg[kk][g] : f;
-          S += uv[m][g] * f;
-        }
-      } else if (b == fb) {
+    for (int m = 0; m < UB; ++m) {
+      const int j = bt * UB + m;
+      if (j >= KPT) break;
+      const int b = tid + j * NT;
+      float Sc = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) S += __expf(fa[g] - lse_g[g]) * oinfo[G + g];
-      }
-      const bool inr = mm < KPTm && b < NB;
-      key[mm] = (inr && S > 0.f) ? __float_as_uint(S) : 0u;
+      for (int g = 0; g < G; ++g) Sc += uv[m][g] * fr[m][g];
+      const float S = b < NBa ? Sc : (b == fb ? Sfresh : 0.f);
+      const bool inr = b < NB;
+      key[j] = (inr && S > 0.f) ? __float_as_uint(S) : 0u;
       const bool c = inr && b >= 1 && b <= NB - 3;
-      candm |= (uint32_t)c << mm;
+      candm |= (uint64_t)c << j;
       if (scores && inr) scores[b] = S;
-      if (c && count) atomicAdd(&hist[key[mm] >> 21], 1);
+      if (c && count) atomicAdd(&hist[key[j] >> 21], 1);
     }
   }
 
@@ -403,27 +378,27 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
   bool use_list = true;
   uint32_t exact_tau = 0u;
   if (count) {
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) find_bin<2048>(hist, krem, ctl);
-    __syncthreads();
+    lds_barrier();
     tau_bin = (uint32_t)ctl[0];
     krem = ctl[1];
     use_list = ctl[2] <= kListMax;
     if (use_list) {
       // the pivot bin's keys, ordered exactly by (key desc, index asc); the first krem are kept
 #pragma unroll
-      for (int m = 0; m < KPT; ++m) {
-        if (((candm >> m) & 1u) && (key[m] >> 21) == tau_bin) {
+      for (int j = 0; j < KPT; ++j) {
+        if (((candm >> j) & 1u) && (key[j] >> 21) == tau_bin) {
           const int slot = atomicAdd(&ctl[3], 1);
-          lkey[slot] = key[m];
-          lidx[slot] = b0 + m;
+          lkey[slot] = key[j];
+          lidx[slot] = tid + j * NT;
         }
       }
-      __syncthreads();
+      lds_barrier();
       const int n = ctl[3];
-      if (tid < n) {
-        const uint32_t ki = lkey[tid];
-        const int ii = lidx[tid];
+      for (int i = tid; i < n; i += NT) {
+        const uint32_t ki = lkey[i];
+        const int ii = lidx[i];
         int rank = 0;
         for (int j0 = 0; j0 < n; j0 += 8) {
           uint32_t kj[8];
@@ -438,29 +413,28 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
         }
         if (rank < krem) atomicOr(&keep_bits[ii >> 5], 1u << (ii & 31));
       }
-      __syncthreads();
+      lds_barrier();
     } else {
       // long runs of equal keys: pin the exact threshold key with two more radix passes
       uint32_t prefix = tau_bin << 21;
-      __syncthreads();
       for (int i = tid; i < 2048; i += NT) hist[i] = 0;
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
-      for (int m = 0; m < KPT; ++m)
-        if (((candm >> m) & 1u) && (key[m] >> 21) == (prefix >> 21)) atomicAdd(&hist[(key[m] >> 10) & 2047u], 1);
-      __syncthreads();
+      for (int j = 0; j < KPT; ++j)
+        if (((candm >> j) & 1u) && (key[j] >> 21) == (prefix >> 21)) atomicAdd(&hist[(key[j] >> 10) & 2047u], 1);
+      lds_barrier();
       if (wave == 0) find_bin<2048>(hist, krem, ctl);
-      __syncthreads();
+      lds_barrier();
       prefix |= ((uint32_t)ctl[0]) << 10;
       krem = ctl[1];
       for (int i = tid; i < 1024; i += NT) hist[i] = 0;
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
-      for (int m = 0; m < KPT; ++m)
-        if (((candm >> m) & 1u) && (key[m] >> 10) == (prefix >> 10)) atomicAdd(&hist[key[m] & 1023u], 1);
-      __syncthreads();
+      for (int j = 0; j < KPT; ++j)
+        if (((candm >> j) & 1u) && (key[j] >> 10) == (prefix >> 10)) atomicAdd(&hist[key[j] & 1023u], 1);
+      lds_barrier();
       if (wave == 0) find_bin<1024>(hist, krem, ctl);
-      __syncthreads();
+      lds_barrier();
       prefix |= (uint32_t)ctl[0];
       krem = ctl[1];
       exact_tau = prefix;
@@ -468,64 +442,78 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
   }
 
   // ================================================================ compact
-  const bool ties_by_index = count && !use_list;
-  int eq_before = 0;
-  if (ties_by_index) {
-    int eqc = 0;
+  // The query goes to LDS now, into area A (the factors are dead once every
+  // wave is past its keys); the prefix barriers below order it before the
+  // attention reads it.
+  lds_barrier();
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) eqc += (((candm >> m) & 1u) && key[m] == exact_tau) ? 1 : 0;
-    int tot;
-    eq_before = block_exclusive_scan<NW>(eqc, scan, tot);
-    __syncthreads();
+  for (int k = 0; k < NQ4; ++k) {
+    const int i = tid + k * NT;
+    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
   }
-  uint32_t takem = 0u;
+  const bool ties_by_index = count && !use_list;
+  int eq_before[KPT];
+  if (ties_by_index) {
+    uint64_t eqm = 0u;
 #pragma unroll
-  for (int m = 0; m < KPT; ++m) {
-    const int b = b0 + m;
-    const bool inr = m < KPTm && b < NB;
-    const bool c = (candm >> m) & 1u;
-    bool t;
-    if (all) {
-      t = inr;
-    } else {
-      t = inr && (b == 0 || b >= NB - 2);
-      if (krem > 0 || !count) {
-        if (ties_by_index) {
-          const bool eq = c && key[m] == exact_tau;
-          t = t || (c && key[m] > exact_tau) || (eq && eq_before < krem);
-          eq_before += eq ? 1 : 0;
-        } else if (count) {
-          t = t || (c && (key[m] >> 21) > tau_bin) || ((keep_bits[b >> 5] >> (b & 31)) & 1u);
-        }
-      } else if (count) {
-        t = t || (c && (key[m] >> 21) > tau_bin);
+    for (int j = 0; j < KPT; ++j) eqm |= (uint64_t)(((candm >> j) & 1u) && key[j] == exact_tau) << j;
+    int tot;
+    tile_prefix<KPT, NW>(eqm, eq_before, cnt, tot);
+    lds_barrier();
+  }
+  uint64_t takem = 0u;
+  if (all) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) takem |= (uint64_t)(tid + j * NT < NB) << j;
+  } else {
+    uint64_t forced = 0u, above = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int b = tid + j * NT;
+      forced |= (uint64_t)(b < NB && (b == 0 || b >= NB - 2)) << j;
+    }
+    if (ties_by_index) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const bool c = (candm >> j) & 1u;
+        above |= (uint64_t)(c && (key[j] > exact_tau || (key[j] == exact_tau && eq_before[j] < krem))) << j;
+      }
+    } else if (count) {
+      uint32_t kw[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) kw[j] = keep_bits[(tid + j * NT) >> 5];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int b = tid + j * NT;
+        const bool c = (candm >> j) & 1u;
+        above |= (uint64_t)(c && ((key[j] >> 21) > tau_bin || ((kw[j] >> (b & 31)) & 1u))) << j;
       }
     }
-    takem |= (uint32_t)(t && inr) << m;
+    takem = forced | above;
   }
-  int nk;
-  int pos = block_exclusive_scan<NW>(__popc(takem), scan, nk);
+  int before[KPT], nk;
+  tile_prefix<KPT, NW>(takem, before, cnt, nk);
   int32_t* sel = a.sel + (size_t)unit * Kb;
   const int lo = p * KPART;
 #pragma unroll
-  for (int m = 0; m < KPT; ++m) {
-    if ((takem >> m) & 1u) {
-      if (p == 0 && pos < Kb) sel[pos] = b0 + m;
-      if (pos >= lo && pos < lo + KPART) klist[pos - lo] = b0 + m;
-      ++pos;
+  for (int j = 0; j < KPT; ++j) {
+    if ((takem >> j) & 1u) {
+      const int pos = before[j];
+      if (p == 0 && pos < Kb) sel[pos] = tid + j * NT;
+      if (pos >= lo && pos < lo + KPART) klist[pos - lo] = tid + j * NT;
     }
   }
   nk = nk < Kb ? nk : Kb;  // the selection keeps exactly min(Kb, NB); never index past sel
   if (p == 0 && tid == 0) a.n_sel[unit] = nk;
-  __syncthreads();
+  lds_barrier();
 
   // ================================================================ attend
-  // Waves 0..KPART-1: one kept block of this part's slice each (exact terms,
-  // minus its compensation if the scoring pass counted it). Waves KPART..:
-  // this part's share of the scoring pass's chunk records.
+  // Wave w: kept block lo + w of this part's slice (exact terms, minus its
+  // compensation if the scoring pass counted it), then its share of this
+  // part's chunk records of the scoring pass.
   WaveState<D, G> st;
   st.init();
-  if (wave < KPART) {
+  {
     const int e = lo + wave;
     const int b = e < nk ? klist[wave] : -1;
     if (b >= 0) {
@@ -544,14 +532,15 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
           absorb<D, G, false>(st, tile, bm, q_l, lane, a.isd);
       }
     }
-  } else {
+  }
+  {
     const int c0 = (int)((long)p * a.C / P), c1 = (int)((long)(p + 1) * a.C / P);
     const float* crec = a.comp + (size_t)unit * a.C * G * W;
-    for (int cb = c0 + wave - KPART; cb < c1; cb += RPW * RW) {
+    for (int cb = c0 + wave; cb < c1; cb += RPW * NW) {
       float rm[RPW][G], rl[RPW][G], racc[RPW][G][VPL];
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
-        const int c = cb + i * RW;
+        const int c = cb + i * NW;
         const int cc = c < c1 ? c : c1 - 1;
         const float* rp = crec + (size_t)cc * G * W;
 #pragma unroll
@@ -568,7 +557,7 @@ __global__ __launch_bounds__(step_threads(G)) void step_kernel(StepArgs a) {
     }
   }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
-  __syncthreads();
+  lds_barrier();
 
   // ================================================================ merge
   if (P == 1) {
@@ -600,18 +589,22 @@ __global__ __launch_bounds__(kThreads) void step_merge_kernel(StepArgs a) {
 
 hipError_t launch_step(int d, int G, const StepArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
+  const int kptb = step_kptb(a.max_blocks);
   const void* f = nullptr;
   const void* m = nullptr;
-#define CKNV_STEP_CASE(DD, GG)                          \
-  if (d == DD && G == GG) {                             \
-    f = (const void*)step_kernel<DD, GG>;               \
-    m = (const void*)step_merge_kernel<DD, GG>;         \
-  }
+#define CKNV_STEP_K(DD, GG, KK) \
+  if (d == DD && G == GG && kptb == KK) f = (const void*)step_kernel<DD, GG, KK>;
+#define CKNV_STEP_CASE(DD, GG)                                                       \
+  CKNV_STEP_K(DD, GG, 4) CKNV_STEP_K(DD, GG, 8) CKNV_STEP_K(DD, GG, 12)             \
+  CKNV_STEP_K(DD, GG, 16) CKNV_STEP_K(DD, GG, 24) CKNV_STEP_K(DD, GG, 32)           \
+  CKNV_STEP_K(DD, GG, 48)                                                           \
+  if (d == DD && G == GG) m = (const void*)step_merge_kernel<DD, GG>;
   CKNV_STEP_CASE(64, 1) CKNV_STEP_CASE(64, 2) CKNV_STEP_CASE(64, 4) CKNV_STEP_CASE(64, 8)
   CKNV_STEP_CASE(128, 1) CKNV_STEP_CASE(128, 2) CKNV_STEP_CASE(128, 4) CKNV_STEP_CASE(128, 8)
 #undef CKNV_STEP_CASE
+#undef CKNV_STEP_K
   if (!f || !m) return hipErrorInvalidValue;
-  hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(step_threads(G)), args, 0, st);
+  hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(kStepThreads), args, 0, st);
   if (e != hipSuccess || a.P == 1) return e;
   return hipLaunchKernel(m, dim3(U), dim3(kThreads), args, 0, st);
 }

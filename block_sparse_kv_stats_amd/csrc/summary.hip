@@ -22,13 +22,13 @@ namespace cknv {
 template <int D, int NTH>
 __device__ __forceinline__ void group_tree_sums(float* cvar, int nslot, int gs) {
   for (int len = 1; len < gs; len <<= 1) {
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < nslot * D; i += NTH) {
       const int c = i % D;
       if (c % (2 * len) == 0) cvar[i] += cvar[i + len];
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // One workgroup per sequence: thread (h, c) handles key coordinate c of head
@@ -77,11 +77,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       a.vbar[row * D + c] = vm;
       if (c == 0) a.cnt[row] = (float)n;
     }
-    __syncthreads();
+    lds_barrier();
     cvar[threadIdx.x] = kv;
     group_tree_sums<D, kAppendThreads>(cvar, HPI, gs);
     if (act && c % gs == 0) a.dbar[row * a.r + c / gs] = cvar[threadIdx.x] / (float)gs;
-    __syncthreads();
+    lds_barrier();
   }
   if (threadIdx.x == 0 && room) a.seq_len[s] = T + 1;
 }

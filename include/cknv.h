@@ -171,6 +171,24 @@ int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uin
                      int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel, float* out,
                      float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of cknv_decode_step, for callers that schedule them apart
+ * (same arguments; call them in this order on one workspace, with nothing
+ * that changes the cache or seq_len in between):
+ *   cknv_decode_score   the streaming pass over the summaries of the blocks
+ *                       that were closed before the step's token (scores'
+ *                       ingredients and the Mean-compensation sums of every
+ *                       one of them); records seq_len in the workspace;
+ *   cknv_decode_finish  the append and the refresh of the block the token
+ *                       lands in, the normalisers, the selection, and the
+ *                       attention with compensation; advances seq_len. */
+int cknv_decode_score(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                      int32_t budget_tokens, int32_t max_blocks, void* ws, size_t ws_bytes,
+                      void* stream);
+int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                       const uint16_t* new_v, const float* q, int32_t budget_tokens,
+                       int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel,
+                       float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Full (dense) softmax attention over every cached token, the baseline the
  * page compares CompKV with ("Assumptions and limits"). Same q/out/lse
  * layouts as cknv_attend. Uses its own region of the workspace. */

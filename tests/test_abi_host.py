@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = cknv.lib()
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
 
@@ -144,3 +144,18 @@ def test_decode_step_rejects_before_launch():
     assert call(ws_bytes=need - 1) == cknv.ENOSPACE
     assert call(mb=2101) == cknv.ENOSPACE
     assert call(cache=cache_struct("seq_len")) == cknv.EINVAL
+
+
+def test_decode_halves_reject_before_launch():
+    sh = shape()
+    c = cache_struct()
+    L = cknv.lib()
+    _, need = wsize(sh)
+    assert L.cknv_decode_score(ctypes.byref(sh), ctypes.byref(c), None, 512, 2048, FAKE, need,
+                               None) == cknv.EINVAL
+    assert L.cknv_decode_score(ctypes.byref(sh), ctypes.byref(c), FAKE, 512, 2048, FAKE, need - 1,
+                               None) == cknv.ENOSPACE
+    assert L.cknv_decode_finish(ctypes.byref(sh), ctypes.byref(c), None, FAKE, FAKE, 512, 2048,
+                                None, FAKE, FAKE, FAKE, None, FAKE, need, None) == cknv.EINVAL
+    assert L.cknv_decode_finish(ctypes.byref(sh), ctypes.byref(c), FAKE, FAKE, FAKE, 512, 2101,
+                                None, FAKE, FAKE, FAKE, None, FAKE, need, None) == cknv.ENOSPACE

@@ -219,3 +219,29 @@ def test_fused_full_cache_attends_existing_tokens():
     for s, T in ((0, 160), (1, 101)):
         for h in range(w.H):
             gu.check_unit(w, data, s, h, T, 0, data["q"][0], sel, nsel, out, lse, scores, w.budget)
+
+
+def test_fused_halves_equal_one_call():
+    """cknv_decode_score then cknv_decode_finish give the same bits as
+    cknv_decode_step."""
+    w = synth.WORKLOADS["llama8b_32k"].replace(prefill=(7777,))
+    data = synth.gen_layer(w)
+    mb = w.max_blocks_after(0)
+    q = torch.from_numpy(data["q"][0]).cuda()
+    nk, nv = gu.new_token(data, list(data["prefill"]))
+    res = []
+    for halves in (False, True):
+        cache = gu.upload(w, data, max_blocks=mb)
+        dec = fused_dec(cache, mb, w.budget)
+        b = cknv.BoundStep(cache, mb, w.budget, dec.ws, dec.sel, dec.n_sel, dec.out, dec.lse, q,
+                           nk, nv, torch.cuda.current_stream(), scores=dec.scores)
+        if halves:
+            b.decode_score()
+            b.decode_finish()
+        else:
+            b.fused_step()
+        torch.cuda.synchronize()
+        res.append([t.clone() for t in (dec.scores, dec.sel, dec.n_sel, dec.out, dec.lse,
+                                         cache.kbar, cache.seq_len)])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
