@@ -15,8 +15,8 @@ Prints ONE JSON line. `value` = steps/s from HIP-graph replay of whole layer
 sweeps (HIP events around exactly K timed steps). `roofline` is for the
 dominant kernel, the streaming score_kernel (issued alone by
 cknv_decode_score): its algorithmic bytes per launch over its average
-duration, measured with HIP events on the launch stream inside eager full
-steps. `cpu_baseline` times the fp64 oracle's per-step path on a bounded
+duration, measured with HIP events on the launch stream around sweeps of
+back-to-back launches, one per layer. `cpu_baseline` times the fp64 oracle's per-step path on a bounded
 sample on the host. The three-call path (cknv_append, cknv_score_select,
 cknv_attend) and the dense baseline are reported beside it.
 
@@ -192,6 +192,25 @@ def time_eager_steps(torch, timer, stream, bench, n):
     return e0.elapsed_time(e1) / n
 
 
+def time_score_kernel(torch, timer, stream, bench, sweeps):
+    """Average duration (ms) of the streaming score kernel: sweeps of
+    back-to-back cknv_decode_score launches over the R layers, each sweep
+    between two HIP events on the launch stream (a launch only rewrites the
+    workspace, so repeating it leaves the layers unchanged). Returns the mean
+    and the median over sweeps of the per-launch time."""
+    evs = [(timer.event(), timer.event()) for _ in range(sweeps)]
+    with torch.cuda.stream(stream):
+        timer.head_start(5.0 + 0.03 * sweeps * bench.R)
+        for i in range(sweeps):
+            evs[i][0].record(stream)
+            for b in bench.bound:
+                b.decode_score()
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(c) / bench.R for a, c in evs)
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
 def time_kernel_events(torch, timer, stream, bench, n, which):
     """Average and median duration (ms) of one half of the fused step inside
     full eager steps, bracketed by HIP events on the launch stream."""
@@ -280,7 +299,7 @@ def run_workload(torch, timer, wname, args, stream, want_dense=True):
     torch.cuda.synchronize()
     ms_step = time_graph_steps(torch, timer, stream, bench, steps, which="fused_step")
     ms_eager = time_eager_steps(torch, timer, stream, bench, n_e)
-    k_avg, k_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "decode_score")
+    k_avg, k_med = time_score_kernel(torch, timer, stream, bench, max(8, 256 // R))
     f_avg, f_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "decode_finish")
     ms_three = time_graph_steps(torch, timer, stream, bench, max(R, steps // 4), which="step")
     T = bench.seq_len()
@@ -310,6 +329,103 @@ def copy_probe(nbytes: int, reps: int):
     print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}))
 
 
+PROFILE_COMMANDS = {
+    "trace": 'rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace -o trace -- '
+             'python3 bench.py --no-cpu --no-dense',
+    "fetch": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/fetch -o fetch -- '
+             'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --also ""',
+    "write": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/write -o write -- '
+             'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --also ""',
+    "copy_fetch": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/copy_fetch -o cf -- '
+                  'python3 bench.py --copy-probe 268435456',
+    "copy_write": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/copy_write -o cw -- '
+                  'python3 bench.py --copy-probe 268435456',
+    "summary": 'python3 bench.py --summarize-profiles $OUT',
+}
+COPY_PROBE_BYTES = 268435456
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _counter_per_dispatch(directory, counter, name_part, grid=None):
+    """Per-dispatch values of one counter for kernels whose name contains name_part."""
+    vals = []
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            if grid is None or int(r["Grid_Size"]) == grid:
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_profiles(out_dir):
+    """Write profiles/ summaries from the rocprofv3 runs listed in
+    PROFILE_COMMANDS (their CSV output under out_dir)."""
+    import statistics
+    from block_sparse_kv_stats_amd import synth
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    # ---- kernel trace: per (kernel, grid) duration statistics
+    stats = {}
+    for r in _csv_rows(os.path.join(out_dir, "trace"), "kernel_trace.csv"):
+        name = r["Kernel_Name"]
+        if "cknv" not in name:
+            continue
+        key = (name.split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]))
+        stats.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# Kernel durations, bench.py default workloads (Llama-3.1-8B 32K, Qwen3-8B 128K)", "",
+             "Command (from the repository root, OUT = an output directory):", "",
+             "    " + PROFILE_COMMANDS["trace"], "    " + PROFILE_COMMANDS["summary"], "",
+             "rocprofv3 kernel trace of every dispatch of the run (graph replays included),",
+             "grouped by kernel and grid size (threads). Durations in microseconds.", "",
+             "| kernel | grid threads | dispatches | avg us | median us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid), d in sorted(stats.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        lines.append(f"| {name} | {grid} | {len(d)} | {statistics.mean(d):.2f} | "
+                     f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
+    with open(os.path.join(prof, "kernels_llama8b_32k_qwen8b_128k_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # ---- HBM traffic of score_kernel at 32K, calibrated on a plain copy
+    w = synth.WORKLOADS["llama8b_32k"]
+    fetch = _counter_per_dispatch(os.path.join(out_dir, "fetch"), "FETCH_SIZE", "score_kernel")
+    write = _counter_per_dispatch(os.path.join(out_dir, "write"), "WRITE_SIZE", "score_kernel")
+    cf = _counter_per_dispatch(os.path.join(out_dir, "copy_fetch"), "FETCH_SIZE", "copy")
+    cw = _counter_per_dispatch(os.path.join(out_dir, "copy_write"), "WRITE_SIZE", "copy")
+    if not (fetch and write and cf and cw):
+        print("missing counter data", file=sys.stderr)
+        return
+    kib = COPY_PROBE_BYTES / 1024.0
+    f_cal = kib / statistics.median(cf)   # bytes per counted KiB, read side
+    w_cal = kib / statistics.median(cw)   # ... write side
+    fb = statistics.median(fetch) * 1024.0 * f_cal
+    wb = statistics.median(write) * 1024.0 * w_cal
+    T = w.prefill[0] + 1
+    sb, _ = step_bytes(w, T)
+    rec = {"kernel": "score_kernel", "workload": w.name,
+           "source_hash": kernel_source_hash(SCORE_SOURCES),
+           "fetch_KiB_per_dispatch_median": statistics.median(fetch),
+           "write_KiB_per_dispatch_median": statistics.median(write),
+           "dispatches": [len(fetch), len(write)],
+           "copy_probe_bytes": COPY_PROBE_BYTES,
+           "copy_fetch_KiB": statistics.median(cf), "copy_write_KiB": statistics.median(cw),
+           "calibration_fetch": round(f_cal, 4), "calibration_write": round(w_cal, 4),
+           "hbm_read_bytes_per_launch": int(fb), "hbm_write_bytes_per_launch": int(wb),
+           "hbm_bytes_per_launch": int(fb + wb),
+           "algorithmic_bytes_per_launch_first_step": sb,
+           "commands": [PROFILE_COMMANDS[k] for k in ("fetch", "write", "copy_fetch",
+                                                      "copy_write", "summary")]}
+    with open(os.path.join(prof, "score_kernel_llama8b_32k_pmc.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,7 +438,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="run only a device copy of this many bytes")
+    ap.add_argument("--summarize-profiles", default="",
+                    help="write profiles/ summaries from rocprofv3 output in this directory")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -374,7 +495,8 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": main_res["score_bytes"],
                      "avg_launch_us": round(main_res["score_ms"] * 1e3, 3),
-                     "median_launch_us": round(main_res["score_ms_median"] * 1e3, 3)},
+                     "median_sweep_us_per_launch": round(main_res["score_ms_median"] * 1e3, 3),
+                     "timing": "HIP events around back-to-back launches (one per layer)"},
         "finish_kernels": {"kernels": "step_kernel + step_merge_kernel (cknv_decode_finish)",
                            "avg_us": round(main_res["finish_ms"] * 1e3, 3),
                            "algorithmic_bytes": main_res["attend_bytes"]},

@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include "cknv_internal.h"
+#include "step_config.h"
 
 namespace cknv {
 

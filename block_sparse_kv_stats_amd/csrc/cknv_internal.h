@@ -23,17 +23,6 @@ constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
 constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
 constexpr int kDenseMaxWGs = 64;          // dense attention: workgroups per unit (at most)
-// Fused step kernel: one wave per SIMD (256 threads); thread t owns blocks
-// t + 256*j for j < KPTB, KPTB the smallest bucket that covers max_blocks;
-// each wave attends one kept block, so a workgroup attends kStepKeptPerPart
-// of them.
-constexpr int kStepThreads = 256;
-constexpr int kStepKeptPerPart = kStepThreads / 64;
-__host__ __device__ constexpr int step_kptb(int max_blocks) {
-  return max_blocks <= 4 * kStepThreads ? 4 : max_blocks <= 8 * kStepThreads ? 8
-       : max_blocks <= 12 * kStepThreads ? 12 : max_blocks <= 16 * kStepThreads ? 16
-       : max_blocks <= 24 * kStepThreads ? 24 : max_blocks <= 32 * kStepThreads ? 32 : 48;
-}
 constexpr int kSelThreads = 1024;       // selection: one workgroup per unit
 constexpr int kSelKeysPerThread = 12;   // blocks per selection thread: max_blocks <= 12288
 

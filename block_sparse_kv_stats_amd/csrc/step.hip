@@ -41,6 +41,7 @@
 //   merge      the waves' records -> out, lse (P == 1) or a part record.
 #include "attend_core.h"
 #include "select_core.h"
+#include "step_config.h"
 
 namespace cknv {
 
@@ -596,7 +597,7 @@ hipError_t launch_step(int d, int G, const StepArgs& a, int U, hipStream_t st) {
   if (d == DD && G == GG && kptb == KK) f = (const void*)step_kernel<DD, GG, KK>;
 #define CKNV_STEP_CASE(DD, GG)                                                       \
   CKNV_STEP_K(DD, GG, 4) CKNV_STEP_K(DD, GG, 8) CKNV_STEP_K(DD, GG, 12)             \
-  CKNV_STEP_K(DD, GG, 16) CKNV_STEP_K(DD, GG, 24) CKNV_STEP_K(DD, GG, 32)           \
+  CKNV_STEP_K(DD, GG, 16) CKNV_STEP_K(DD, GG, 24) CKNV_STEP_K(DD, GG, 34)           \
   CKNV_STEP_K(DD, GG, 48)                                                           \
   if (d == DD && G == GG) m = (const void*)step_merge_kernel<DD, GG>;
   CKNV_STEP_CASE(64, 1) CKNV_STEP_CASE(64, 2) CKNV_STEP_CASE(64, 4) CKNV_STEP_CASE(64, 8)
