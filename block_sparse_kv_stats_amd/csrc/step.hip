@@ -22,8 +22,8 @@
 // any of them: this kernel computes its summary from its tokens, folds its
 // a into the normalisers, and never removes compensation for it.
 //
-// Phases of a workgroup (NT threads; thread t owns blocks t*KPT.. of the
-// unit, in order):
+// Phases of a workgroup (NT threads; thread t owns blocks t + NT*j of the
+// unit):
 //   loads      score-group partials, the thread's u terms, the query, and
 //              (last wave) the fresh block's tokens;
 //   fresh      last wave: summary of the fresh block, its a and σ̂²; part 0
@@ -36,8 +36,9 @@
 //              keys, pinned by two more radix passes, ties by index);
 //   compact    kept blocks in ascending order -> sel, and this part's slice;
 //   attend     the first KPART waves: one kept block of this part's slice
-//              each (exact terms minus its compensation); the others: this
-//              part's share of the scoring pass's chunk records;
+//              each (exact terms minus its compensation); every wave: its
+//              share of this part's chunk records of the scoring pass (the
+//              first one loaded with the other inputs);
 //   merge      the waves' records -> out, lse (P == 1) or a part record.
 #include "attend_core.h"
 #include "select_core.h"
@@ -59,7 +60,7 @@ struct StepCfg {
   static constexpr int NBATCH = (KPT + UB - 1) / UB;
   static constexpr int KPART = kStepKeptPerPart;                   // kept blocks per workgroup
   static constexpr int RPW = 2;                                    // records per wave per batch
-  static_assert(KPART == NW, "one kept block per wave");
+  static_assert(KPART <= NW, "one kept block per attending wave");
 };
 
 // out[g][c] = sum_i rec_i[g][c] e^{m_i - M} / L (and lse = M + ln L) over n
@@ -170,6 +171,24 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   for (int k = 0; k < NQ4; ++k) {
     const int i = tid + k * NT;
     q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
+  }
+  // This wave's first chunk record of the scoring pass (this part's share),
+  // folded in the attend phase; it does not depend on the selection.
+  const int c0 = (int)((long)p * a.C / P), c1 = (int)((long)(p + 1) * a.C / P);
+  const float* crec = a.comp + (size_t)unit * a.C * G * W;
+  float pm[G], pl[G], pacc[G][VPL];
+  {
+    const int c = c0 + wave;
+    const int cc = c < c1 ? c : (c1 > 0 ? c1 - 1 : 0);
+    const float* rp = crec + (size_t)cc * G * W;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float2 ml = *reinterpret_cast<const float2*>(rp + g * W);
+      pm[g] = c < c1 ? ml.x : -INFINITY;
+      pl[g] = ml.y;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) pacc[g][e] = rp[g * W + 4 + lane * VPL + e];
+    }
   }
   // Fresh-block tokens (wave OW): np = T0 % 16 cached tokens plus the new one.
   const int fblk = T0 / kBlock;
@@ -514,7 +533,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   // part's chunk records of the scoring pass.
   WaveState<D, G> st;
   st.init();
-  {
+  fold_record<D, G>(st, pm, pl, pacc);
+  if (wave < KPART) {
     const int e = lo + wave;
     const int b = e < nk ? klist[wave] : -1;
     if (b >= 0) {
@@ -535,9 +555,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     }
   }
   {
-    const int c0 = (int)((long)p * a.C / P), c1 = (int)((long)(p + 1) * a.C / P);
-    const float* crec = a.comp + (size_t)unit * a.C * G * W;
-    for (int cb = c0 + wave; cb < c1; cb += RPW * NW) {
+    for (int cb = c0 + wave + NW; cb < c1; cb += RPW * NW) {
       float rm[RPW][G], rl[RPW][G], racc[RPW][G][VPL];
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
@@ -596,9 +614,9 @@ hipError_t launch_step(int d, int G, const StepArgs& a, int U, hipStream_t st) {
 #define CKNV_STEP_K(DD, GG, KK) \
   if (d == DD && G == GG && kptb == KK) f = (const void*)step_kernel<DD, GG, KK>;
 #define CKNV_STEP_CASE(DD, GG)                                                       \
-  CKNV_STEP_K(DD, GG, 4) CKNV_STEP_K(DD, GG, 8) CKNV_STEP_K(DD, GG, 12)             \
-  CKNV_STEP_K(DD, GG, 16) CKNV_STEP_K(DD, GG, 24) CKNV_STEP_K(DD, GG, 34)           \
-  CKNV_STEP_K(DD, GG, 48)                                                           \
+  CKNV_STEP_K(DD, GG, 2) CKNV_STEP_K(DD, GG, 4) CKNV_STEP_K(DD, GG, 6)              \
+  CKNV_STEP_K(DD, GG, 8) CKNV_STEP_K(DD, GG, 12) CKNV_STEP_K(DD, GG, 17)            \
+  CKNV_STEP_K(DD, GG, 24)                                                           \
   if (d == DD && G == GG) m = (const void*)step_merge_kernel<DD, GG>;
   CKNV_STEP_CASE(64, 1) CKNV_STEP_CASE(64, 2) CKNV_STEP_CASE(64, 4) CKNV_STEP_CASE(64, 8)
   CKNV_STEP_CASE(128, 1) CKNV_STEP_CASE(128, 2) CKNV_STEP_CASE(128, 4) CKNV_STEP_CASE(128, 8)
