@@ -588,19 +588,67 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
 }
 
-// P > 1: one workgroup per unit merges the parts; the unit's first head
-// advances seq_len.
+// P > 1: one workgroup per unit merges the unit's P part records into out
+// and lse, and the unit's first head advances seq_len. Thread t owns output
+// columns t + 256*k; the records are read in batches of 8, every load of a
+// batch issued before the first use.
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void step_merge_kernel(StepArgs a) {
   constexpr int W = rec_words(D);
-  constexpr int CAP = stage_cap<G>();
-  __shared__ __align__(16) float recs[CAP * G * W];
-  __shared__ float scl[CAP * G + 3 * G];
-  const int unit = blockIdx.x;
+  constexpr int COLS = (G * D + kThreads - 1) / kThreads;  // output columns per thread
+  constexpr int PB = 8;                                    // records per batch
+  const int unit = blockIdx.x, tid = threadIdx.x;
   const int s = unit / a.H, h = unit - s * a.H;
-  finish_unit<D, G>(a.part + (size_t)unit * a.P * G * W, a.P, a.out + (size_t)unit * G * D,
-                    a.lse ? a.lse + (size_t)unit * G : nullptr, recs, CAP, scl);
-  if (h == 0 && threadIdx.x == 0) {
+  const int P = a.P;
+  const float* parts = a.part + (size_t)unit * P * G * W;
+  float M[COLS], L[COLS], A[COLS];
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) { M[k] = -INFINITY; L[k] = 0.f; A[k] = 0.f; }
+  for (int p0 = 0; p0 < P; p0 += PB) {
+    float m[PB][COLS], l[PB][COLS], x[PB][COLS];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int pi = p0 + i < P ? p0 + i : P - 1;
+#pragma unroll
+      for (int k = 0; k < COLS; ++k) {
+        int col = tid + k * kThreads;
+        col = col < G * D ? col : G * D - 1;
+        const int g = col / D, c = col - g * D;
+        const float* r = parts + ((size_t)pi * G + g) * W;
+        m[i][k] = p0 + i < P ? r[0] : -INFINITY;
+        l[i][k] = r[1];
+        x[i][k] = r[4 + c];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < COLS; ++k) {
+      float MM = M[k];
+#pragma unroll
+      for (int i = 0; i < PB; ++i) MM = fmaxf(MM, m[i][k]);
+      const float so = rescale(M[k], MM);
+      float LL = L[k] * so, AA = A[k] * so;
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const float f = rescale(m[i][k], MM);
+        LL += l[i][k] * f;
+        AA += x[i][k] * f;
+      }
+      M[k] = MM;
+      L[k] = LL;
+      A[k] = AA;
+    }
+  }
+  float* out = a.out + (size_t)unit * G * D;
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) {
+    const int col = tid + k * kThreads;
+    if (col < G * D) {
+      const bool ok = L[k] > 0.f;
+      out[col] = ok ? A[k] / L[k] : 0.f;
+      if (col % D == 0 && a.lse) a.lse[(size_t)unit * G + col / D] = ok ? M[k] + __logf(L[k]) : -INFINITY;
+    }
+  }
+  if (h == 0 && tid == 0) {
     const int T0 = a.t0[s];
     if (T0 < (long)a.cap_blocks * kBlock) a.seq_len[s] = T0 + 1;
   }
