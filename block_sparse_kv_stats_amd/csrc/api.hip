@@ -38,9 +38,11 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   Plan q{};
   q.U = sh->S * sh->H;
   q.NBmax = max_blocks;
-  q.NG = (max_blocks + score_bpw(G) - 1) / score_bpw(G);
+  q.rows = score_rows(G, max_blocks, q.U);
+  q.bpw = 4 * q.rows;
+  q.NG = (max_blocks + q.bpw - 1) / q.bpw;
   q.Kb = budget_tokens / kBlock;
-  q.C = (max_blocks + score_bpwg(G) - 1) / score_bpwg(G);
+  q.C = (max_blocks + 4 * q.bpw - 1) / (4 * q.bpw);
   const int per_wg = kWaves;  // kept blocks per attend workgroup (one per wave)
   q.P = (q.Kb + per_wg - 1) / per_wg;
   const int pc = (q.C + kMaxChunksPerAttendWG - 1) / kMaxChunksPerAttendWG;
@@ -140,7 +142,7 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   a.u = reinterpret_cast<float*>(w + p.off_u);
   a.comp = reinterpret_cast<float*>(w + p.off_comp);
   a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
-  a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C;
+  a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C; a.rows = p.rows;
   a.xcd = (p.U % 8) == 0;
   a.isd = 1.0f / sqrtf((float)shape->d);
   hipError_t e = launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream);
@@ -149,7 +151,7 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   sa.seq_len = cache->seq_len; sa.grp = a.grp; sa.u = a.u;
   sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel;
   sa.H = shape->H; sa.cap_blocks = shape->cap_blocks; sa.max_blocks = max_blocks; sa.NG = p.NG;
-  sa.Kb = p.Kb;
+  sa.Kb = p.Kb; sa.bpw_shift = p.bpw == 8 ? 3 : 4;
   return hip_status(launch_select(shape->G, sa, p.U, (hipStream_t)stream));
 }
 
@@ -162,7 +164,7 @@ static int decode_score_impl(const Plan& p, const cknv_shape* shape, const cknv_
   a.u = reinterpret_cast<float*>(w + p.off_u);
   a.comp = reinterpret_cast<float*>(w + p.off_comp);
   a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
-  a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C;
+  a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C; a.rows = p.rows;
   a.xcd = (p.U % 8) == 0;
   a.closed_only = 1;
   a.t0_out = reinterpret_cast<int32_t*>(w + p.off_t0);
@@ -186,6 +188,7 @@ static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv
   sa.part = reinterpret_cast<float*>(w + p.off_fpart);
   sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
   sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf;
+  sa.bpw_shift = p.bpw == 8 ? 3 : 4;
   sa.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_step(shape->d, shape->G, sa, p.U, (hipStream_t)stream));
 }

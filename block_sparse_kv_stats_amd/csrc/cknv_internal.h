@@ -14,11 +14,13 @@ constexpr int kBlock = 16;          // tokens per block (CompKV page, "Assumptio
 constexpr int kThreads = 256;       // threads per workgroup of the score and attend kernels
 constexpr int kWaves = kThreads / 64;
 // Score-kernel geometry: a wave covers 4 blocks per row (16 lanes each) and
-// score_rows(G) rows, so that rows x G = 16 (clamped to 2..4 rows) and the
-// transposed reduction leaves one (block, query head) per lane.
-__host__ __device__ constexpr int score_rows(int G) { return G >= 8 ? 2 : 4; }
-__host__ __device__ constexpr int score_bpw(int G) { return 4 * score_rows(G); }    // blocks per wave
-__host__ __device__ constexpr int score_bpwg(int G) { return 4 * score_bpw(G); }   // blocks per workgroup
+// 2 or 4 rows (a score group of 8 or 16 blocks; 2 rows at G = 8). Fewer rows
+// give more waves, which pays while the grid is small; the workspace plan
+// picks the rows. The selection works with either group size.
+constexpr int kScoreMinGroup = 8;  // blocks of the smaller score group
+__host__ __device__ constexpr int score_rows(int G, int max_blocks, int units) {
+  return G >= 8 ? 2 : G <= 2 ? 4 : ((long)units * ((max_blocks + 7) / 8) <= 4096 ? 2 : 4);
+}
 constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
 constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
@@ -35,9 +37,11 @@ __host__ __device__ constexpr int rec_words(int d) { return d + 4; }
 struct Plan {
   int U;            // units = S*H
   int NBmax;        // max_blocks
-  int NG;           // score groups per unit (one per score wave) = ceil(NBmax/score_bpw(G))
+  int rows;         // score-kernel rows per wave (2 or 4)
+  int bpw;          // blocks per score group = 4*rows
+  int NG;           // score groups per unit (one per score wave) = ceil(NBmax/bpw)
   int Kb;           // block slots of the budget
-  int C;            // score workgroups per unit = ceil(NBmax/score_bpwg(G))
+  int C;            // score workgroups per unit = ceil(NBmax/(4*bpw))
   int P;            // attend workgroups per unit
   int Pf;           // fused-step workgroups per unit = ceil(Kb/kStepKeptPerPart)
   int Pd;           // dense-attend workgroups per unit
@@ -62,7 +66,7 @@ struct ScoreArgs {
   const float* kbar; const float* dbar; const float* cnt; const float* vbar;
   const int32_t* seq_len; const float* q;
   float* grp; float* u; float* comp;
-  int S, H, r, cap_blocks, max_blocks, NG, C, xcd;
+  int S, H, r, cap_blocks, max_blocks, NG, C, xcd, rows;
   int closed_only;  // 1: score only blocks closed before this step's token (fused step)
   int32_t* t0_out;  // fused step: seq_len before the step, per sequence (or null)
   float isd;  // 1/sqrt(d)
@@ -71,7 +75,7 @@ struct ScoreArgs {
 struct SelectArgs {
   const int32_t* seq_len; const float* grp; const float* u;
   float* scores; int32_t* sel; int32_t* n_sel;
-  int H, cap_blocks, max_blocks, NG, Kb;
+  int H, cap_blocks, max_blocks, NG, Kb, bpw_shift;
 };
 
 struct AttendArgs {
@@ -88,7 +92,7 @@ struct StepArgs {
   const uint16_t* new_k; const uint16_t* new_v; const float* q;
   const float* grp; const float* u; const float* comp;
   float* scores; int32_t* sel; int32_t* n_sel; float* out; float* lse; float* part;
-  int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P;
+  int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P, bpw_shift;
   float isd;
 };
 

@@ -33,6 +33,13 @@ namespace {
 // How a lane's 4 coordinates 4c..4c+3 map to D̄ entries (group size gs = d/r).
 enum DbarMode { kDbarOne = 0, kDbarPair = 1, kDbarQuad = 2 };  // gs >= 4, gs == 2, gs == 1
 
+// A load of data read once per step (no reuse in the caches).
+__device__ __forceinline__ float4 stream_load4(const float4* p) {
+  typedef float v4 __attribute__((ext_vector_type(4)));
+  const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+
 __device__ __forceinline__ float dot4(const float4 a, const float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
@@ -134,13 +141,13 @@ __device__ __forceinline__ float seg_sum(float x) {
 template <int L>
 __device__ __forceinline__ float row_bcast(float x) { return dpp<kDppBcast0 + L>(x); }
 
-template <int D, int G, int DM>
+template <int D, int G, int DM, int ROWS>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   constexpr int KC = D / 64;              // float4 chunks per lane per block (16 lanes per block)
   constexpr int E = 4 * KC;               // coordinates per lane
-  constexpr int ROWS = score_rows(G);     // blocks per lane: base + 4*row + (lane >> 4)
+  // ROWS: blocks per lane, base + 4*row + (lane >> 4)
   constexpr int NP = ROWS * G;            // (row, head) pairs of a 16-lane row
-  constexpr int BPW = score_bpw(G), BPWG = score_bpwg(G);
+  constexpr int BPW = 4 * ROWS, BPWG = kWaves * BPW;
   constexpr int W = rec_words(D);
   constexpr int NA = G * E;               // compensation sums per lane before the cross-row step
   __shared__ __align__(16) float cacc[kWaves * G * D];  // per-wave compensation sums
@@ -183,8 +190,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const int c = j + 16 * i;  // float4 chunk: coordinates 4c..4c+3
-      kv[rw][i] = kbar4[row * (D / 4) + c];
-      vv[rw][i] = vbar4[row * (D / 4) + c];
+      kv[rw][i] = stream_load4(kbar4 + row * (D / 4) + c);
+      vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + c);
       dt.load(a.dbar, row, c, r, D, rw, i);
     }
   }
@@ -324,15 +331,17 @@ hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st)
   const int gs = d / a.r;
   const int dm = gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
   const void* f = nullptr;
-#define CKNV_SCORE_CASE(DD, GG)                                         \
-  if (d == DD && G == GG) {                                             \
-    f = dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne>    \
-      : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair>  \
-                        : (const void*)score_kernel<DD, GG, kDbarQuad>; \
+#define CKNV_SCORE_R(DD, GG, RR)                                                  \
+  if (d == DD && G == GG && a.rows == RR) {                                       \
+    f = dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR>          \
+      : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair, RR>        \
+                        : (const void*)score_kernel<DD, GG, kDbarQuad, RR>;       \
   }
-  CKNV_SCORE_CASE(64, 1) CKNV_SCORE_CASE(64, 2) CKNV_SCORE_CASE(64, 4) CKNV_SCORE_CASE(64, 8)
-  CKNV_SCORE_CASE(128, 1) CKNV_SCORE_CASE(128, 2) CKNV_SCORE_CASE(128, 4) CKNV_SCORE_CASE(128, 8)
+#define CKNV_SCORE_CASE(DD) \
+  CKNV_SCORE_R(DD, 1, 4) CKNV_SCORE_R(DD, 2, 4) CKNV_SCORE_R(DD, 4, 2) CKNV_SCORE_R(DD, 4, 4) CKNV_SCORE_R(DD, 8, 2)
+  CKNV_SCORE_CASE(64) CKNV_SCORE_CASE(128)
 #undef CKNV_SCORE_CASE
+#undef CKNV_SCORE_R
   if (!f) return hipErrorInvalidValue;
   return hipLaunchKernel(f, dim3(U * a.C), dim3(kThreads), args, 0, st);
 }

@@ -37,8 +37,7 @@ template <int G>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   constexpr int KPT = kSelKeysPerThread;
   constexpr int NW = KPT * kSelThreads / 32;  // words of the kept-block bitmap
-  constexpr int BPW = score_bpw(G);              // blocks per score group
-  constexpr int NGmax = kSelThreads * kSelKeysPerThread / BPW;
+  constexpr int NGmax = kSelThreads * kSelKeysPerThread / kScoreMinGroup;  // score groups, at most
   __shared__ float f[NGmax * G];                 // exp(group max - LSE_g)
   __shared__ float red[kSelWaves * G * 2];
   __shared__ __align__(16) int hist[2048];
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     if (tid == 0) a.n_sel[unit] = 0;
     return;
   }
-  const int NGu = (NB + BPW - 1) / BPW;
+  const int NGu = (NB + (1 << a.bpw_shift) - 1) >> a.bpw_shift;
   const int nper = (NB + kSelThreads - 1) / kSelThreads;
   const int Kb = a.Kb;
   const bool all = NB <= Kb;
@@ -148,7 +147,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       const int bc = b < NB ? b : NB - 1;
       float S = 0.f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) S += ub[m][g] * f[(bc / BPW) * G + g];
+      for (int g = 0; g < G; ++g) S += ub[m][g] * f[(bc >> a.bpw_shift) * G + g];
       key[m0 + m] = (b < NB && S > 0.f) ? __float_as_uint(S) : 0u;
       const bool c = b >= 1 && b <= NB - 3;
       candm |= (uint32_t)c << (m0 + m);

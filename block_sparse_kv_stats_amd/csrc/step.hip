@@ -53,8 +53,7 @@ struct StepCfg {
   static constexpr int NT = kStepThreads;
   static constexpr int NW = NT / 64;
   static constexpr int KPT = KPTB;                                 // blocks per thread
-  static constexpr int BPW = score_bpw(G);                         // blocks per score group
-  static constexpr int NGMAX = (NT * KPT + BPW - 1) / BPW;         // score groups covered
+  static constexpr int NGMAX = (NT * KPT + kScoreMinGroup - 1) / kScoreMinGroup;  // score groups, at most
   static constexpr int GPT = (NGMAX + NT - 1) / NT;                // score groups per thread
   static constexpr int UB = KPT < 128 / G ? KPT : 128 / G;         // blocks per u load batch
   static constexpr int NBATCH = (KPT + UB - 1) / UB;
@@ -109,7 +108,7 @@ __device__ __forceinline__ void fold_record(WaveState<D, G>& st, const float (&r
 template <int D, int G, int KPTB>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   using C = StepCfg<G, KPTB>;
-  constexpr int NT = C::NT, NW = C::NW, KPT = C::KPT, UB = C::UB, BPW = C::BPW;
+  constexpr int NT = C::NT, NW = C::NW, KPT = C::KPT, UB = C::UB;
   constexpr int GPT = C::GPT, NGMAX = C::NGMAX, KPART = C::KPART, RPW = C::RPW;
   constexpr int W = rec_words(D), VPL = D / 64;
   constexpr int OW = NW - 1;  // the wave that refreshes the fresh block
@@ -221,7 +220,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   int NBa = T0 / kBlock;
   NBa = NBa < MB ? NBa : MB;
   const int fb = (room && fblk < MB) ? fblk : -1;  // fresh block (always the last block)
-  const int NGa = (NBa + BPW - 1) / BPW;
+  const int gsh = a.bpw_shift;  // score group = 1 << gsh blocks
+  const int NGa = (NBa + (1 << gsh) - 1) >> gsh;
   const bool all = NB <= Kb;
   int krem = Kb - 3;
   const bool count = !all && krem > 0;
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int m = 0; m < UB; ++m) {
       const int b = tid + (bt * UB + m) * NT;
-      int gi = b / BPW;
+      int gi = b >> gsh;
       gi = gi < NGa ? gi : (NGa > 0 ? NGa - 1 : 0);
 #pragma unroll
       for (int g = 0; g < G; ++g) fr[m][g] = fgrp[gi * G + g];
