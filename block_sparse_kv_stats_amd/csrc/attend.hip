@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
     Tile<D> t0, t1;
     const bool u1 = b + 1 < hi;
     t0.load(kc, vc, (long)b * kBlock, T, lane);
-    t1.load(kc, vc, (long)(b + 1) * kBlock, u1 ? (long)T : 0, lane);
+    t1.load(kc, vc, (long)(u1 ? b + 1 : b) * kBlock, u1 ? (long)T : 0, lane);  // a valid block even when unused
     absorb<D, G, false>(st, t0, none, q_l, lane, a.isd);
     if (u1) absorb<D, G, false>(st, t1, none, q_l, lane, a.isd);
   }

@@ -40,26 +40,26 @@ struct Tile {
     const int tq = lane >> 4, cc = lane & 15;
     const long left = T - tok0;
     nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+    const int last = nt > 0 ? nt - 1 : 0;  // loads read token min(t, last), values masked after
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int t = 4 * m + tq;
       tv[m] = t < nt;
-      const size_t off = (size_t)(tok0 + t) * D + cc * EPL;
+      const uint16_t* src = kc + (size_t)(tok0 + (t < last ? t : last)) * D + cc * EPL;
       if (EPL == 8) {
-        const uint4 kk = tv[m] ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
-        k[m][0] = kk.x; k[m][1] = kk.y; k[m][2] = kk.z; k[m][3] = kk.w;
+        const uint4 kk = stream_load_u4(src);
+        k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
+        k[m][2] = tv[m] ? kk.z : 0u; k[m][3] = tv[m] ? kk.w : 0u;
       } else {
-        const uint2 kk = tv[m] ? *reinterpret_cast<const uint2*>(kc + off) : make_uint2(0, 0);
-        k[m][0] = kk.x; k[m][1] = kk.y;
+        const uint2 kk = stream_load_u2(src);
+        k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
       }
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const size_t off = (size_t)(tok0 + t) * D + lane * VPL;
-      if (VPL == 2)
-        v[t] = t < nt ? *reinterpret_cast<const uint32_t*>(vc + off) : 0u;
-      else
-        v[t] = t < nt ? (uint32_t)vc[off] : 0u;
+      const uint16_t* src = vc + (size_t)(tok0 + (t < last ? t : last)) * D + lane * VPL;
+      const uint32_t w = VPL == 2 ? stream_load_u1(src) : stream_load_h(src);
+      v[t] = t < nt ? w : 0u;
     }
   }
   // The block a decode step appends to: np (0..15) tokens from the cache at
@@ -76,18 +76,18 @@ struct Tile {
       tv[m] = t < nt;
       const uint16_t* src = (t < np ? kc + (size_t)(tok0 + t) * D : nk) + cc * EPL;
       if (EPL == 8) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(src);
+        const uint4 kk = stream_load_u4(src);
         k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
         k[m][2] = tv[m] ? kk.z : 0u; k[m][3] = tv[m] ? kk.w : 0u;
       } else {
-        const uint2 kk = *reinterpret_cast<const uint2*>(src);
+        const uint2 kk = stream_load_u2(src);
         k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
       }
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const uint16_t* src = (t < np ? vc + (size_t)(tok0 + t) * D : nv) + lane * VPL;
-      const uint32_t w = VPL == 2 ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*src;
+      const uint32_t w = VPL == 2 ? stream_load_u1(src) : stream_load_h(src);
       v[t] = t < nt ? w : 0u;
     }
   }

@@ -178,6 +178,30 @@ __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(l, h);
 }
 
+// Loads of data read once per step: non-temporal, so they do not displace
+// reused lines from the caches.
+__device__ __forceinline__ float4 stream_load4(const float4* p) {
+  typedef float v4 __attribute__((ext_vector_type(4)));
+  const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint4 stream_load_u4(const uint16_t* p) {
+  typedef unsigned v4 __attribute__((ext_vector_type(4)));
+  const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ uint2 stream_load_u2(const uint16_t* p) {
+  typedef unsigned v2 __attribute__((ext_vector_type(2)));
+  const v2 x = __builtin_nontemporal_load(reinterpret_cast<const v2*>(p));
+  return make_uint2(x[0], x[1]);
+}
+__device__ __forceinline__ uint32_t stream_load_u1(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint32_t stream_load_h(const uint16_t* p) {
+  return (uint32_t)__builtin_nontemporal_load(p);
+}
+
 // Workgroup barrier for data exchanged through LDS only. __syncthreads()
 // also orders global memory, so it first waits for every outstanding global
 // load and store of the wave; kernels here never read in one wave what

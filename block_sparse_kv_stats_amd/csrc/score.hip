@@ -33,13 +33,6 @@ namespace {
 // How a lane's 4 coordinates 4c..4c+3 map to D̄ entries (group size gs = d/r).
 enum DbarMode { kDbarOne = 0, kDbarPair = 1, kDbarQuad = 2 };  // gs >= 4, gs == 2, gs == 1
 
-// A load of data read once per step (no reuse in the caches).
-__device__ __forceinline__ float4 stream_load4(const float4* p) {
-  typedef float v4 __attribute__((ext_vector_type(4)));
-  const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
-  return make_float4(x[0], x[1], x[2], x[3]);
-}
-
 __device__ __forceinline__ float dot4(const float4 a, const float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
