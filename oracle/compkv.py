@@ -213,20 +213,25 @@ def dense_attention(q, k, v, T: int):
 
 
 def decode_step(q, k_bits, v_bits, T: int, r: int, budget: int, block: int = BLOCK,
-                sel=None) -> dict:
+                sel=None, compensate: bool = True, mass_order: int = 2,
+                variance_factor: bool = True) -> dict:
     """One CompKV decode step of one unit, from the cache contents (summaries rebuilt).
 
     q: fp32/fp64 [G][d]; k_bits, v_bits: bf16 bit patterns [>=T][d].
     ``sel`` overrides the selection (used to evaluate the output on another,
-    equally valid, selection). Returns summaries, scores, sel, o, lse.
+    equally valid, selection). ``compensate``, ``mass_order`` and
+    ``variance_factor`` select the page's ablation variants ("Assumptions and
+    limits": Mean compensation removed, first-order mass estimate, score
+    without the outer variance factor); the defaults are CompKV itself.
+    Returns summaries, scores, sel, o, lse.
     """
     k = decode_bf16(np.asarray(k_bits)[:T])
     v = decode_bf16(np.asarray(v_bits)[:T])
     cnt, kbar, dbar, vbar = block_summaries(k, v, T, r, block)
-    sc = block_scores(q, cnt, kbar, dbar)
+    sc = block_scores(q, cnt, kbar, dbar, mass_order=mass_order, variance_factor=variance_factor)
     chosen = select_blocks(sc["S"], budget // block)
     use = chosen if sel is None else np.asarray(sel)
-    o, lse = compensated_attention(q, k, v, T, use, cnt, kbar, vbar, block)
+    o, lse = compensated_attention(q, k, v, T, use, cnt, kbar, vbar, block, compensate=compensate)
     return {"cnt": cnt, "kbar": kbar, "dbar": dbar, "vbar": vbar, **sc,
             "sel": chosen, "o": o, "lse": lse}
 

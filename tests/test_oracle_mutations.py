@@ -100,6 +100,10 @@ def _attention_no_count(q, k, v, T, sel, cnt, kbar, vbar, block=16, compensate=T
 
 _real_attention = ok.compensated_attention
 
+
+def _attention_always_compensates(q, k, v, T, sel, cnt, kbar, vbar, block=16, compensate=True):
+    return _real_attention(q, k, v, T, sel, cnt, kbar, vbar, block, True)
+
 P9 = lambda: pins.test_p9_second_order_mass_estimate_converges_at_fourth_order()
 
 MUTATIONS = {
@@ -125,6 +129,12 @@ MUTATIONS = {
                        pins.test_p2_constant_blocks_compensate_exactly]),
     "ties to higher index": (("select_blocks", _select_ties_high),
                              [pins.test_p2_constant_blocks_compensate_exactly]),
+    "variance factor kept in the mass-only ablation": (("block_scores", _scores_variant("plain")),
+        [lambda: pins.test_p7_ablation_mass_score_without_compensation_is_optimal(0)]),
+    "compensation kept in the no-compensation ablation": (
+        ("compensated_attention", _attention_always_compensates),
+        [lambda: pins.test_p7_no_compensation_single_head_is_topk_mass(0),
+         lambda: pins.test_p7_ablation_mass_score_without_compensation_is_optimal(0)]),
     "compensation without block size": (("compensated_attention", _attention_no_count),
                                         [lambda: pins.test_p5_log_partition_identity_and_token_level_output(0)]),
 }

@@ -221,6 +221,35 @@ def test_p7_no_compensation_single_head_is_topk_mass(seed):
     np.testing.assert_allclose(lse_d - lse_nc, bl, rtol=1e-9)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_p7_ablation_mass_score_without_compensation_is_optimal(seed):
+    """The page's ablations "Mean compensation removed" and "no outer variance
+    factor" together: with one query head, the score is the estimated block
+    mass p̂_b. When p̂ is accurate (single-coordinate keys with a small
+    spread, r = d), the oracle's kept set from summaries alone equals the
+    brute-force minimiser of the exact no-compensation loss, and its output
+    normaliser is ln Z minus that loss."""
+    rng = np.random.default_rng(200 + seed)
+    d, NB, Kb = 16, 10, 5
+    T = 16 * NB
+    amp = 0.05 * np.exp(rng.uniform(-1.0, 1.0, NB))
+    k = one_coordinate_keys(NB, d, rng, amp=amp, mean_scale=0.8)
+    v = rng.standard_normal((T, d))
+    q = rng.standard_normal((1, d))
+    kb, vb = synth.bf16_bits(k), synth.bf16_bits(v)
+    kd, vd = ok.decode_bf16(kb), ok.decode_bf16(vb)
+    ex = th.exact_block_quantities(q, kd, T)
+    best, bl, second = th.brute_force_best(lambda s: th.no_compensation_loss(ex["p"], s), NB, Kb)
+    res = ok.decode_step(q, kb, vb, T, d, 16 * Kb, compensate=False, variance_factor=False)
+    np.testing.assert_allclose(res["S"], res["phat"][0], rtol=1e-12)
+    if second > bl * 1.02:
+        np.testing.assert_array_equal(res["sel"], best)
+    _, lse_d = ok.dense_attention(q, kd, vd, T)
+    cnt, kbar, _, vbar = ok.block_summaries(kd, vd, T, d)
+    _, lse_best = ok.compensated_attention(q, kd, vd, T, best, cnt, kbar, vbar, compensate=False)
+    np.testing.assert_allclose(lse_d - lse_best, bl, rtol=1e-9)
+
+
 # ---------------------------------------------------------------- P8
 @pytest.mark.parametrize("seed", range(4))
 def test_p8_forced_set_and_budget_by_brute_force(seed):
