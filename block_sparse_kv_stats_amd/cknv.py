@@ -110,6 +110,12 @@ def _ptr(t, dtype=None, numel=None, what=""):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# cknv_shape.flags bits: the page's ablation variants (cknv.h)
+FLAG_NO_COMPENSATION = 0x1
+FLAG_MASS_ONLY_SCORE = 0x2
+FLAG_FIRST_ORDER_MASS = 0x4
+
+
 def make_shape(S, H, G, d, r, cap_blocks, flags=0) -> Shape:
     return Shape(S, H, G, d, r, BLOCK, cap_blocks, flags)
 

@@ -17,7 +17,7 @@ static int check_shape(const cknv_shape* sh) {
   if (sh->d != 64 && sh->d != 128) return CKNV_EUNSUPPORTED;
   if (sh->G != 1 && sh->G != 2 && sh->G != 4 && sh->G != 8) return CKNV_EUNSUPPORTED;
   if (sh->r > sh->d || sh->d % sh->r != 0) return CKNV_EUNSUPPORTED;
-  if (sh->flags != 0u) return CKNV_EUNSUPPORTED;
+  if (sh->flags & ~CKNV_FLAGS_ALL) return CKNV_EUNSUPPORTED;
   if ((long long)sh->S * sh->H > (1 << 20)) return CKNV_EUNSUPPORTED;
   return CKNV_OK;
 }
@@ -144,6 +144,7 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
   a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C; a.rows = p.rows;
   a.xcd = (p.U % 8) == 0;
+  a.flags = (int)shape->flags;
   a.isd = 1.0f / sqrtf((float)shape->d);
   hipError_t e = launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream);
   if (e != hipSuccess) return CKNV_EHIP;
@@ -168,6 +169,7 @@ static int decode_score_impl(const Plan& p, const cknv_shape* shape, const cknv_
   a.xcd = (p.U % 8) == 0;
   a.closed_only = 1;
   a.t0_out = reinterpret_cast<int32_t*>(w + p.off_t0);
+  a.flags = (int)shape->flags;
   a.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream));
 }
@@ -189,6 +191,7 @@ static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv
   sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
   sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf;
   sa.bpw_shift = p.bpw == 8 ? 3 : 4;
+  sa.flags = (int)shape->flags;
   sa.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_step(shape->d, shape->G, sa, p.U, (hipStream_t)stream));
 }
@@ -260,6 +263,7 @@ static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const
   a.S = shape->S; a.H = shape->H; a.cap_blocks = shape->cap_blocks; a.max_blocks = max_blocks;
   a.Kb = p.Kb; a.C = p.C; a.P = dense ? p.Pd : p.P; a.BPW = p.BPW;
   a.xcd = (p.U % 8) == 0;
+  a.flags = (int)shape->flags;
   a.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_attend(shape->d, shape->G, dense, a, p.U, (hipStream_t)stream));
 }

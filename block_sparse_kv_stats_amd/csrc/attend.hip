@@ -60,7 +60,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   static_assert(G * D / 4 <= kThreads, "one float4 of q per thread");
   const float4 qv = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : G * D / 4 - 1];
   const int c0 = (int)((long)p * a.C / a.P), c1 = (int)((long)(p + 1) * a.C / a.P);
-  stage_records<D, G>(a.comp + ((size_t)unit * a.C + c0) * G * W, c1 - c0, recs + kWaves * G * W);
+  // The no-compensation ablation has no chunk records and subtracts nothing.
+  const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
+  const int nrec = nc ? 0 : c1 - c0;
+  stage_records<D, G>(a.comp + ((size_t)unit * a.C + c0) * G * W, nrec, recs + kWaves * G * W);
   if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
   lds_barrier();
 
@@ -85,12 +88,17 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   st.init();
 #pragma unroll
   for (int i = 0; i < kBlocksPerAttendWave; ++i)
-    if (use[i]) absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
+    if (use[i]) {
+      if (nc)
+        absorb<D, G, false>(st, tile[i], bm[i], q_l, lane, a.isd);
+      else
+        absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
+    }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
   lds_barrier();
 
   float* po = a.part + ((size_t)unit * a.P + p) * G * W;
-  merge_records<D, G>(recs, kWaves + (c1 - c0), po, scl);
+  merge_records<D, G>(recs, kWaves + nrec, po, scl);
 }
 
 template <int D, int G>

@@ -69,6 +69,7 @@ struct ScoreArgs {
   int S, H, r, cap_blocks, max_blocks, NG, C, xcd, rows;
   int closed_only;  // 1: score only blocks closed before this step's token (fused step)
   int32_t* t0_out;  // fused step: seq_len before the step, per sequence (or null)
+  int flags;        // CKNV_FLAG_* (ablation variants)
   float isd;  // 1/sqrt(d)
 };
 
@@ -83,6 +84,7 @@ struct AttendArgs {
   const int32_t* seq_len; const float* q; const int32_t* sel; const int32_t* n_sel;
   float* out; float* lse; const float* comp; float* part;
   int S, H, cap_blocks, max_blocks, Kb, C, P, BPW, xcd;  // BPW: dense blocks per workgroup
+  int flags;  // CKNV_FLAG_* (ablation variants)
   float isd;
 };
 
@@ -93,6 +95,7 @@ struct StepArgs {
   const float* grp; const float* u; const float* comp;
   float* scores; int32_t* sel; int32_t* n_sel; float* out; float* lse; float* part;
   int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P, bpw_shift;
+  int flags;  // CKNV_FLAG_* (ablation variants)
   float isd;
 };
 

@@ -134,7 +134,8 @@ __device__ __forceinline__ float seg_sum(float x) {
 template <int L>
 __device__ __forceinline__ float row_bcast(float x) { return dpp<kDppBcast0 + L>(x); }
 
-template <int D, int G, int DM, int ROWS>
+// NC: the no-compensation ablation; the mean values are neither read nor summed.
+template <int D, int G, int DM, int ROWS, bool NC>
 __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   constexpr int KC = D / 64;              // float4 chunks per lane per block (16 lanes per block)
   constexpr int E = 4 * KC;               // coordinates per lane
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     for (int i = 0; i < KC; ++i) {
       const int c = j + 16 * i;  // float4 chunk: coordinates 4c..4c+3
       kv[rw][i] = stream_load4(kbar4 + row * (D / 4) + c);
-      vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + c);
+      if constexpr (!NC) vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + c);
       dt.load(a.dbar, row, c, r, D, rw, i);
     }
   }
@@ -218,16 +219,21 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   const bool tv = tb < NB && j < NP;  // a valid block, and not a duplicate lane (NP < 16)
   const float z = x[0] * a.isd, s2 = x[1] * invd;
 
-  // ---- scoring partials of this wave's group: a = ln|b| + z̄ + σ̂²/2
+  // ---- scoring partials of this wave's group: a = ln|b| + z̄ + σ̂²/2, and
+  // u = e^{a - group max} σ̂². The first-order-mass ablation drops σ̂²/2 from a,
+  // the mass-only ablation drops the factor σ̂² from u.
   {
-    const float av = tv ? __logf(n) + z + 0.5f * s2 : -INFINITY;
+    const float half = (a.flags & CKNV_FLAG_FIRST_ORDER_MASS) ? 0.f : 0.5f;
+    const float av = tv ? __logf(n) + z + half * s2 : -INFINITY;
     const float ref = rows_max(seg_max<ROWS>(av));
     const float e = tv ? __expf(av - ref) : 0.f;
     const float l = rows_sum(seg_sum<ROWS>(e));
-    if (tv) a.u[((size_t)unit * MB + tb) * G + tg] = e * s2;
+    const float uf = (a.flags & CKNV_FLAG_MASS_ONLY_SCORE) ? 1.f : s2;
+    if (tv) a.u[((size_t)unit * MB + tb) * G + tg] = e * uf;
     if (base < NB && lane < NP && trow == 0)
       reinterpret_cast<float2*>(a.grp)[((size_t)unit * a.NG + base / BPW) * G + tg] = make_float2(ref, l);
   }
+  if constexpr (NC) return;
 
   // ---- Mean compensation of every block of the wave (kept ones are removed later)
   const float mz = rows_max(seg_max<ROWS>(tv ? z : -INFINITY));
@@ -324,17 +330,21 @@ hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st)
   const int gs = d / a.r;
   const int dm = gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
   const void* f = nullptr;
+  const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
+#define CKNV_SCORE_NC(DD, GG, RR, NC)                                             \
+  f = dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR, NC>        \
+    : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair, RR, NC>      \
+                      : (const void*)score_kernel<DD, GG, kDbarQuad, RR, NC>;
 #define CKNV_SCORE_R(DD, GG, RR)                                                  \
   if (d == DD && G == GG && a.rows == RR) {                                       \
-    f = dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR>          \
-      : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair, RR>        \
-                        : (const void*)score_kernel<DD, GG, kDbarQuad, RR>;       \
+    if (nc) { CKNV_SCORE_NC(DD, GG, RR, true) } else { CKNV_SCORE_NC(DD, GG, RR, false) } \
   }
 #define CKNV_SCORE_CASE(DD) \
   CKNV_SCORE_R(DD, 1, 4) CKNV_SCORE_R(DD, 2, 4) CKNV_SCORE_R(DD, 4, 2) CKNV_SCORE_R(DD, 4, 4) CKNV_SCORE_R(DD, 8, 2)
   CKNV_SCORE_CASE(64) CKNV_SCORE_CASE(128)
 #undef CKNV_SCORE_CASE
 #undef CKNV_SCORE_R
+#undef CKNV_SCORE_NC
   if (!f) return hipErrorInvalidValue;
   return hipLaunchKernel(f, dim3(U * a.C), dim3(kThreads), args, 0, st);
 }

@@ -175,6 +175,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   // folded in the attend phase; it does not depend on the selection.
   const int c0 = (int)((long)p * a.C / P), c1 = (int)((long)(p + 1) * a.C / P);
   const float* crec = a.comp + (size_t)unit * a.C * G * W;
+  // The no-compensation ablation has no records: the fold sees an empty one.
+  const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
   float pm[G], pl[G], pacc[G][VPL];
   {
     const int c = c0 + wave;
@@ -183,10 +185,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float2 ml = *reinterpret_cast<const float2*>(rp + g * W);
-      pm[g] = c < c1 ? ml.x : -INFINITY;
-      pl[g] = ml.y;
+      pm[g] = (c < c1 && !nc) ? ml.x : -INFINITY;
+      pl[g] = nc ? 0.f : ml.y;
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) pacc[g][e] = rp[g * W + 4 + lane * VPL + e];
+      for (int e = 0; e < VPL; ++e) pacc[g][e] = nc ? 0.f : rp[g * W + 4 + lane * VPL + e];
     }
   }
   // Fresh-block tokens (wave OW): np = T0 % 16 cached tokens plus the new one.
@@ -274,8 +276,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       const float z = group_sum<64>(zp) * a.isd;
       const float s2 = group_sum<64>(sp) / (float)D;
       if (lane == 0) {
-        oinfo[g] = __logf((float)n) + z + 0.5f * s2;
-        oinfo[G + g] = s2;
+        // a and the factor of p̂ in S_b, with the ablations' switches
+        const float half = (a.flags & CKNV_FLAG_FIRST_ORDER_MASS) ? 0.f : 0.5f;
+        oinfo[g] = __logf((float)n) + z + half * s2;
+        oinfo[G + g] = (a.flags & CKNV_FLAG_MASS_ONLY_SCORE) ? 1.f : s2;
       }
     }
     if (p == 0) {
@@ -547,14 +551,14 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       } else {
         tile.load(kc, vc, (long)b * kBlock, (long)T0, lane);
         bm.load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
-        if (b < NBa)
+        if (b < NBa && !nc)
           absorb<D, G, true>(st, tile, bm, q_l, lane, a.isd);
         else
           absorb<D, G, false>(st, tile, bm, q_l, lane, a.isd);
       }
     }
   }
-  {
+  if (!nc) {
     for (int cb = c0 + wave + NW; cb < c1; cb += RPW * NW) {
       float rm[RPW][G], rl[RPW][G], racc[RPW][G][VPL];
 #pragma unroll

@@ -49,7 +49,14 @@ extern "C" {
 
 #define CKNV_OK 0
 #define CKNV_EINVAL (-1)        /* null pointer, non-positive or inconsistent size */
-#define CKNV_EUNSUPPORTED (-2)  /* d not 64/128, G not 1/2/4/8, block != 16, r not dividing d, flags != 0, or too many blocks */
+#define CKNV_EUNSUPPORTED (-2)  /* d not 64/128, G not 1/2/4/8, block != 16, r not dividing d, unknown flags, or too many blocks */
+
+/* cknv_shape.flags: the ablation variants the page reports ("Assumptions and
+ * limits"); 0 is CompKV itself. Any combination is allowed. */
+#define CKNV_FLAG_NO_COMPENSATION 0x1u  /* unselected blocks are dropped instead of Mean-compensated */
+#define CKNV_FLAG_MASS_ONLY_SCORE 0x2u  /* S_b = sum_g p̂_{g,b}: no outer variance factor */
+#define CKNV_FLAG_FIRST_ORDER_MASS 0x4u /* p̂ from |b| exp(z̄): no σ̂²/2 in the mass estimate */
+#define CKNV_FLAGS_ALL 0x7u
 #define CKNV_ENOSPACE (-3)      /* workspace smaller than cknv_workspace_size, or max_blocks > cap_blocks */
 #define CKNV_EHIP (-4)          /* a HIP call or kernel launch failed */
 
@@ -62,7 +69,7 @@ typedef struct cknv_shape {
   int32_t r;          /* variance groups of the key coordinates, divides d */
   int32_t block;      /* tokens per block, must be 16 */
   int32_t cap_blocks; /* capacity of every unit, in blocks */
-  uint32_t flags;     /* must be 0 (reserved for the page's ablation variants) */
+  uint32_t flags;     /* 0, or CKNV_FLAG_* bits (ablation variants) */
 } cknv_shape;
 
 /* KV cache and block-summary store of one layer, all in HBM (device pointers).

@@ -18,12 +18,19 @@ def to_dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def upload(w: synth.Workload, data: dict, cap_blocks=None, max_blocks=None):
+def oracle_variant(flags: int) -> dict:
+    """The oracle's keyword arguments for the ablation flags of a shape."""
+    return dict(compensate=not flags & cknv.FLAG_NO_COMPENSATION,
+                variance_factor=not flags & cknv.FLAG_MASS_ONLY_SCORE,
+                mass_order=1 if flags & cknv.FLAG_FIRST_ORDER_MASS else 2)
+
+
+def upload(w: synth.Workload, data: dict, cap_blocks=None, max_blocks=None, flags=0):
     """LayerCache holding each sequence's prefill tokens (later slots zero),
     seq_len = prefill, summaries built on the GPU."""
     import torch
     cb = cap_blocks or w.cap_blocks
-    shape = cknv.make_shape(w.S, w.H, w.G, w.d, w.r, cb)
+    shape = cknv.make_shape(w.S, w.H, w.G, w.d, w.r, cb, flags)
     cache = cknv.LayerCache.allocate(shape)
     k = np.zeros((w.S, w.H, cb * 16, w.d), dtype=np.uint16)
     v = np.zeros_like(k)
@@ -88,12 +95,13 @@ def rel_l2(a, b):
 
 
 def check_unit(w, data, s, h, T, step, q_all, sel_all, nsel_all, out_all, lse_all, scores_all,
-               budget):
+               budget, flags=0):
     """Compare one unit's GPU results with the oracle's from-scratch step."""
     G = w.G
     u = s * w.H + h
     q = q_all[s, h * G:(h + 1) * G]
-    ref = ok.decode_step(q, data["k"][s, h], data["v"][s, h], T, w.r, budget)
+    var = oracle_variant(flags)
+    ref = ok.decode_step(q, data["k"][s, h], data["v"][s, h], T, w.r, budget, **var)
     Kb = budget // 16
     n = int(nsel_all[u])
     check_selection(ref["S"], sel_all[u], n, Kb)
@@ -102,7 +110,7 @@ def check_unit(w, data, s, h, T, step, q_all, sel_all, nsel_all, out_all, lse_al
         check_scores(scores_all[s, h, :NB], ref["S"])
     # output against the oracle evaluated on the GPU's (valid) kept set
     o_ref = ok.decode_step(q, data["k"][s, h], data["v"][s, h], T, w.r, budget,
-                           sel=np.asarray(sel_all[u][:n]))
+                           sel=np.asarray(sel_all[u][:n]), **var)
     err = rel_l2(out_all[s, h * G:(h + 1) * G], o_ref["o"])
     assert np.all(err <= OUT_RTOL_L2), f"unit {u}: output rel L2 {err}"
     lse_err = np.abs(lse_all[s, h * G:(h + 1) * G] - o_ref["lse"])
@@ -127,6 +135,7 @@ def step_and_check(w, data, cache, dec, step, units=None, check_summaries=False)
     nk, nv = new_token(data, t_idx)
     import torch
     q = torch.from_numpy(data["q"][step]).cuda()
+    flags = int(cache.shape.flags)
     dec(q, nk, nv)
     torch.cuda.synchronize()
     sel, nsel = dec.sel.cpu().numpy(), dec.n_sel.cpu().numpy()
@@ -140,7 +149,7 @@ def step_and_check(w, data, cache, dec, step, units=None, check_summaries=False)
                 continue
             T = t_idx[s] + 1
             worst = max(worst, check_unit(w, data, s, h, T, step, data["q"][step], sel, nsel,
-                                             out, lse, scores, w.budget))
+                                             out, lse, scores, w.budget, flags))
             if check_summaries:
                 summaries_equal(cache, data, w, s, h, T)
     return worst

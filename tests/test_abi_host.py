@@ -55,9 +55,22 @@ def test_workspace_size_valid_and_monotone():
 @pytest.mark.parametrize("kw,code", [
     (dict(d=96), cknv.EUNSUPPORTED), (dict(G=3), cknv.EUNSUPPORTED), (dict(r=3), cknv.EUNSUPPORTED),
     (dict(r=256), cknv.EUNSUPPORTED), (dict(S=0), cknv.EINVAL), (dict(H=-1), cknv.EINVAL),
-    (dict(flags=1), cknv.EUNSUPPORTED)])
+    (dict(flags=8), cknv.EUNSUPPORTED), (dict(flags=0x80000001), cknv.EUNSUPPORTED)])
 def test_bad_shapes(kw, code):
     assert wsize(shape(**kw))[0] == code
+
+
+@pytest.mark.parametrize("flags", range(8))
+def test_ablation_flags_accepted(flags):
+    """Every combination of the three ablation bits is a valid shape."""
+    assert wsize(shape(flags=flags))[0] == cknv.OK
+
+
+def test_flag_bits_match_header():
+    text = open(os.path.join(ROOT, "include", "cknv.h")).read()
+    for name in ("NO_COMPENSATION", "MASS_ONLY_SCORE", "FIRST_ORDER_MASS"):
+        m = re.search(rf"#define CKNV_FLAG_{name} (0x[0-9a-f]+)u", text)
+        assert m and int(m.group(1), 16) == getattr(cknv, f"FLAG_{name}")
 
 
 def test_block_size_must_be_16():

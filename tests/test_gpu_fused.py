@@ -25,13 +25,13 @@ def fused_dec(cache, mb, budget, want_scores=True):
     return cknv.DecodeStep(cache, mb, budget, want_scores=want_scores, fused=True)
 
 
-def run_steps(w, steps=None, check_every=1, summaries_every=0):
+def run_steps(w, steps=None, check_every=1, summaries_every=0, flags=0):
     say(f"{w.name}: S={w.S} H={w.H} G={w.G} d={w.d} r={w.r} budget={w.budget} "
-        f"prefill={w.prefill[:4]} steps={w.steps}")
+        f"prefill={w.prefill[:4]} steps={w.steps} flags={flags}")
     data = synth.gen_layer(w)
     n = w.steps if steps is None else steps
     mb = w.max_blocks_after(n - 1)
-    cache = gu.upload(w, data, max_blocks=mb)
+    cache = gu.upload(w, data, max_blocks=mb, flags=flags)
     dec = fused_dec(cache, mb, w.budget)
     for step in range(n):
         if step % check_every == 0 or step == n - 1:
@@ -154,7 +154,24 @@ def test_fused_mixed_ties_at_the_cut():
     gu.step_and_check(w, data, cache, dec, 0, check_summaries=False)
 
 
-def test_fused_equals_three_calls():
+@pytest.mark.parametrize("flags", range(1, 8))
+def test_fused_ablation_variants(flags):
+    """The page's ablations (no compensation, mass-only score, first-order
+    mass, and their combinations) against the oracle's same variant, across
+    a block close, with a partial open block and a short sequence."""
+    w = synth.WORKLOADS["llama8b_32k"].replace(S=2, prefill=(16 * 700 - 2, 40), steps=3,
+                                                budget=512)
+    run_steps(w, summaries_every=2, flags=flags)
+
+
+@pytest.mark.parametrize("flags", [1, 2, 4, 7])
+def test_fused_ablation_variants_many_parts(flags):
+    w = synth.WORKLOADS["qwen8b_128k"].replace(prefill=(16 * 3000 + 5,), steps=1)
+    run_steps(w, flags=flags)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 6])
+def test_fused_equals_three_calls(flags):
     """Same inputs through cknv_decode_step and through append + score_select
     + attend: identical kept lists and summaries, outputs and scores equal to
     fp32 rounding."""
@@ -163,7 +180,7 @@ def test_fused_equals_three_calls():
     mb = w.max_blocks_after(0)
     res = []
     for fused in (False, True):
-        cache = gu.upload(w, data, max_blocks=mb)
+        cache = gu.upload(w, data, max_blocks=mb, flags=flags)
         dec = cknv.DecodeStep(cache, mb, w.budget, want_scores=True, fused=fused)
         nk, nv = gu.new_token(data, list(data["prefill"]))
         dec(torch.from_numpy(data["q"][0]).cuda(), nk, nv)

@@ -24,12 +24,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-def run_single_step(w, units=None, check_summaries=True):
+def run_single_step(w, units=None, check_summaries=True, flags=0):
     say(f"workload {w.name}: S={w.S} H={w.H} G={w.G} d={w.d} r={w.r} budget={w.budget} "
-        f"prefill={w.prefill[:4]}")
+        f"prefill={w.prefill[:4]} flags={flags}")
     data = synth.gen_layer(w)
     mb = w.max_blocks_after(0)
-    cache = gu.upload(w, data, max_blocks=mb)
+    cache = gu.upload(w, data, max_blocks=mb, flags=flags)
     dec = cknv.DecodeStep(cache, mb, w.budget, want_scores=True)
     return gu.step_and_check(w, data, cache, dec, 0, units, check_summaries)
 
@@ -49,6 +49,14 @@ def test_llama8b_32k_partial_open_block():
 
 def test_qwen32b_64k_r128_step():
     run_single_step(synth.WORKLOADS["qwen32b_64k"])
+
+
+@pytest.mark.parametrize("flags", range(1, 8))
+def test_ablation_variants(flags):
+    """The page's ablations through append + score_select + attend, against
+    the oracle's same variant; a partial open block and a short sequence."""
+    w = synth.WORKLOADS["llama8b_32k"].replace(S=2, prefill=(16 * 900 + 3, 33), budget=1024)
+    run_single_step(w, flags=flags)
 
 
 def test_streaming_with_block_closes_shortened():
