@@ -58,15 +58,17 @@ def step_bytes(w, T: int):
     """Algorithmic HBM bytes of one fused step over all units, split by
     kernel (T = tokens after the step's append).
     score_kernel: k̄ + D̄ + |b| of every block closed before the step and v̄
-    of those of them that are not kept;
+    of those of them that are not kept; the append (the open block's cached
+    BF16 tokens read, the token and its block's summary written);
     step_kernel: BF16 K and V of the kept blocks' tokens."""
     U = w.S * w.H
     NB = math.ceil(T / 16)
     closed = (T - 1) // 16
     kept = min(w.Kb, NB)
     kept_closed = kept - (NB - closed)  # the block holding the new token is always kept
-    score = U * (closed * (w.d + w.r + 1) * 4 + (closed - kept_closed) * w.d * 4)
     open_n = T - 16 * (NB - 1)
+    append = (open_n - 1) * 2 * w.d * 2 + 2 * w.d * 2 + (2 * w.d + w.r + 1) * 4
+    score = U * (closed * (w.d + w.r + 1) * 4 + (closed - kept_closed) * w.d * 4 + append)
     kept_tokens = (kept - 1) * 16 + open_n
     attend = U * kept_tokens * 2 * w.d * 2
     return score, attend

@@ -54,9 +54,10 @@ SIGNATURES = {
                           P],
     "cknv_decode_step": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P, I32, I32, P, P, P,
                          P, P, P, SZ, P],
-    "cknv_decode_score": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, I32, I32, P, SZ, P],
-    "cknv_decode_finish": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P, I32, I32, P, P,
-                           P, P, P, P, SZ, P],
+    "cknv_decode_score": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P, I32, I32, P, SZ,
+                          P],
+    "cknv_decode_finish": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, I32, I32, P, P, P, P,
+                           P, P, SZ, P],
 }
 
 
@@ -328,7 +329,8 @@ class BoundStep:
                            self.attend_args[7], self.attend_args[8], w, wn, st)
         self._append, self._score = L.cknv_append, L.cknv_score_select
         self._attend, self._dense = L.cknv_attend, L.cknv_dense_attend
-        self.dscore_args = (self.shape, cp, qp, budget, max_blocks, w, wn, st)
+        self.dscore_args = self.fused_args[:7] + (w, wn, st)
+        self.dfinish_args = (self.shape, cp) + self.fused_args[4:]
         self._fused = L.cknv_decode_step
         self._dscore, self._dfinish = L.cknv_decode_score, L.cknv_decode_finish
 
@@ -365,13 +367,13 @@ class BoundStep:
             raise CknvError(st, "cknv_decode_step")
 
     def decode_score(self):
-        """First half of cknv_decode_step (the streaming scoring pass)."""
+        """First half of cknv_decode_step (the append and the streaming scoring pass)."""
         st = self._dscore(*self.dscore_args)
         if st:
             raise CknvError(st, "cknv_decode_score")
 
     def decode_finish(self):
         """Second half of cknv_decode_step."""
-        st = self._dfinish(*self.fused_args)
+        st = self._dfinish(*self.dfinish_args)
         if st:
             raise CknvError(st, "cknv_decode_finish")

@@ -42,7 +42,7 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   q.bpw = 4 * q.rows;
   q.NG = (max_blocks + q.bpw - 1) / q.bpw;
   q.Kb = budget_tokens / kBlock;
-  q.C = (max_blocks + 4 * q.bpw - 1) / (4 * q.bpw);
+  q.C = (max_blocks + kScoreWaves * q.bpw - 1) / (kScoreWaves * q.bpw);
   const int per_wg = kWaves;  // kept blocks per attend workgroup (one per wave)
   q.P = (q.Kb + per_wg - 1) / per_wg;
   const int pc = (q.C + kMaxChunksPerAttendWG - 1) / kMaxChunksPerAttendWG;
@@ -51,7 +51,7 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   bpw = bpw > kDenseBlocksPerWG ? bpw : kDenseBlocksPerWG;
   q.BPW = bpw;
   q.Pd = (max_blocks + bpw - 1) / bpw;
-  q.Pf = (q.Kb + kStepKeptPerPart - 1) / kStepKeptPerPart;
+  q.Pf = (q.Kb + step_kept_per_part(G) - 1) / step_kept_per_part(G);
   const size_t W = (size_t)rec_words(d);
   size_t off = 0;
   q.off_grp = off;
@@ -68,6 +68,10 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   off = align256(off + (size_t)sh->S * 4);
   q.off_fpart = off;
   off = align256(off + (size_t)q.U * q.Pf * G * W * 4);
+  q.off_finfo = off;
+  off = align256(off + (size_t)q.U * G * 2 * 4);
+  q.off_hdr = off;
+  off = align256(off + (size_t)q.U * q.C * G * 2 * 4);
   q.total = off;
   if (max_blocks > kSelThreads * kSelKeysPerThread) return CKNV_EUNSUPPORTED;
   *p = q;
@@ -141,6 +145,7 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   a.grp = reinterpret_cast<float*>(w + p.off_grp);
   a.u = reinterpret_cast<float*>(w + p.off_u);
   a.comp = reinterpret_cast<float*>(w + p.off_comp);
+  a.hdr = reinterpret_cast<float*>(w + p.off_hdr);
   a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
   a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C; a.rows = p.rows;
   a.xcd = (p.U % 8) == 0;
@@ -157,35 +162,41 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
 }
 
 static int decode_score_impl(const Plan& p, const cknv_shape* shape, const cknv_cache* cache,
-                             const float* q, int32_t max_blocks, char* w, void* stream) {
+                             const uint16_t* new_k, const uint16_t* new_v, const float* q,
+                             int32_t max_blocks, char* w, void* stream) {
   ScoreArgs a{};
   a.kbar = cache->kbar; a.dbar = cache->dbar; a.cnt = cache->cnt; a.vbar = cache->vbar;
   a.seq_len = cache->seq_len; a.q = q;
   a.grp = reinterpret_cast<float*>(w + p.off_grp);
   a.u = reinterpret_cast<float*>(w + p.off_u);
   a.comp = reinterpret_cast<float*>(w + p.off_comp);
+  a.hdr = reinterpret_cast<float*>(w + p.off_hdr);
   a.S = shape->S; a.H = shape->H; a.r = shape->r; a.cap_blocks = shape->cap_blocks;
   a.max_blocks = max_blocks; a.NG = p.NG; a.C = p.C; a.rows = p.rows;
   a.xcd = (p.U % 8) == 0;
   a.closed_only = 1;
+  a.nfresh = p.U;
+  a.k = cache->k; a.v = cache->v; a.new_k = new_k; a.new_v = new_v;
   a.t0_out = reinterpret_cast<int32_t*>(w + p.off_t0);
+  a.finfo = reinterpret_cast<float*>(w + p.off_finfo);
   a.flags = (int)shape->flags;
   a.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream));
 }
 
 static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv_cache* cache,
-                              const uint16_t* new_k, const uint16_t* new_v, const float* q,
-                              int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel,
-                              float* out, float* lse, char* w, void* stream) {
+                              const float* q, int32_t max_blocks, float* scores, int32_t* sel,
+                              int32_t* n_sel, float* out, float* lse, char* w, void* stream) {
   StepArgs sa{};
   sa.k = cache->k; sa.v = cache->v; sa.kbar = cache->kbar; sa.dbar = cache->dbar;
   sa.cnt = cache->cnt; sa.vbar = cache->vbar; sa.seq_len = cache->seq_len;
   sa.t0 = reinterpret_cast<const int32_t*>(w + p.off_t0);
-  sa.new_k = new_k; sa.new_v = new_v; sa.q = q;
+  sa.q = q;
+  sa.finfo = reinterpret_cast<const float*>(w + p.off_finfo);
   sa.grp = reinterpret_cast<const float*>(w + p.off_grp);
   sa.u = reinterpret_cast<const float*>(w + p.off_u);
   sa.comp = reinterpret_cast<const float*>(w + p.off_comp);
+  sa.hdr = reinterpret_cast<const float*>(w + p.off_hdr);
   sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel; sa.out = out; sa.lse = lse;
   sa.part = reinterpret_cast<float*>(w + p.off_fpart);
   sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
@@ -206,26 +217,27 @@ static int decode_check(const cknv_shape* shape, const cknv_cache* cache, int32_
   return CKNV_OK;
 }
 
-int cknv_decode_score(const cknv_shape* shape, const cknv_cache* cache, const float* q,
-                      int32_t budget_tokens, int32_t max_blocks, void* ws, size_t ws_bytes,
-                      void* stream) {
+int cknv_decode_score(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                      const uint16_t* new_v, const float* q, int32_t budget_tokens,
+                      int32_t max_blocks, void* ws, size_t ws_bytes, void* stream) {
   Plan p;
   int st = decode_check(shape, cache, max_blocks, budget_tokens, ws, ws_bytes, &p);
   if (st) return st;
-  if (!q) return CKNV_EINVAL;
-  return decode_score_impl(p, shape, cache, q, max_blocks, static_cast<char*>(ws), stream);
+  if (!new_k || !new_v || !q) return CKNV_EINVAL;
+  return decode_score_impl(p, shape, cache, new_k, new_v, q, max_blocks, static_cast<char*>(ws),
+                           stream);
 }
 
-int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
-                       const uint16_t* new_v, const float* q, int32_t budget_tokens,
-                       int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel,
-                       float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                       int32_t budget_tokens, int32_t max_blocks, float* scores, int32_t* sel,
+                       int32_t* n_sel, float* out, float* lse, void* ws, size_t ws_bytes,
+                       void* stream) {
   Plan p;
   int st = decode_check(shape, cache, max_blocks, budget_tokens, ws, ws_bytes, &p);
   if (st) return st;
-  if (!new_k || !new_v || !q || !sel || !n_sel || !out) return CKNV_EINVAL;
-  return decode_finish_impl(p, shape, cache, new_k, new_v, q, max_blocks, scores, sel, n_sel, out,
-                            lse, static_cast<char*>(ws), stream);
+  if (!q || !sel || !n_sel || !out) return CKNV_EINVAL;
+  return decode_finish_impl(p, shape, cache, q, max_blocks, scores, sel, n_sel, out, lse,
+                            static_cast<char*>(ws), stream);
 }
 
 int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
@@ -237,9 +249,9 @@ int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uin
   if (st) return st;
   if (!new_k || !new_v || !q || !sel || !n_sel || !out) return CKNV_EINVAL;
   char* w = static_cast<char*>(ws);
-  if ((st = decode_score_impl(p, shape, cache, q, max_blocks, w, stream))) return st;
-  return decode_finish_impl(p, shape, cache, new_k, new_v, q, max_blocks, scores, sel, n_sel, out,
-                            lse, w, stream);
+  if ((st = decode_score_impl(p, shape, cache, new_k, new_v, q, max_blocks, w, stream))) return st;
+  return decode_finish_impl(p, shape, cache, q, max_blocks, scores, sel, n_sel, out, lse, w,
+                            stream);
 }
 
 static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const float* q,

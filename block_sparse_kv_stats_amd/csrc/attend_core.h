@@ -117,7 +117,9 @@ __device__ __forceinline__ void spread_rows(float x, float& r0, float& r1, float
   r1 = swap32_lo(b, r3);
 }
 
-// Add one block's exact terms (and, with COMP, remove its compensation terms).
+// Add one block's exact terms (and, with COMP, remove its compensation terms;
+// a BlockMean with n = 0 removes nothing). A tile with no valid token adds
+// nothing and leaves the state unchanged.
 template <int D, int G, bool COMP>
 __device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, const BlockMean<D>& bm,
                                        const float* q_l, int lane, float isd) {
@@ -152,7 +154,7 @@ __device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, co
   for (int g = 0; g < G; ++g) {
     float bmax = fmaxf(fmaxf(z[0][g], z[1][g]), fmaxf(z[2][g], z[3][g]));
     bmax = rows_max(bmax);
-    if (COMP) bmax = fmaxf(bmax, zbar[g]);
+    if (COMP && bm.n > 0.f) bmax = fmaxf(bmax, zbar[g]);
     const float M = fmaxf(st.m[g], bmax);
     const float sc = rescale(st.m[g], M);
     float l = st.l[g] * sc;
@@ -177,7 +179,7 @@ __device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, co
       }
     }
     if (COMP) {
-      const float w = bm.n * __expf(zbar[g] - M);
+      const float w = bm.n > 0.f ? bm.n * __expf(zbar[g] - M) : 0.f;
       l -= w;
 #pragma unroll
       for (int e = 0; e < VPL; ++e) acc[e] -= w * bm.vb[e];

@@ -17,6 +17,8 @@ constexpr int kWaves = kThreads / 64;
 // 2 or 4 rows (a score group of 8 or 16 blocks; 2 rows at G = 8). Fewer rows
 // give more waves, which pays while the grid is small; the workspace plan
 // picks the rows. The selection works with either group size.
+constexpr int kScoreThreads = 256;  // score kernel: 4 waves per workgroup (one chunk record each)
+constexpr int kScoreWaves = kScoreThreads / 64;
 constexpr int kScoreMinGroup = 8;  // blocks of the smaller score group
 __host__ __device__ constexpr int score_rows(int G, int max_blocks, int units) {
   return G >= 8 ? 2 : G <= 2 ? 4 : ((long)units * ((max_blocks + 7) / 8) <= 4096 ? 2 : 4);
@@ -46,7 +48,7 @@ struct Plan {
   int Pf;           // fused-step workgroups per unit = ceil(Kb/kStepKeptPerPart)
   int Pd;           // dense-attend workgroups per unit
   int BPW;          // dense-attend blocks per workgroup
-  size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, total;
+  size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, off_finfo, off_hdr, total;
 };
 
 int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p);
@@ -63,12 +65,18 @@ struct BuildArgs {
 };
 
 struct ScoreArgs {
-  const float* kbar; const float* dbar; const float* cnt; const float* vbar;
+  float* kbar; float* dbar; float* cnt; float* vbar;  // written only by the fresh-block workgroups
   const int32_t* seq_len; const float* q;
   float* grp; float* u; float* comp;
+  float* hdr;  // per chunk and query head: (max, sum) of a over the chunk's blocks
   int S, H, r, cap_blocks, max_blocks, NG, C, xcd, rows;
   int closed_only;  // 1: score only blocks closed before this step's token (fused step)
-  int32_t* t0_out;  // fused step: seq_len before the step, per sequence (or null)
+  // Fused step only (nfresh = S*H, else 0): workgroups 0..nfresh-1 append the
+  // step's token of unit blockIdx and summarise the block it lands in.
+  int nfresh;
+  uint16_t* k; uint16_t* v; const uint16_t* new_k; const uint16_t* new_v;
+  int32_t* t0_out;  // seq_len before the step, per sequence
+  float* finfo;     // per unit and query head: (a, factor of p̂ in S) of that block; a = -inf if none
   int flags;        // CKNV_FLAG_* (ablation variants)
   float isd;  // 1/sqrt(d)
 };
@@ -90,10 +98,10 @@ struct AttendArgs {
 
 struct StepArgs {
   uint16_t* k; uint16_t* v; float* kbar; float* dbar; float* cnt; float* vbar;
-  int32_t* seq_len; const int32_t* t0;
-  const uint16_t* new_k; const uint16_t* new_v; const float* q;
-  const float* grp; const float* u; const float* comp;
+  int32_t* seq_len; const int32_t* t0; const float* q;
+  const float* grp; const float* u; const float* comp; const float* hdr;
   float* scores; int32_t* sel; int32_t* n_sel; float* out; float* lse; float* part;
+  const float* finfo;  // per unit and query head: (a, factor) of the block the token landed in
   int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P, bpw_shift;
   int flags;  // CKNV_FLAG_* (ablation variants)
   float isd;

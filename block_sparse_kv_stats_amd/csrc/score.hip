@@ -14,16 +14,22 @@
 // σ̂² is evaluated per coordinate, (1/d) sum_i q_{g,i}^2 D̄_{b,t(i)} with t(i)
 // the group of coordinate i, which is the same sum regrouped.
 //
-// Grid: C workgroups ("chunks") per unit, 64 blocks each, 16 per wave; a
-// block is read by 16 lanes (d/64 float4 of k̄, D̄ and v̄ each), so the wave
-// reads 4 blocks' rows per load instruction. Every load is issued before
+// Grid: C workgroups ("chunks") per unit of kScoreWaves waves, 4*ROWS blocks
+// per wave; a block is read by 16 lanes (d/64 float4 of k̄, D̄ and v̄ each), so
+// the wave reads 4 blocks' rows per load instruction. Every load is issued before
 // seq_len is known; blocks past the context are masked afterwards. Per wave
 // (a 16-block group) the kernel writes the LSE partial of
 // a = ln|b| + z̄ + σ̂²/2 and per block u_{g,b} = exp(a - group max) σ̂²; per
 // chunk it writes the Mean-compensation sums of ALL its blocks,
 //   (m, l = sum |b| e^{z̄-m}, acc = sum |b| e^{z̄-m} v̄_b),
 // which the attend kernel corrects by removing the kept blocks' terms (the
-// kept set is not known yet). The selection kernel (select.hip) runs next.
+// kept set is not known yet), and apart from it the chunk's LSE partial of a
+// per query head. The selection kernel (select.hip) runs next.
+//
+// In the fused step the grid starts with one extra workgroup per unit that
+// appends the step's token and summarises the block it lands in ("How to use
+// it": the current block's statistics are refreshed every step); the
+// scoring workgroups then cover only the blocks closed before the token.
 #include "cknv_internal.h"
 
 namespace cknv {
@@ -134,21 +140,142 @@ __device__ __forceinline__ float seg_sum(float x) {
 template <int L>
 __device__ __forceinline__ float row_bcast(float x) { return dpp<kDppBcast0 + L>(x); }
 
+// Fused step, wave 0 of workgroup `unit`: store the token (new_k, new_v) at
+// slot T0 = seq_len, summarise its block from the np = T0 % 16 cached tokens
+// and the new one ({|b|, k̄, D̄, v̄}, population variances, D̄ over contiguous
+// groups of d/r coordinates), and write that block's a and its factor in S
+// (σ̂², or 1 for the mass-only ablation) per query head to finfo. A sequence
+// whose cache is full (or whose block lies past max_blocks) appends nothing
+// and gets a = -inf. Lane l owns coordinates [l*VPL, l*VPL + VPL).
+template <int D, int G>
+__device__ void fresh_block(const ScoreArgs& a, int unit) {
+  constexpr int VPL = D / 64;
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int s = unit / a.H, h = unit - s * a.H;
+  const int T0 = a.seq_len[s];
+  const long cap_tok = (long)a.cap_blocks * kBlock;
+  const int fblk = T0 / kBlock;
+  const bool app = T0 < cap_tok && fblk < a.max_blocks;
+  float2* fi = reinterpret_cast<float2*>(a.finfo) + (size_t)unit * G;
+  if (!app) {
+    if (lane < G) fi[lane] = make_float2(-INFINITY, 0.f);
+    if (h == 0 && lane == 0) a.t0_out[s] = T0;
+    return;
+  }
+  uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
+  uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
+  const long tok0 = (long)fblk * kBlock;
+  const int np = T0 - fblk * kBlock, n = np + 1;
+  uint32_t fk[16], fv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    long t = tok0 + j;
+    t = t < T0 ? t : (T0 > 0 ? T0 - 1 : 0);  // clamp into written tokens; unused past np
+    const size_t off = (size_t)t * D + lane * VPL;
+    fk[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(kc + off) : (uint32_t)kc[off];
+    fv[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(vc + off) : (uint32_t)vc[off];
+  }
+  const size_t noff = (size_t)unit * D + lane * VPL;
+  const uint32_t nkw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_k + noff) : (uint32_t)a.new_k[noff];
+  const uint32_t nvw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_v + noff) : (uint32_t)a.new_v[noff];
+  float fq[G][VPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) fq[g][e] = a.q[((size_t)unit * G + g) * D + lane * VPL + e];
+
+  float km[VPL], kvr[VPL], vm[VPL];
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) {
+    float kx[16], vx[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t wk = j < np ? fk[j] : nkw;
+      const uint32_t wv = j < np ? fv[j] : nvw;
+      kx[j] = e == 0 ? bf16_lo(wk) : bf16_hi(wk);
+      vx[j] = e == 0 ? bf16_lo(wv) : bf16_hi(wv);
+    }
+    float vvar;
+    mean_var16(kx, n, km[e], kvr[e]);
+    mean_var16(vx, n, vm[e], vvar);
+  }
+  // D̄: mean coordinate variance of each group of gs = D/r coordinates,
+  // summed as a pairwise tree (the order of the summary kernels)
+  const int gs = D / a.r;
+  float dl[VPL];
+  if (gs >= VPL) {
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) part += kvr[e];
+    for (int o = 1; o < gs / VPL; o <<= 1) part += __shfl_xor(part, o);
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) dl[e] = part / (float)gs;
+  } else {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) dl[e] = kvr[e];
+  }
+  const float half = (a.flags & CKNV_FLAG_FIRST_ORDER_MASS) ? 0.f : 0.5f;
+  const bool mass_only = (a.flags & CKNV_FLAG_MASS_ONLY_SCORE) != 0;
+  float2 info = make_float2(-INFINITY, 0.f);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float zp = 0.f, sp = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) {
+      zp += fq[g][e] * km[e];
+      sp += fq[g][e] * fq[g][e] * dl[e];
+    }
+    const float z = group_sum<64>(zp) * a.isd;
+    const float s2 = group_sum<64>(sp) / (float)D;
+    if (lane == g) info = make_float2(__logf((float)n) + z + half * s2, mass_only ? 1.f : s2);
+  }
+  // every store after the last load
+  if (lane < G) fi[lane] = info;
+  const size_t toff = (size_t)T0 * D + lane * VPL;
+  const size_t row = (size_t)unit * a.cap_blocks + fblk;
+  if (VPL == 2) {
+    *reinterpret_cast<uint32_t*>(kc + toff) = nkw;
+    *reinterpret_cast<uint32_t*>(vc + toff) = nvw;
+  } else {
+    kc[toff] = (uint16_t)nkw;
+    vc[toff] = (uint16_t)nvw;
+  }
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) {
+    a.kbar[row * D + lane * VPL + e] = km[e];
+    a.vbar[row * D + lane * VPL + e] = vm[e];
+  }
+  if (gs >= VPL) {
+    if ((lane * VPL) % gs == 0) a.dbar[row * a.r + (lane * VPL) / gs] = dl[0];
+  } else {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) a.dbar[row * a.r + lane * VPL + e] = dl[e];
+  }
+  if (lane == 0) a.cnt[row] = (float)n;
+  if (h == 0 && lane == 0) a.t0_out[s] = T0;
+}
+
 // NC: the no-compensation ablation; the mean values are neither read nor summed.
 template <int D, int G, int DM, int ROWS, bool NC>
-__global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   constexpr int KC = D / 64;              // float4 chunks per lane per block (16 lanes per block)
   constexpr int E = 4 * KC;               // coordinates per lane
   // ROWS: blocks per lane, base + 4*row + (lane >> 4)
   constexpr int NP = ROWS * G;            // (row, head) pairs of a 16-lane row
-  constexpr int BPW = 4 * ROWS, BPWG = kWaves * BPW;
+  constexpr int BPW = 4 * ROWS, BPWG = kScoreWaves * BPW;
   constexpr int W = rec_words(D);
   constexpr int NA = G * E;               // compensation sums per lane before the cross-row step
-  __shared__ __align__(16) float cacc[kWaves * G * D];  // per-wave compensation sums
-  __shared__ float cml[kWaves * G * 2];                 // per-wave (max, normaliser)
+  __shared__ __align__(16) float cacc[kScoreWaves * G * D];  // per-wave compensation sums
+  __shared__ float cml[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of z̄
+  __shared__ float cma[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of a
 
+  if ((int)blockIdx.x < a.nfresh) {
+    fresh_block<D, G>(a, blockIdx.x);
+    return;
+  }
   int unit, chunk;
-  map_wg(blockIdx.x, a.S * a.H, a.C, a.xcd, unit, chunk);
+  map_wg(blockIdx.x - a.nfresh, a.S * a.H, a.C, a.xcd, unit, chunk);
   const int s = unit / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bg = lane >> 4, j = lane & 15;
@@ -164,7 +291,6 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   // Block indices are clamped into [0, MB); blocks past the scored range are
   // masked once seq_len has arrived.
   const int T = a.seq_len[s];
-  if (a.t0_out && unit == s * a.H && chunk == 0 && tid == 0) a.t0_out[s] = T;
   float4 qv[G][KC];
   {
     const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D);
@@ -222,18 +348,36 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
   // ---- scoring partials of this wave's group: a = ln|b| + z̄ + σ̂²/2, and
   // u = e^{a - group max} σ̂². The first-order-mass ablation drops σ̂²/2 from a,
   // the mass-only ablation drops the factor σ̂² from u.
+  const float half = (a.flags & CKNV_FLAG_FIRST_ORDER_MASS) ? 0.f : 0.5f;
+  const float av = tv ? __logf(n) + z + half * s2 : -INFINITY;
+  const float aref = rows_max(seg_max<ROWS>(av));
+  const float ae = tv ? __expf(av - aref) : 0.f;
+  const float al = rows_sum(seg_sum<ROWS>(ae));
   {
-    const float half = (a.flags & CKNV_FLAG_FIRST_ORDER_MASS) ? 0.f : 0.5f;
-    const float av = tv ? __logf(n) + z + half * s2 : -INFINITY;
-    const float ref = rows_max(seg_max<ROWS>(av));
-    const float e = tv ? __expf(av - ref) : 0.f;
-    const float l = rows_sum(seg_sum<ROWS>(e));
     const float uf = (a.flags & CKNV_FLAG_MASS_ONLY_SCORE) ? 1.f : s2;
-    if (tv) a.u[((size_t)unit * MB + tb) * G + tg] = e * uf;
+    if (tv) a.u[((size_t)unit * MB + tb) * G + tg] = ae * uf;
     if (base < NB && lane < NP && trow == 0)
-      reinterpret_cast<float2*>(a.grp)[((size_t)unit * a.NG + base / BPW) * G + tg] = make_float2(ref, l);
+      reinterpret_cast<float2*>(a.grp)[((size_t)unit * a.NG + base / BPW) * G + tg] = make_float2(aref, al);
   }
-  if constexpr (NC) return;
+  const bool head_lane = bg == 0 && lane < NP && trow == 0;  // one lane per query head tg
+  if (head_lane) {
+    cma[(wave * G + tg) * 2] = aref;
+    cma[(wave * G + tg) * 2 + 1] = al;
+  }
+  if constexpr (NC) {
+    // no compensation: the record carries only the chunk's LSE partial of a
+    lds_barrier();
+    if (tid < G) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kScoreWaves; ++q) M = fmaxf(M, cma[(q * G + tid) * 2]);
+      float L = 0.f;
+#pragma unroll
+      for (int q = 0; q < kScoreWaves; ++q) L += cma[(q * G + tid) * 2 + 1] * rescale(cma[(q * G + tid) * 2], M);
+      reinterpret_cast<float2*>(a.hdr)[((size_t)unit * a.C + chunk) * G + tid] = make_float2(M, L);
+    }
+    return;
+  }
 
   // ---- Mean compensation of every block of the wave (kept ones are removed later)
   const float mz = rows_max(seg_max<ROWS>(tv ? z : -INFINITY));
@@ -286,28 +430,28 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
       const int v = v0 + m, g = v / E, e = v % E;
       cw[g * D + 4 * (j + 16 * (e / 4)) + (e % 4)] = y[m];
     }
-    if (bg == 0 && lane < NP && trow == 0) {
+    if (head_lane) {
       cml[(wave * G + tg) * 2] = mz;
       cml[(wave * G + tg) * 2 + 1] = lz;
     }
   }
   lds_barrier();
   // ---- the workgroup's record: the waves' sums under their common max
-  constexpr int CPT = (G * D + kThreads - 1) / kThreads;  // coordinates per thread (1, 2 or 4)
+  constexpr int CPT = (G * D + kScoreThreads - 1) / kScoreThreads;  // coordinates per thread (1, 2 or 4)
   const int f0 = tid * CPT;
   if (f0 < G * D) {
     const int g = f0 / D, c0 = f0 - g * D;
-    float mw[kWaves], M = -INFINITY;
+    float mw[kScoreWaves], M = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q) { mw[q] = cml[(q * G + g) * 2]; M = fmaxf(M, mw[q]); }
-    float sc[kWaves];
+    for (int q = 0; q < kScoreWaves; ++q) { mw[q] = cml[(q * G + g) * 2]; M = fmaxf(M, mw[q]); }
+    float sc[kScoreWaves];
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q) sc[q] = rescale(mw[q], M);
+    for (int q = 0; q < kScoreWaves; ++q) sc[q] = rescale(mw[q], M);
     float acc[CPT];
 #pragma unroll
     for (int e = 0; e < CPT; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q)
+    for (int q = 0; q < kScoreWaves; ++q)
 #pragma unroll
       for (int e = 0; e < CPT; ++e) acc[e] += cacc[(q * G + g) * D + c0 + e] * sc[q];
     float* co = a.comp + (((size_t)unit * a.C + chunk) * G + g) * W;
@@ -316,11 +460,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs a) {
     if (c0 == 0) {
       float l = 0.f;
 #pragma unroll
-      for (int q = 0; q < kWaves; ++q) l += cml[(q * G + g) * 2 + 1] * sc[q];
-      co[0] = M;
-      co[1] = l;
-      co[2] = 0.f;
-      co[3] = 0.f;
+      for (int q = 0; q < kScoreWaves; ++q) l += cml[(q * G + g) * 2 + 1] * sc[q];
+      float Ma = -INFINITY, La = 0.f;
+#pragma unroll
+      for (int q = 0; q < kScoreWaves; ++q) Ma = fmaxf(Ma, cma[(q * G + g) * 2]);
+#pragma unroll
+      for (int q = 0; q < kScoreWaves; ++q) La += cma[(q * G + g) * 2 + 1] * rescale(cma[(q * G + g) * 2], Ma);
+      *reinterpret_cast<float2*>(co) = make_float2(M, l);
+      reinterpret_cast<float2*>(a.hdr)[((size_t)unit * a.C + chunk) * G + g] = make_float2(Ma, La);
     }
   }
 }
@@ -346,7 +493,7 @@ hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st)
 #undef CKNV_SCORE_R
 #undef CKNV_SCORE_NC
   if (!f) return hipErrorInvalidValue;
-  return hipLaunchKernel(f, dim3(U * a.C), dim3(kThreads), args, 0, st);
+  return hipLaunchKernel(f, dim3(a.nfresh + U * a.C), dim3(kScoreThreads), args, 0, st);
 }
 
 }  // namespace cknv

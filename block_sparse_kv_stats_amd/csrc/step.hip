@@ -1,10 +1,8 @@
-// The fused decode step after the scoring pass: append, selection and
+// The fused decode step after the scoring pass: normalisers, selection and
 // attention of one unit in one workgroup (or in P workgroups that each
 // attend a slice of the kept list, merged by step_merge_kernel).
 //
 // CompKV page (onedev.kr/papers/157):
-//   "How to use it" -- every step stores the new token and refreshes the
-//     statistics of the block it lands in;
 //   "What differs"  -- p̂ is normalised over all blocks, S_b = sum_g p̂ σ̂²;
 //     the first block and the two most recent blocks are always kept and
 //     count against the budget, the rest of the budget goes to the largest
@@ -13,32 +11,32 @@
 //     every other block its Mean compensation |b| e^{z̄} (1, v̄), all under
 //     one normaliser.
 //
-// Inputs from the scoring pass (score_kernel with closed_only = 1), which
-// covered the NBa = T0/16 blocks that were closed before this step (T0 =
-// tokens before the step): per score group the (max, sum) of
-// a = ln|b| + z̄ + σ̂²/2, per block u_{g,b} = exp(a - group max) σ̂², per
-// chunk the Mean-compensation sums of all its blocks, and T0 per sequence.
-// The block the new token lands in (the fresh block, index T0/16) is not in
-// any of them: this kernel computes its summary from its tokens, folds its
-// a into the normalisers, and never removes compensation for it.
+// Inputs from the scoring pass (score_kernel in fused mode). It appended the
+// step's token, summarised the block the token lands in (the fresh block,
+// index T0/16, T0 = tokens before the step) and wrote that block's a and
+// factor per query head (finfo). It covered the NBa = T0/16 blocks closed
+// before the step: per score group the (max, sum) of a = ln|b| + z̄ + σ̂²/2,
+// per block u_{g,b} = exp(a - group max) σ̂², per chunk the Mean-compensation
+// sums of all its blocks and the chunk's (max, sum) of a, and T0 per
+// sequence. The fresh block is in none of the sums: it is always kept.
 //
 // Phases of a workgroup (NT threads; thread t owns blocks t + NT*j of the
 // unit):
-//   loads      score-group partials, the thread's u terms, the query, and
-//              (last wave) the fresh block's tokens;
-//   fresh      last wave: summary of the fresh block, its a and σ̂²; part 0
-//              writes the token and the summary to the cache;
-//   LSE        per query head over all blocks;
+//   loads      T0, finfo, the chunk headers, the thread's score groups and
+//              u terms, the query, the wave's first chunk records;
+//   LSE        every wave reduces the chunk headers and the fresh block's a
+//              itself (the same bits in every wave); factors
+//              e^{group max - LSE} of the thread's score groups to LDS; the
+//              wave folds its first chunk records;
 //   keys       S_b per block (fp32 bits order like the values, S_b >= 0);
 //              scores; 2048-bin histogram of the candidates' top 11 bits;
 //   select     the bin holding the (Kb-3)-th largest candidate key; keys
 //              in that bin are ranked exactly (or, for long runs of equal
 //              keys, pinned by two more radix passes, ties by index);
 //   compact    kept blocks in ascending order -> sel, and this part's slice;
-//   attend     the first KPART waves: one kept block of this part's slice
-//              each (exact terms minus its compensation); every wave: its
-//              share of this part's chunk records of the scoring pass (the
-//              first one loaded with the other inputs);
+//   attend     wave w: kept blocks w + NW*i (i < KPW) of this part's slice
+//              (exact terms minus their compensation), then the rest of its
+//              share of this part's chunk records;
 //   merge      the waves' records -> out, lse (P == 1) or a part record.
 #include "attend_core.h"
 #include "select_core.h"
@@ -48,18 +46,55 @@ namespace cknv {
 
 namespace {
 
-template <int G, int KPTB>
+template <int D, int G, int KPTB>
 struct StepCfg {
   static constexpr int NT = kStepThreads;
-  static constexpr int NW = NT / 64;
+  static constexpr int NW = kStepWaves;
   static constexpr int KPT = KPTB;                                 // blocks per thread
   static constexpr int NGMAX = (NT * KPT + kScoreMinGroup - 1) / kScoreMinGroup;  // score groups, at most
   static constexpr int GPT = (NGMAX + NT - 1) / NT;                // score groups per thread
-  static constexpr int UB = KPT < 128 / G ? KPT : 128 / G;         // blocks per u load batch
+  static constexpr int UMAX = G >= 8 ? 64 / G : 128 / G;
+  static constexpr int UB = KPT < UMAX ? KPT : UMAX;               // blocks per u load batch
   static constexpr int NBATCH = (KPT + UB - 1) / UB;
-  static constexpr int KPART = kStepKeptPerPart;                   // kept blocks per workgroup
-  static constexpr int RPW = 2;                                    // records per wave per batch
-  static_assert(KPART <= NW, "one kept block per attending wave");
+  static constexpr int KPW = step_kept_per_wave(G);                // kept blocks per wave
+  static constexpr int KPART = step_kept_per_part(G);              // kept blocks per workgroup
+  static constexpr int CPL = step_chunks_per_lane(KPTB);           // chunk headers per lane
+  // Chunk records per wave loaded with the inputs (what the registers left
+  // by the other inputs hold, 1..8), and per later batch (after the tiles).
+  static constexpr int RWORDS = G * (2 + D / 64);
+  static constexpr int RBUDGET = 176 - UB * G - 2 * GPT * G - 2 * CPL * G;
+  static constexpr int RPF = RBUDGET / RWORDS < 1 ? 1 : (RBUDGET / RWORDS > 8 ? 8 : RBUDGET / RWORDS);
+  static constexpr int RPW = 32 / RWORDS < 1 ? 1 : (32 / RWORDS > 4 ? 4 : 32 / RWORDS);
+  static constexpr int AW = kStepAttendWaves;                      // attending waves
+  static_assert(KPART == AW * KPW && AW <= NW, "kept slice of a workgroup");
+};
+
+// The lane's part of one chunk record of the scoring pass: (m, l) and the
+// lane's value coordinates per query head; an empty record when !valid.
+// `valid` is wave-uniform: an empty record issues no load.
+template <int D, int G>
+struct RecordRegs {
+  float m[G], l[G], acc[G][D / 64];
+  __device__ __forceinline__ void load(const float* rp, bool valid, int lane) {
+    constexpr int W = rec_words(D), VPL = D / 64;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) acc[g][e] = 0.f;
+    }
+    if (valid) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float2 ml = *reinterpret_cast<const float2*>(rp + g * W);
+        m[g] = ml.x;
+        l[g] = ml.y;
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) acc[g][e] = rp[g * W + 4 + lane * VPL + e];
+      }
+    }
+  }
 };
 
 // out[g][c] = sum_i rec_i[g][c] e^{m_i - M} / L (and lse = M + ln L) over n
@@ -87,31 +122,48 @@ __device__ __forceinline__ void finalize_records(const float* recs, int n, float
   }
 }
 
+// Keep a wave state in registers at this point: the compiler may not move
+// the arithmetic that produced it past here.
+template <int D, int G>
+__device__ __forceinline__ void pin_state(WaveState<D, G>& st) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    asm volatile("" : "+v"(st.m[g]), "+v"(st.l[g]));
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) asm volatile("" : "+v"(st.acc[g][e]));
+  }
+}
+
 // Fold one compensation record (this lane's coordinates) into a wave state.
 template <int D, int G>
-__device__ __forceinline__ void fold_record(WaveState<D, G>& st, const float (&rm)[G], const float (&rl)[G],
-                                            const float (&racc)[G][D / 64]) {
+__device__ __forceinline__ void fold_record(WaveState<D, G>& st, const RecordRegs<D, G>& r) {
   constexpr int VPL = D / 64;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float M = fmaxf(st.m[g], rm[g]);
-    const float a = rescale(st.m[g], M), b = rescale(rm[g], M);
+    const float M = fmaxf(st.m[g], r.m[g]);
+    const float a = rescale(st.m[g], M), b = rescale(r.m[g], M);
     st.m[g] = M;
-    st.l[g] = st.l[g] * a + rl[g] * b;
+    st.l[g] = st.l[g] * a + r.l[g] * b;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) st.acc[g][e] = st.acc[g][e] * a + racc[g][e] * b;
+    for (int e = 0; e < VPL; ++e) st.acc[g][e] = st.acc[g][e] * a + r.acc[g][e] * b;
   }
 }
 
 }  // namespace
 
+// A sequence appends (and its seq_len advances) when its cache has room and
+// the block the token lands in lies below max_blocks.
+__device__ __forceinline__ bool step_appends(int T0, int cap_blocks, int max_blocks) {
+  return T0 < (long)cap_blocks * kBlock && T0 / kBlock < max_blocks;
+}
+
 template <int D, int G, int KPTB>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
-  using C = StepCfg<G, KPTB>;
+  using C = StepCfg<D, G, KPTB>;
   constexpr int NT = C::NT, NW = C::NW, KPT = C::KPT, UB = C::UB;
-  constexpr int GPT = C::GPT, NGMAX = C::NGMAX, KPART = C::KPART, RPW = C::RPW;
-  constexpr int W = rec_words(D), VPL = D / 64;
-  constexpr int OW = NW - 1;  // the wave that refreshes the fresh block
+  constexpr int GPT = C::GPT, NGMAX = C::NGMAX, KPW = C::KPW, KPART = C::KPART, AW = C::AW;
+  constexpr int CPL = C::CPL, RPF = C::RPF, RPW = C::RPW;
+  constexpr int W = rec_words(D);
   // LDS: area A holds the score-group factors during the keys, then the
   // query and the waves' attention records; area B the selection scratch.
   constexpr int NBITS = (KPT * NT + 31) / 32;  // kept-block bitmap of the pivot-bin path
@@ -122,9 +174,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   __shared__ int lidx[kListMax];
   __shared__ uint32_t keep_bits[NBITS];
   __shared__ int cnt[KPT * NW + 1];
-  __shared__ float red[NW * G * 2];
   __shared__ float scl[NW * G + 2 * G];
-  __shared__ float oinfo[2 * G];  // fresh block: a_g, σ̂²_g
   __shared__ int ctl[8];
   __shared__ int klist[KPART];
   float* fgrp = areaA;                   // [NGMAX][G] exp(group max - LSE_g)
@@ -135,19 +185,36 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   const int unit = blockIdx.x / P, p = blockIdx.x - unit * P;
   const int s = unit / a.H, h = unit - s * a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int MB = a.max_blocks, Kb = a.Kb;
+  const int MB = a.max_blocks, Kb = a.Kb, NC = a.C;
   const long cap_tok = (long)a.cap_blocks * kBlock;
   const size_t ubase = (size_t)unit * a.cap_blocks;
-  uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
-  uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
+  const uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
+  const uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
   const float* u = a.u + (size_t)unit * MB * G;
   const float2* grp = reinterpret_cast<const float2*>(a.grp) + (size_t)unit * a.NG * G;
+  const float* crec = a.comp + (size_t)unit * NC * G * W;
   const int NG = a.NG;
+  // The no-compensation ablation has no records: folds see empty ones.
+  const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
   // thread tid owns blocks tid + NT*j, j < KPT (NT*KPT >= MB), and score
   // groups tid + NT*k, k < GPT
 
   // ================================================================ loads
   const int T0 = a.t0[s];
+  float2 fi[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) fi[g] = reinterpret_cast<const float2*>(a.finfo)[(size_t)unit * G + g];
+  float2 hd[CPL][G];  // chunk lane + 64k: (max, sum) of a
+  {
+    const float2* hp = reinterpret_cast<const float2*>(a.hdr) + (size_t)unit * NC * G;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = lane + 64 * k;
+      const int cc = c < NC ? c : NC - 1;
+#pragma unroll
+      for (int g = 0; g < G; ++g) hd[k][g] = hp[(size_t)cc * G + g];
+    }
+  }
   float2 gp[GPT][G];
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
@@ -171,57 +238,25 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     const int i = tid + k * NT;
     q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
   }
-  // This wave's first chunk record of the scoring pass (this part's share),
-  // folded in the attend phase; it does not depend on the selection.
-  const int c0 = (int)((long)p * a.C / P), c1 = (int)((long)(p + 1) * a.C / P);
-  const float* crec = a.comp + (size_t)unit * a.C * G * W;
-  // The no-compensation ablation has no records: the fold sees an empty one.
-  const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
-  float pm[G], pl[G], pacc[G][VPL];
-  {
-    const int c = c0 + wave;
-    const int cc = c < c1 ? c : (c1 > 0 ? c1 - 1 : 0);
-    const float* rp = crec + (size_t)cc * G * W;
+  // This part's chunk records: wave w folds records c0 + w + NW*i. The
+  // first RPF are loaded now; they do not depend on the selection.
+  const int c0 = (int)((long)p * NC / P), c1 = (int)((long)(p + 1) * NC / P);
+  const int clast = c1 > 0 ? c1 - 1 : 0;
+  RecordRegs<D, G> rf[RPF];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float2 ml = *reinterpret_cast<const float2*>(rp + g * W);
-      pm[g] = (c < c1 && !nc) ? ml.x : -INFINITY;
-      pl[g] = nc ? 0.f : ml.y;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) pacc[g][e] = nc ? 0.f : rp[g * W + 4 + lane * VPL + e];
-    }
-  }
-  // Fresh-block tokens (wave OW): np = T0 % 16 cached tokens plus the new one.
-  const int fblk = T0 / kBlock;
-  const long ftok0 = (long)fblk * kBlock;
-  uint32_t fk[16], fv[16], nkw = 0u, nvw = 0u;
-  float fq[G][VPL];
-  if (wave == OW) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      long t = ftok0 + j;
-      t = t < T0 ? t : (T0 > 0 ? T0 - 1 : 0);  // clamp into written tokens
-      const size_t off = (size_t)t * D + lane * VPL;
-      fk[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(kc + off) : (uint32_t)kc[off];
-      fv[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(vc + off) : (uint32_t)vc[off];
-    }
-    const size_t noff = (size_t)unit * D + lane * VPL;
-    nkw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_k + noff) : (uint32_t)a.new_k[noff];
-    nvw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_v + noff) : (uint32_t)a.new_v[noff];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) fq[g][e] = a.q[((size_t)unit * G + g) * D + lane * VPL + e];
+  for (int i = 0; i < RPF; ++i) {
+    const int c = c0 + wave + NW * i;
+    rf[i].load(crec + (size_t)(c < c1 ? c : clast) * G * W, c < c1 && !nc, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const bool room = T0 < cap_tok;
-  const int T = T0 + (room ? 1 : 0);
+  const bool app = step_appends(T0, a.cap_blocks, MB);
+  const int T = T0 + (app ? 1 : 0);
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < MB ? NB : MB;
   int NBa = T0 / kBlock;
   NBa = NBa < MB ? NBa : MB;
-  const int fb = (room && fblk < MB) ? fblk : -1;  // fresh block (always the last block)
+  const int fb = app ? T0 / kBlock : -1;  // fresh block (always the last block)
   const int gsh = a.bpw_shift;  // score group = 1 << gsh blocks
   const int NGa = (NBa + (1 << gsh) - 1) >> gsh;
   const bool all = NB <= Kb;
@@ -231,111 +266,22 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   for (int i = tid; i < NBITS; i += NT) keep_bits[i] = 0u;
   if (tid == 0) ctl[3] = 0;
 
-  // ================================================================ fresh block
-  if (wave == OW && fb >= 0) {
-    const int np = T0 - fblk * kBlock;  // cached tokens of the block, 0..15
-    const int n = np + 1;
-    float km[VPL], kvr[VPL], vm[VPL];
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) {
-      float kx[16], vx[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t wk = j < np ? fk[j] : nkw;
-        const uint32_t wv = j < np ? fv[j] : nvw;
-        kx[j] = e == 0 ? bf16_lo(wk) : bf16_hi(wk);
-        vx[j] = e == 0 ? bf16_lo(wv) : bf16_hi(wv);
-      }
-      float vvar;
-      mean_var16(kx, n, km[e], kvr[e]);
-      mean_var16(vx, n, vm[e], vvar);
-    }
-    // D̄: mean coordinate variance of each contiguous group of gs = D/r
-    // coordinates, summed as a pairwise tree (the order of the summary kernels)
-    const int gs = D / a.r;
-    float dl[VPL];
-    if (gs >= VPL) {
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) part += kvr[e];
-      for (int o = 1; o < gs / VPL; o <<= 1) part += __shfl_xor(part, o);
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) dl[e] = part / (float)gs;
-    } else {
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) dl[e] = kvr[e];
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float zp = 0.f, sp = 0.f;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) {
-        zp += fq[g][e] * km[e];
-        sp += fq[g][e] * fq[g][e] * dl[e];
-      }
-      const float z = group_sum<64>(zp) * a.isd;
-      const float s2 = group_sum<64>(sp) / (float)D;
-      if (lane == 0) {
-        // a and the factor of p̂ in S_b, with the ablations' switches
-        const float half = (a.flags & CKNV_FLAG_FIRST_ORDER_MASS) ? 0.f : 0.5f;
-        oinfo[g] = __logf((float)n) + z + half * s2;
-        oinfo[G + g] = (a.flags & CKNV_FLAG_MASS_ONLY_SCORE) ? 1.f : s2;
-      }
-    }
-    if (p == 0) {
-      const size_t toff = (size_t)T0 * D + lane * VPL;
-      const size_t row = ubase + fblk;
-      if (VPL == 2) {
-        *reinterpret_cast<uint32_t*>(kc + toff) = nkw;
-        *reinterpret_cast<uint32_t*>(vc + toff) = nvw;
-      } else {
-        kc[toff] = (uint16_t)nkw;
-        vc[toff] = (uint16_t)nvw;
-      }
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) {
-        a.kbar[row * D + lane * VPL + e] = km[e];
-        a.vbar[row * D + lane * VPL + e] = vm[e];
-      }
-      if (gs >= VPL) {
-        if ((lane * VPL) % gs == 0) a.dbar[row * a.r + (lane * VPL) / gs] = dl[0];
-      } else {
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) a.dbar[row * a.r + lane * VPL + e] = dl[e];
-      }
-      if (lane == 0) a.cnt[row] = (float)n;
-    }
-  }
-
   // ================================================================ LSE
+  float lse_g[G], fa[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float r = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < GPT; ++k) r = fmaxf(r, tid + k * NT < NGa ? gp[k][g].x : -INFINITY);
+    for (int k = 0; k < CPL; ++k) r = fmaxf(r, lane + 64 * k < NC ? hd[k][g].x : -INFINITY);
     const float Mw = group_max<64>(r);
     float l = 0.f;
 #pragma unroll
-    for (int k = 0; k < GPT; ++k) l += tid + k * NT < NGa ? gp[k][g].y * rescale(gp[k][g].x, Mw) : 0.f;
+    for (int k = 0; k < CPL; ++k) l += lane + 64 * k < NC ? hd[k][g].y * rescale(hd[k][g].x, Mw) : 0.f;
     const float Lw = group_sum<64>(l);
-    if (lane == 0) {
-      red[(wave * G + g) * 2] = Mw;
-      red[(wave * G + g) * 2 + 1] = Lw;
-    }
-  }
-  lds_barrier();
-  float lse_g[G], fa[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float fa_g = fb >= 0 ? oinfo[g] : -INFINITY;
-    float M = fa_g;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[(w * G + g) * 2]);
-    float L = rescale(fa_g, M);
-#pragma unroll
-    for (int w = 0; w < NW; ++w) L += red[(w * G + g) * 2 + 1] * rescale(red[(w * G + g) * 2], M);
+    fa[g] = fb >= 0 ? fi[g].x : -INFINITY;
+    const float M = fmaxf(Mw, fa[g]);
+    const float L = Lw * rescale(Mw, M) + rescale(fa[g], M);
     lse_g[g] = L > 0.f ? M + __logf(L) : INFINITY;
-    fa[g] = fa_g;
   }
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
@@ -345,6 +291,12 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       for (int g = 0; g < G; ++g) fgrp[gi * G + g] = __expf(gp[k][g].x - lse_g[g]);
     }
   }
+  WaveState<D, G> st;
+  st.init();
+#pragma unroll
+  for (int i = 0; i < RPF; ++i)
+    if (c0 + wave + NW * i < c1 && !nc) fold_record<D, G>(st, rf[i]);  // wave-uniform
+  pin_state(st);  // fold here: the records' registers die before the selection
   lds_barrier();
 
   // ================================================================ keys
@@ -354,7 +306,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   float Sfresh = 0.f;
   if (fb >= 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) Sfresh += __expf(fa[g] - lse_g[g]) * oinfo[G + g];
+    for (int g = 0; g < G; ++g) Sfresh += __expf(fa[g] - lse_g[g]) * fi[g].y;
   }
   uint32_t key[KPT];
   uint64_t candm = 0u;  // bit j: block tid + NT*j is a Top-K candidate
@@ -532,52 +484,43 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   lds_barrier();
 
   // ================================================================ attend
-  // Wave w: kept block lo + w of this part's slice (exact terms, minus its
-  // compensation if the scoring pass counted it), then its share of this
-  // part's chunk records of the scoring pass.
-  WaveState<D, G> st;
-  st.init();
-  fold_record<D, G>(st, pm, pl, pacc);
-  if (wave < KPART) {
-    const int e = lo + wave;
-    const int b = e < nk ? klist[wave] : -1;
-    if (b >= 0) {
-      Tile<D> tile;
-      BlockMean<D> bm;
-      if (b == fb) {
-        tile.load_fresh(kc, vc, (long)b * kBlock, T0 - b * kBlock, a.new_k + (size_t)unit * D,
-                        a.new_v + (size_t)unit * D, lane);
-        absorb<D, G, false>(st, tile, bm, q_l, lane, a.isd);
-      } else {
-        tile.load(kc, vc, (long)b * kBlock, (long)T0, lane);
-        bm.load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
-        if (b < NBa && !nc)
-          absorb<D, G, true>(st, tile, bm, q_l, lane, a.isd);
-        else
-          absorb<D, G, false>(st, tile, bm, q_l, lane, a.isd);
-      }
+  // Wave w < AW: kept blocks lo + w + AW*i of this part's slice (exact terms,
+  // minus their compensation where the scoring pass counted them); every
+  // tile is loaded before the first is absorbed.
+  if (wave < AW) {
+    int bk[KPW];
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int e = lo + wave + AW * i;
+      bk[i] = e < nk ? klist[wave + AW * i] : -1;
     }
+    Tile<D> tile[KPW];
+    BlockMean<D> bm[KPW];
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      const int b = bk[i] >= 0 ? bk[i] : 0;
+      tile[i].load(kc, vc, (long)b * kBlock, bk[i] >= 0 ? (long)T : 0, lane);
+      bm[i].load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
+      // one code path: a block whose compensation the scoring pass did not
+      // count removes a zero-mass term (its z̄ never exceeds its largest logit)
+      if (!(bk[i] >= 0 && bk[i] < NBa && !nc)) bm[i].n = 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every tile load issued before the first use
+    // an empty slot (bk < 0) holds no valid token and n = 0: it adds nothing
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
   }
-  if (!nc) {
-    for (int cb = c0 + wave + NW; cb < c1; cb += RPW * NW) {
-      float rm[RPW][G], rl[RPW][G], racc[RPW][G][VPL];
+  // Records past the first RPF of the wave (more than the registers hold
+  // with the inputs): RPW per round trip.
+  for (int cb = c0 + wave + NW * RPF; cb < c1 && !nc; cb += NW * RPW) {
+    RecordRegs<D, G> rb[RPW];
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int c = cb + i * NW;
-        const int cc = c < c1 ? c : c1 - 1;
-        const float* rp = crec + (size_t)cc * G * W;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float2 ml = *reinterpret_cast<const float2*>(rp + g * W);
-          rm[i][g] = c < c1 ? ml.x : -INFINITY;
-          rl[i][g] = ml.y;
-#pragma unroll
-          for (int e = 0; e < VPL; ++e) racc[i][g][e] = rp[g * W + 4 + lane * VPL + e];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) fold_record<D, G>(st, rm[i], rl[i], racc[i]);
+    for (int i = 0; i < RPW; ++i) {
+      const int c = cb + NW * i;
+      rb[i].load(crec + (size_t)(c < c1 ? c : clast) * G * W, c < c1, lane);
     }
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) fold_record<D, G>(st, rb[i]);
   }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
   lds_barrier();
@@ -586,7 +529,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   if (P == 1) {
     finalize_records<D, G, NT>(recs, NW, a.out + (size_t)unit * G * D,
                                a.lse ? a.lse + (size_t)unit * G : nullptr, scl);
-    if (h == 0 && tid == 0 && room) a.seq_len[s] = T;
+    if (h == 0 && tid == 0 && app) a.seq_len[s] = T;
   } else {
     merge_records<D, G, NT>(recs, NW, a.part + ((size_t)unit * P + p) * G * W, scl);
   }
@@ -654,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void step_merge_kernel(StepArgs a) {
   }
   if (h == 0 && tid == 0) {
     const int T0 = a.t0[s];
-    if (T0 < (long)a.cap_blocks * kBlock) a.seq_len[s] = T0 + 1;
+    if (step_appends(T0, a.cap_blocks, a.max_blocks)) a.seq_len[s] = T0 + 1;
   }
 }
 
@@ -675,6 +618,7 @@ hipError_t launch_step(int d, int G, const StepArgs& a, int U, hipStream_t st) {
 #undef CKNV_STEP_CASE
 #undef CKNV_STEP_K
   if (!f || !m) return hipErrorInvalidValue;
+  if (a.C > 64 * step_chunks_per_lane(kptb)) return hipErrorInvalidValue;  // chunk headers per lane
   hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(kStepThreads), args, 0, st);
   if (e != hipSuccess || a.P == 1) return e;
   return hipLaunchKernel(m, dim3(U), dim3(kThreads), args, 0, st);

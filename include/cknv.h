@@ -163,15 +163,16 @@ int cknv_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q
                 void* stream);
 
 /* One whole decode step, fused: the same results as cknv_append, then
- * cknv_score_select, then cknv_attend on the same arguments, in two or three
- * kernel launches instead of five or six.
+ * cknv_score_select, then cknv_attend on the same arguments, in two kernel
+ * launches (three when the budget exceeds 512 tokens) instead of five or six.
  *   - new_k, new_v: bfloat16 [S][H][d], the step's token ("How to use it":
  *     the new K/V are stored and the current block's statistics refreshed);
  *   - q, budget_tokens, scores, sel, n_sel: as for cknv_score_select, with
  *     NB counted after the append; out, lse: as for cknv_attend.
  * max_blocks bounds NB after the append. seq_len[s] advances by one for
  * every sequence whose cache has room (a full cache is left unchanged and
- * the step attends its existing tokens). The workspace regions are those of
+ * the step attends its existing tokens; so is a sequence whose token would
+ * land at or past block max_blocks, which breaks the bound). The workspace regions are those of
  * cknv_score_select / cknv_attend plus the step's own. */
 int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
                      const uint16_t* new_v, const float* q, int32_t budget_tokens,
@@ -179,22 +180,24 @@ int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uin
                      float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* The two halves of cknv_decode_step, for callers that schedule them apart
- * (same arguments; call them in this order on one workspace, with nothing
- * that changes the cache or seq_len in between):
- *   cknv_decode_score   the streaming pass over the summaries of the blocks
- *                       that were closed before the step's token (scores'
- *                       ingredients and the Mean-compensation sums of every
- *                       one of them); records seq_len in the workspace;
- *   cknv_decode_finish  the append and the refresh of the block the token
- *                       lands in, the normalisers, the selection, and the
- *                       attention with compensation; advances seq_len. */
-int cknv_decode_score(const cknv_shape* shape, const cknv_cache* cache, const float* q,
-                      int32_t budget_tokens, int32_t max_blocks, void* ws, size_t ws_bytes,
-                      void* stream);
-int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
-                       const uint16_t* new_v, const float* q, int32_t budget_tokens,
-                       int32_t max_blocks, float* scores, int32_t* sel, int32_t* n_sel,
-                       float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+ * (call them in this order on one workspace, with nothing that changes the
+ * cache or seq_len in between):
+ *   cknv_decode_score   the append of the step's token and the summary of
+ *                       the block it lands in, and the streaming pass over
+ *                       the summaries of the blocks closed before the token
+ *                       (scores' ingredients and the Mean-compensation sums
+ *                       of every one of them); records seq_len in the
+ *                       workspace and leaves it unchanged;
+ *   cknv_decode_finish  the normalisers, the selection, and the attention
+ *                       with compensation; advances seq_len.
+ * Arguments as for cknv_decode_step. */
+int cknv_decode_score(const cknv_shape* shape, const cknv_cache* cache, const uint16_t* new_k,
+                      const uint16_t* new_v, const float* q, int32_t budget_tokens,
+                      int32_t max_blocks, void* ws, size_t ws_bytes, void* stream);
+int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const float* q,
+                       int32_t budget_tokens, int32_t max_blocks, float* scores, int32_t* sel,
+                       int32_t* n_sel, float* out, float* lse, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Full (dense) softmax attention over every cached token, the baseline the
  * page compares CompKV with ("Assumptions and limits"). Same q/out/lse

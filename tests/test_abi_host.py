@@ -164,11 +164,20 @@ def test_decode_halves_reject_before_launch():
     c = cache_struct()
     L = cknv.lib()
     _, need = wsize(sh)
-    assert L.cknv_decode_score(ctypes.byref(sh), ctypes.byref(c), None, 512, 2048, FAKE, need,
-                               None) == cknv.EINVAL
-    assert L.cknv_decode_score(ctypes.byref(sh), ctypes.byref(c), FAKE, 512, 2048, FAKE, need - 1,
-                               None) == cknv.ENOSPACE
-    assert L.cknv_decode_finish(ctypes.byref(sh), ctypes.byref(c), None, FAKE, FAKE, 512, 2048,
-                                None, FAKE, FAKE, FAKE, None, FAKE, need, None) == cknv.EINVAL
-    assert L.cknv_decode_finish(ctypes.byref(sh), ctypes.byref(c), FAKE, FAKE, FAKE, 512, 2101,
-                                None, FAKE, FAKE, FAKE, None, FAKE, need, None) == cknv.ENOSPACE
+
+    def score(nk=FAKE, nv=FAKE, q=FAKE, mb=2048, ws_bytes=need):
+        return L.cknv_decode_score(ctypes.byref(sh), ctypes.byref(c), nk, nv, q, 512, mb, FAKE,
+                                   ws_bytes, None)
+
+    def finish(q=FAKE, sel=FAKE, n_sel=FAKE, out=FAKE, mb=2048, ws_bytes=need):
+        return L.cknv_decode_finish(ctypes.byref(sh), ctypes.byref(c), q, 512, mb, None, sel, n_sel,
+                                    out, None, FAKE, ws_bytes, None)
+
+    for kw in (dict(nk=None), dict(nv=None), dict(q=None)):
+        assert score(**kw) == cknv.EINVAL, kw
+    assert score(ws_bytes=need - 1) == cknv.ENOSPACE
+    assert score(mb=2101) == cknv.ENOSPACE
+    for kw in (dict(q=None), dict(sel=None), dict(n_sel=None), dict(out=None)):
+        assert finish(**kw) == cknv.EINVAL, kw
+    assert finish(ws_bytes=need - 1) == cknv.ENOSPACE
+    assert finish(mb=2101) == cknv.ENOSPACE
