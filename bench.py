@@ -78,6 +78,13 @@ def dense_bytes(w, T: int) -> int:
     return w.S * w.H * T * 2 * w.d * 2
 
 
+def build_bytes(w, T: int) -> int:
+    """Algorithmic HBM bytes of one bulk summary build over T tokens per
+    unit: the BF16 K and V read once, every block's summary written once."""
+    NB = math.ceil(T / 16)
+    return w.S * w.H * (T * 2 * w.d * 2 + NB * (2 * w.d + w.r + 1) * 4)
+
+
 class Bench:
     def __init__(self, w, R, appends, stream):
         import numpy as np
@@ -304,12 +311,13 @@ def run_workload(torch, timer, wname, args, stream, want_dense=True):
     k_avg, k_med = time_score_kernel(torch, timer, stream, bench, max(8, 256 // R))
     f_avg, f_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "decode_finish")
     ms_three = time_graph_steps(torch, timer, stream, bench, max(R, steps // 4), which="step")
+    ms_build = time_build(torch, timer, stream, bench, max(2, 64 // R))
     T = bench.seq_len()
     sb, ab = step_bytes(w, T)
     res = {"w": w, "R": R, "steps": steps, "warmup": warm, "ms_step": ms_step,
            "ms_eager": ms_eager, "T": T, "score_bytes": sb, "attend_bytes": ab,
            "score_ms": k_avg, "score_ms_median": k_med, "finish_ms": f_avg,
-           "ms_three_calls": ms_three}
+           "ms_three_calls": ms_three, "build_ms": ms_build, "build_bytes": build_bytes(w, T)}
     if want_dense:
         res["dense_ms_step"] = time_graph_steps(torch, timer, stream, bench, max(R, steps // 4),
                                                 which="dense")
@@ -318,6 +326,23 @@ def run_workload(torch, timer, wname, args, stream, want_dense=True):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def time_build(torch, timer, stream, bench, sweeps):
+    """Average duration (ms) of cknv_build_summaries over a whole layer
+    (rebuilds what is there, so repeats are harmless), rotating the R layers so
+    every launch reads its cache from HBM."""
+    from block_sparse_kv_stats_amd import cknv
+    e0, e1 = timer.event(), timer.event()
+    with torch.cuda.stream(stream):
+        timer.head_start(5.0 + 0.3 * sweeps * bench.R)
+        e0.record(stream)
+        for _ in range(sweeps):
+            for L in bench.layers:
+                cknv.build_summaries(L, bench.max_blocks, stream=stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (sweeps * bench.R)
 
 
 def copy_probe(nbytes: int, reps: int):
@@ -428,6 +453,13 @@ def summarize_profiles(out_dir):
     print(json.dumps(rec))
 
 
+def build_line(res):
+    gbps = res["build_bytes"] / (res["build_ms"] * 1e-3) / 1e9
+    return {"kernel": "build_kernel (cknv_build_summaries)", "avg_us": round(res["build_ms"] * 1e3, 2),
+            "algorithmic_bytes": res["build_bytes"], "GBps": round(gbps, 1),
+            "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -504,6 +536,7 @@ def main():
                            "algorithmic_bytes": main_res["attend_bytes"]},
         "three_call_path": {"steps_per_s": round(1000.0 / main_res["ms_three_calls"], 2),
                             "calls": "cknv_append + cknv_score_select + cknv_attend"},
+        "bulk_build": build_line(main_res),
     }
     if "dense_ms_step" in main_res:
         line["dense_baseline"] = {
@@ -521,7 +554,8 @@ def main():
             "score_kernel_GBps": round(e_score, 1), "score_frac": round(e_score / PEAK_HBM_GBPS, 4),
             "score_avg_launch_us": round(extra["score_ms"] * 1e3, 3),
             "finish_avg_us": round(extra["finish_ms"] * 1e3, 3),
-            "three_call_steps_per_s": round(1000.0 / extra["ms_three_calls"], 2)}
+            "three_call_steps_per_s": round(1000.0 / extra["ms_three_calls"], 2),
+            "bulk_build": build_line(extra)}
         if "dense_ms_step" in extra:
             line["also"]["dense_steps_per_s"] = round(1000.0 / extra["dense_ms_step"], 2)
             line["also"]["speedup_of_compkv"] = round(extra["dense_ms_step"] / extra["ms_step"], 3)

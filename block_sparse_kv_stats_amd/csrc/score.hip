@@ -31,6 +31,7 @@
 // it": the current block's statistics are refreshed every step); the
 // scoring workgroups then cover only the blocks closed before the token.
 #include "cknv_internal.h"
+#include "summary_core.h"
 
 namespace cknv {
 
@@ -168,14 +169,7 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
   const long tok0 = (long)fblk * kBlock;
   const int np = T0 - fblk * kBlock, n = np + 1;
   uint32_t fk[16], fv[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    long t = tok0 + j;
-    t = t < T0 ? t : (T0 > 0 ? T0 - 1 : 0);  // clamp into written tokens; unused past np
-    const size_t off = (size_t)t * D + lane * VPL;
-    fk[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(kc + off) : (uint32_t)kc[off];
-    fv[j] = VPL == 2 ? *reinterpret_cast<const uint32_t*>(vc + off) : (uint32_t)vc[off];
-  }
+  load_block_words<D>(kc, vc, tok0, np, lane, fk, fv);  // the np cached tokens
   const size_t noff = (size_t)unit * D + lane * VPL;
   const uint32_t nkw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_k + noff) : (uint32_t)a.new_k[noff];
   const uint32_t nvw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_v + noff) : (uint32_t)a.new_v[noff];
@@ -184,37 +178,13 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < VPL; ++e) fq[g][e] = a.q[((size_t)unit * G + g) * D + lane * VPL + e];
-
-  float km[VPL], kvr[VPL], vm[VPL];
 #pragma unroll
-  for (int e = 0; e < VPL; ++e) {
-    float kx[16], vx[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t wk = j < np ? fk[j] : nkw;
-      const uint32_t wv = j < np ? fv[j] : nvw;
-      kx[j] = e == 0 ? bf16_lo(wk) : bf16_hi(wk);
-      vx[j] = e == 0 ? bf16_lo(wv) : bf16_hi(wv);
-    }
-    float vvar;
-    mean_var16(kx, n, km[e], kvr[e]);
-    mean_var16(vx, n, vm[e], vvar);
+  for (int j = 0; j < 16; ++j) {  // the new token is token np
+    fk[j] = j < np ? fk[j] : nkw;
+    fv[j] = j < np ? fv[j] : nvw;
   }
-  // D̄: mean coordinate variance of each group of gs = D/r coordinates,
-  // summed as a pairwise tree (the order of the summary kernels)
-  const int gs = D / a.r;
-  float dl[VPL];
-  if (gs >= VPL) {
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) part += kvr[e];
-    for (int o = 1; o < gs / VPL; o <<= 1) part += __shfl_xor(part, o);
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) dl[e] = part / (float)gs;
-  } else {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) dl[e] = kvr[e];
-  }
+  float km[VPL], vm[VPL], dl[VPL];
+  block_summary<D>(fk, fv, n, a.r, km, vm, dl);
   const float half = (a.flags & CKNV_FLAG_FIRST_ORDER_MASS) ? 0.f : 0.5f;
   const bool mass_only = (a.flags & CKNV_FLAG_MASS_ONLY_SCORE) != 0;
   float2 info = make_float2(-INFINITY, 0.f);
@@ -241,18 +211,7 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
     kc[toff] = (uint16_t)nkw;
     vc[toff] = (uint16_t)nvw;
   }
-#pragma unroll
-  for (int e = 0; e < VPL; ++e) {
-    a.kbar[row * D + lane * VPL + e] = km[e];
-    a.vbar[row * D + lane * VPL + e] = vm[e];
-  }
-  if (gs >= VPL) {
-    if ((lane * VPL) % gs == 0) a.dbar[row * a.r + (lane * VPL) / gs] = dl[0];
-  } else {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) a.dbar[row * a.r + lane * VPL + e] = dl[e];
-  }
-  if (lane == 0) a.cnt[row] = (float)n;
+  store_block_summary<D>(a.kbar, a.dbar, a.cnt, a.vbar, row, a.r, n, lane, km, vm, dl);
   if (h == 0 && lane == 0) a.t0_out[s] = T0;
 }
 

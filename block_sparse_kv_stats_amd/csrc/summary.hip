@@ -7,10 +7,12 @@
 // "How to use it": every decode step a fused kernel refreshes the current
 // block's statistics and stores the new K/V.
 //
-// Both kernels recompute a block from its (at most 16) BF16 tokens with the
-// same device function: two passes in FP32 (mean, then the mean squared
-// deviation, i.e. the population variance), summed in token order.
+// Both recompute a block from its (at most 16) BF16 tokens: two passes in
+// FP32 (mean, then the mean squared deviation, i.e. the population
+// variance), summed in token order; D̄ groups summed as a balanced pairwise
+// tree. The bulk build and the fused step's refresh share summary_core.h.
 #include "cknv_internal.h"
+#include "summary_core.h"
 
 namespace cknv {
 
@@ -86,46 +88,29 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   if (threadIdx.x == 0 && room) a.seq_len[s] = T + 1;
 }
 
-// Bulk build: 256 threads = 256/D blocks per workgroup, one thread per coordinate.
+// Bulk build: one wave per block (kWaves blocks per workgroup), lane l owning
+// coordinates [l*VPL, l*VPL + VPL) of all its tokens; every load of the wave
+// is issued before the first use. Blocks at or past NB are left untouched.
 template <int D>
 __global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
-  constexpr int SLOTS = kThreads / D;
-  __shared__ float cvar[kThreads];
+  constexpr int VPL = D / 64;
   const int unit = blockIdx.y, s = unit / a.H;
-  const int slot = threadIdx.x / D, c = threadIdx.x % D;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int T = a.seq_len[s];
-  const long cap_tok = (long)a.cap_blocks * kBlock;
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < a.max_blocks ? NB : a.max_blocks;
-  const int b = blockIdx.x * SLOTS + slot;
-  const bool valid = b < NB;
-  float kv = 0.f;
-  if (valid) {
-    const int n = (T - b * kBlock) < kBlock ? (T - b * kBlock) : kBlock;
-    const size_t tok0 = (size_t)unit * cap_tok + (size_t)b * kBlock;
-    const uint16_t* kb = a.k + tok0 * D + c;
-    const uint16_t* vb = a.v + tok0 * D + c;
-    float kx[16], vx[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      kx[j] = (j < n) ? bf16_1(kb[(size_t)j * D]) : 0.f;
-      vx[j] = (j < n) ? bf16_1(vb[(size_t)j * D]) : 0.f;
-    }
-    float km, vm, vv;
-    mean_var16(kx, n, km, kv);
-    mean_var16(vx, n, vm, vv);
-    const size_t row = (size_t)unit * a.cap_blocks + b;
-    a.kbar[row * D + c] = km;
-    a.vbar[row * D + c] = vm;
-    if (c == 0) a.cnt[row] = (float)n;
-  }
-  cvar[threadIdx.x] = kv;
-  const int gs = D / a.r;
-  group_tree_sums<D, kThreads>(cvar, SLOTS, gs);
-  if (valid && c % gs == 0) {
-    const size_t row = (size_t)unit * a.cap_blocks + b;
-    a.dbar[row * a.r + c / gs] = cvar[threadIdx.x] / (float)gs;
-  }
+  if (b >= NB) return;  // wave-uniform
+  const int n = (T - b * kBlock) < kBlock ? (T - b * kBlock) : kBlock;
+  const long cap_tok = (long)a.cap_blocks * kBlock;
+  const uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
+  const uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
+  uint32_t fk[16], fv[16];
+  load_block_words<D>(kc, vc, (long)b * kBlock, n, lane, fk, fv);
+  float km[VPL], vm[VPL], dl[VPL];
+  block_summary<D>(fk, fv, n, a.r, km, vm, dl);
+  store_block_summary<D>(a.kbar, a.dbar, a.cnt, a.vbar, (size_t)unit * a.cap_blocks + b, a.r, n,
+                         lane, km, vm, dl);
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, size_t n) {
@@ -141,8 +126,7 @@ hipError_t launch_append(int d, const AppendArgs& a, hipStream_t st) {
 
 hipError_t launch_build(int d, const BuildArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
-  const int slots = kThreads / d;
-  const int gx = (a.max_blocks + slots - 1) / slots;
+  const int gx = (a.max_blocks + kWaves - 1) / kWaves;
   const void* f = d == 128 ? (const void*)build_kernel<128> : (const void*)build_kernel<64>;
   return hipLaunchKernel(f, dim3(gx, U), dim3(kThreads), args, 0, st);
 }
