@@ -39,7 +39,8 @@ METRIC = "decode steps/sec (1 layer, B=1) at 32K/128K ctx + achieved HBM GB/s vs
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 SCORE_SOURCES = ["block_sparse_kv_stats_amd/csrc/score.hip",
-                 "block_sparse_kv_stats_amd/csrc/cknv_internal.h"]
+                 "block_sparse_kv_stats_amd/csrc/cknv_internal.h",
+                 "block_sparse_kv_stats_amd/csrc/summary_core.h"]
 
 
 def log(msg):

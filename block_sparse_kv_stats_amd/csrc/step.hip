@@ -23,20 +23,20 @@
 // Phases of a workgroup (NT threads; thread t owns blocks t + NT*j of the
 // unit):
 //   loads      T0, finfo, the chunk headers, the thread's score groups and
-//              u terms, the query, the wave's first chunk records;
+//              u terms, the query, and (waves AW..NW-1) their first chunk
+//              records;
 //   LSE        every wave reduces the chunk headers and the fresh block's a
 //              itself (the same bits in every wave); factors
-//              e^{group max - LSE} of the thread's score groups to LDS; the
-//              wave folds its first chunk records;
+//              e^{group max - LSE} of the thread's score groups to LDS;
 //   keys       S_b per block (fp32 bits order like the values, S_b >= 0);
 //              scores; 2048-bin histogram of the candidates' top 11 bits;
 //   select     the bin holding the (Kb-3)-th largest candidate key; keys
 //              in that bin are ranked exactly (or, for long runs of equal
 //              keys, pinned by two more radix passes, ties by index);
 //   compact    kept blocks in ascending order -> sel, and this part's slice;
-//   attend     wave w: kept blocks w + NW*i (i < KPW) of this part's slice
-//              (exact terms minus their compensation), then the rest of its
-//              share of this part's chunk records;
+//   attend     waves w < AW: kept block w of this part's slice (exact terms
+//              minus its compensation); meanwhile waves w >= AW fold this
+//              part's chunk records;
 //   merge      the waves' records -> out, lse (P == 1) or a part record.
 #include "attend_core.h"
 #include "select_core.h"
@@ -59,14 +59,15 @@ struct StepCfg {
   static constexpr int KPW = step_kept_per_wave(G);                // kept blocks per wave
   static constexpr int KPART = step_kept_per_part(G);              // kept blocks per workgroup
   static constexpr int CPL = step_chunks_per_lane(KPTB);           // chunk headers per lane
-  // Chunk records per wave loaded with the inputs (what the registers left
-  // by the other inputs hold, 1..8), and per later batch (after the tiles).
+  // Chunk records per record-folding wave loaded with the inputs (what the
+  // registers left by the other inputs hold, 1..4), and per later batch.
   static constexpr int RWORDS = G * (2 + D / 64);
-  static constexpr int RBUDGET = 176 - UB * G - 2 * GPT * G - 2 * CPL * G;
-  static constexpr int RPF = RBUDGET / RWORDS < 1 ? 1 : (RBUDGET / RWORDS > 8 ? 8 : RBUDGET / RWORDS);
+  static constexpr int RBUDGET = 112 - UB * G - 2 * GPT * G - 2 * CPL * G;
+  static constexpr int RPF = RBUDGET / RWORDS < 1 ? 1 : (RBUDGET / RWORDS > 4 ? 4 : RBUDGET / RWORDS);
   static constexpr int RPW = 32 / RWORDS < 1 ? 1 : (32 / RWORDS > 4 ? 4 : 32 / RWORDS);
   static constexpr int AW = kStepAttendWaves;                      // attending waves
-  static_assert(KPART == AW * KPW && AW <= NW, "kept slice of a workgroup");
+  static constexpr int RW = NW - AW;                               // record-folding waves
+  static_assert(KPART == AW * KPW && AW < NW, "kept slice of a workgroup");
 };
 
 // The lane's part of one chunk record of the scoring pass: (m, l) and the
@@ -122,18 +123,6 @@ __device__ __forceinline__ void finalize_records(const float* recs, int n, float
   }
 }
 
-// Keep a wave state in registers at this point: the compiler may not move
-// the arithmetic that produced it past here.
-template <int D, int G>
-__device__ __forceinline__ void pin_state(WaveState<D, G>& st) {
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    asm volatile("" : "+v"(st.m[g]), "+v"(st.l[g]));
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) asm volatile("" : "+v"(st.acc[g][e]));
-  }
-}
-
 // Fold one compensation record (this lane's coordinates) into a wave state.
 template <int D, int G>
 __device__ __forceinline__ void fold_record(WaveState<D, G>& st, const RecordRegs<D, G>& r) {
@@ -162,6 +151,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   using C = StepCfg<D, G, KPTB>;
   constexpr int NT = C::NT, NW = C::NW, KPT = C::KPT, UB = C::UB;
   constexpr int GPT = C::GPT, NGMAX = C::NGMAX, KPW = C::KPW, KPART = C::KPART, AW = C::AW;
+  constexpr int RW = C::RW;
   constexpr int CPL = C::CPL, RPF = C::RPF, RPW = C::RPW;
   constexpr int W = rec_words(D);
   // LDS: area A holds the score-group factors during the keys, then the
@@ -238,15 +228,18 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     const int i = tid + k * NT;
     q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
   }
-  // This part's chunk records: wave w folds records c0 + w + NW*i. The
-  // first RPF are loaded now; they do not depend on the selection.
+  // This part's chunk records are folded by the waves that attend no tile
+  // (w >= AW), while the others attend: wave w folds records
+  // c0 + (w - AW) + RW*i. The first RPF are loaded now; they do not depend
+  // on the selection.
   const int c0 = (int)((long)p * NC / P), c1 = (int)((long)(p + 1) * NC / P);
   const int clast = c1 > 0 ? c1 - 1 : 0;
+  const int rw = wave - AW;  // record wave index (negative: an attending wave)
   RecordRegs<D, G> rf[RPF];
 #pragma unroll
   for (int i = 0; i < RPF; ++i) {
-    const int c = c0 + wave + NW * i;
-    rf[i].load(crec + (size_t)(c < c1 ? c : clast) * G * W, c < c1 && !nc, lane);
+    const int c = c0 + rw + RW * i;
+    rf[i].load(crec + (size_t)(c < c1 ? c : clast) * G * W, rw >= 0 && c < c1 && !nc, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -293,10 +286,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
   WaveState<D, G> st;
   st.init();
-#pragma unroll
-  for (int i = 0; i < RPF; ++i)
-    if (c0 + wave + NW * i < c1 && !nc) fold_record<D, G>(st, rf[i]);  // wave-uniform
-  pin_state(st);  // fold here: the records' registers die before the selection
   lds_barrier();
 
   // ================================================================ keys
@@ -510,17 +499,21 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int i = 0; i < KPW; ++i) absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
   }
-  // Records past the first RPF of the wave (more than the registers hold
-  // with the inputs): RPW per round trip.
-  for (int cb = c0 + wave + NW * RPF; cb < c1 && !nc; cb += NW * RPW) {
-    RecordRegs<D, G> rb[RPW];
+  if (rw >= 0 && !nc) {
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int c = cb + NW * i;
-      rb[i].load(crec + (size_t)(c < c1 ? c : clast) * G * W, c < c1, lane);
+    for (int i = 0; i < RPF; ++i)
+      if (c0 + rw + RW * i < c1) fold_record<D, G>(st, rf[i]);  // wave-uniform
+    // records past the first RPF of the wave: RPW per round trip
+    for (int cb = c0 + rw + RW * RPF; cb < c1; cb += RW * RPW) {
+      RecordRegs<D, G> rb[RPW];
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int c = cb + RW * i;
+        rb[i].load(crec + (size_t)(c < c1 ? c : clast) * G * W, c < c1, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) fold_record<D, G>(st, rb[i]);
     }
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) fold_record<D, G>(st, rb[i]);
   }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
   lds_barrier();
