@@ -129,8 +129,8 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
   for (int b = lo + 2 * wave; b < hi; b += 2 * kWaves) {
     Tile<D> t0, t1;
     const bool u1 = b + 1 < hi;
-    t0.load(kc, vc, (long)b * kBlock, T, lane);
-    t1.load(kc, vc, (long)(u1 ? b + 1 : b) * kBlock, u1 ? (long)T : 0, lane);  // a valid block even when unused
+    t0.template load<true>(kc, vc, (long)b * kBlock, T, lane);
+    t1.template load<true>(kc, vc, (long)(u1 ? b + 1 : b) * kBlock, u1 ? (long)T : 0, lane);  // a valid block even when unused
     absorb<D, G, false>(st, t0, none, q_l, lane, a.isd);
     if (u1) absorb<D, G, false>(st, t1, none, q_l, lane, a.isd);
   }

@@ -36,6 +36,7 @@ struct Tile {
   uint32_t v[16];  // d=128: 2 bf16 (one word) per token; d=64: 1 bf16 in the low half
   bool tv[4];
   int nt;          // valid tokens
+  template <bool NT = false>
   __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
     const int tq = lane >> 4, cc = lane & 15;
     const long left = T - tok0;
@@ -47,18 +48,18 @@ struct Tile {
       tv[m] = t < nt;
       const uint16_t* src = kc + (size_t)(tok0 + (t < last ? t : last)) * D + cc * EPL;
       if (EPL == 8) {
-        const uint4 kk = stream_load_u4(src);
+        const uint4 kk = stream_load_u4<NT>(src);
         k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
         k[m][2] = tv[m] ? kk.z : 0u; k[m][3] = tv[m] ? kk.w : 0u;
       } else {
-        const uint2 kk = stream_load_u2(src);
+        const uint2 kk = stream_load_u2<NT>(src);
         k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
       }
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const uint16_t* src = vc + (size_t)(tok0 + (t < last ? t : last)) * D + lane * VPL;
-      const uint32_t w = VPL == 2 ? stream_load_u1(src) : stream_load_h(src);
+      const uint32_t w = VPL == 2 ? stream_load_u1<NT>(src) : stream_load_h<NT>(src);
       v[t] = t < nt ? w : 0u;
     }
   }
@@ -76,18 +77,18 @@ struct Tile {
       tv[m] = t < nt;
       const uint16_t* src = (t < np ? kc + (size_t)(tok0 + t) * D : nk) + cc * EPL;
       if (EPL == 8) {
-        const uint4 kk = stream_load_u4(src);
+        const uint4 kk = stream_load_u4<false>(src);
         k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
         k[m][2] = tv[m] ? kk.z : 0u; k[m][3] = tv[m] ? kk.w : 0u;
       } else {
-        const uint2 kk = stream_load_u2(src);
+        const uint2 kk = stream_load_u2<false>(src);
         k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
       }
     }
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const uint16_t* src = (t < np ? vc + (size_t)(tok0 + t) * D : nv) + lane * VPL;
-      const uint32_t w = VPL == 2 ? stream_load_u1(src) : stream_load_h(src);
+      const uint32_t w = VPL == 2 ? stream_load_u1<false>(src) : stream_load_h<false>(src);
       v[t] = t < nt ? w : 0u;
     }
   }
@@ -189,6 +190,145 @@ __device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, co
 #pragma unroll
     for (int e = 0; e < VPL; ++e) st.acc[g][e] = acc[e];
   }
+}
+
+// ---------------------------------------------------------------- MFMA tiles
+// The logits of a 16-token tile on the matrix cores: S[t][g] = K[t] . q_g as
+// v_mfma_f32_16x16x32_bf16 with A = the tile's keys (token t = row) and
+// B = the query heads (head g = column, G of 16 used). The operand layouts
+// (checked on gfx950): A lane l holds row l%16, k = 8*(l/16) + e; B lane l
+// holds column l%16, the same k; D lane l holds column l%16, rows
+// 4*(l/16) + e. The k index is mapped to key coordinates so that lane l reads
+// D/4 consecutive coordinates of its token: instruction i, lane group
+// c = l/16, element e -> coordinate (D/4)*c + 8*i + e (A and B agree, so the
+// sum is the same). q is FP32: it goes in as two BF16 halves (q = hi + lo up
+// to 2^-16 relative), and the BF16 keys are exact, so the logits carry
+// FP32-level error. Softmax and the value sums stay on the vector units.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct TileM {
+  static constexpr int NI = D / 32, VPL = D / 64;
+  u32x4_t k[NI];   // keys, MFMA A layout
+  uint32_t v[16];  // values: lane's VPL coordinates of every token (as Tile)
+  int nt;          // valid tokens
+  __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
+    const long left = T - tok0;
+    nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+    const int last = nt > 0 ? nt - 1 : 0;  // loads read token min(t, last), masked after
+    const int t = lane & 15, c = lane >> 4;
+    const uint16_t* ks = kc + (size_t)(tok0 + (t < last ? t : last)) * D + (D / 4) * c;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      k[i] = *reinterpret_cast<const u32x4_t*>(ks + 8 * i);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint16_t* src = vc + (size_t)(tok0 + (j < last ? j : last)) * D + lane * VPL;
+      const uint32_t w = VPL == 2 ? stream_load_u1<false>(src) : stream_load_h<false>(src);
+      v[j] = j < nt ? w : 0u;
+    }
+  }
+};
+
+// The query heads as MFMA B operands (head l%16 < G, zero columns after).
+template <int D>
+struct QMfma {
+  static constexpr int NI = D / 32;
+  bf16x8_t hi[NI], lo[NI];
+  template <int G>
+  __device__ void build(const float* q_l, int lane) {
+    const int j = lane & 15, c = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = j < G ? q_l[j * D + (D / 4) * c + 8 * i + e] : 0.f;
+        const __bf16 h = (__bf16)x;
+        hi[i][e] = h;
+        lo[i][e] = (__bf16)(x - (float)h);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// absorb<D, G, true> with the logits on MFMA: add one block's exact terms and
+// remove its compensation terms (none when bm.n = 0). `pw`: this wave's LDS
+// scratch of 16*G floats (the probabilities, read back as broadcasts).
+template <int D, int G>
+__device__ __forceinline__ void absorb_mfma(WaveState<D, G>& st, const TileM<D>& t, const BlockMean<D>& bm,
+                                            const QMfma<D>& qm, const float* q_l, float* pw, int lane,
+                                            float isd) {
+  constexpr int VPL = D / 64, NI = D / 32;
+  static_assert(G <= 16, "one MFMA column per query head");
+  const int j = lane & 15, c = lane >> 4;
+  float zbar[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float zp = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) zp += bm.kb[e] * q_l[g * D + lane * VPL + e];
+    zbar[g] = group_sum<64>(zp) * isd;
+  }
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, t.k[i]);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qm.hi[i], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qm.lo[i], s, 0, 0, 0);
+  }
+  float z[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = 4 * c + e < t.nt ? s[e] * isd : -INFINITY;
+  const float cmax = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));  // head j's block max
+  float M[G], sc[G], w[G];
+  float Mj = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float bmax = lane_value(cmax, g);
+    if (bm.n > 0.f) bmax = fmaxf(bmax, zbar[g]);
+    M[g] = fmaxf(st.m[g], bmax);
+    sc[g] = rescale(st.m[g], M[g]);
+    w[g] = bm.n > 0.f ? bm.n * __expf(zbar[g] - M[g]) : 0.f;
+    Mj = j == g ? M[g] : Mj;
+  }
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = z[e] == -INFINITY ? 0.f : __expf(z[e] - Mj);
+  const float ps = rows_sum((p[0] + p[1]) + (p[2] + p[3]));
+  if (j < G) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pw[(4 * c + e) * G + j] = p[e];
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.l[g] = st.l[g] * sc[g] + lane_value(ps, g) - w[g];
+    st.m[g] = M[g];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) st.acc[g][e] *= sc[g];
+  }
+  // the wave reads back its own LDS writes (LDS operations of a wave run in order)
+#pragma unroll
+  for (int tk = 0; tk < 16; ++tk) {
+    float pv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) pv[g] = pw[tk * G + g];
+    const uint32_t vw = t.v[tk];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      st.acc[g][0] += pv[g] * bf16_lo(vw);
+      if (VPL == 2) st.acc[g][1 % VPL] += pv[g] * bf16_hi(vw);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) st.acc[g][e] -= w[g] * bm.vb[e];
 }
 
 // Write the wave's record [m, l, 0, 0, acc[D]] per g.

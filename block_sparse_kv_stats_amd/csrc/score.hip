@@ -169,7 +169,7 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
   const long tok0 = (long)fblk * kBlock;
   const int np = T0 - fblk * kBlock, n = np + 1;
   uint32_t fk[16], fv[16];
-  load_block_words<D>(kc, vc, tok0, np, lane, fk, fv);  // the np cached tokens
+  load_block_words<D, false>(kc, vc, tok0, np, lane, fk, fv);  // the np cached tokens
   const size_t noff = (size_t)unit * D + lane * VPL;
   const uint32_t nkw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_k + noff) : (uint32_t)a.new_k[noff];
   const uint32_t nvw = VPL == 2 ? *reinterpret_cast<const uint32_t*>(a.new_v + noff) : (uint32_t)a.new_v[noff];

@@ -167,6 +167,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   __shared__ float scl[NW * G + 2 * G];
   __shared__ int ctl[8];
   __shared__ int klist[KPART];
+  __shared__ __align__(16) float pbuf[AW * 16 * G];  // attending waves' tile probabilities
   float* fgrp = areaA;                   // [NGMAX][G] exp(group max - LSE_g)
   float* recs = areaA;                   // [NW][G][W] after the selection
   float* q_l = areaA + NW * G * W;       // [G][D] after the selection
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       const int e = lo + wave + AW * i;
       bk[i] = e < nk ? klist[wave + AW * i] : -1;
     }
-    Tile<D> tile[KPW];
+    TileM<D> tile[KPW];
     BlockMean<D> bm[KPW];
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
@@ -491,13 +492,16 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       tile[i].load(kc, vc, (long)b * kBlock, bk[i] >= 0 ? (long)T : 0, lane);
       bm[i].load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
       // one code path: a block whose compensation the scoring pass did not
-      // count removes a zero-mass term (its z̄ never exceeds its largest logit)
+      // count removes a zero-mass term
       if (!(bk[i] >= 0 && bk[i] < NBa && !nc)) bm[i].n = 0.f;
     }
+    QMfma<D> qm;
+    qm.template build<G>(q_l, lane);
     __builtin_amdgcn_sched_barrier(0);  // every tile load issued before the first use
     // an empty slot (bk < 0) holds no valid token and n = 0: it adds nothing
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
+    for (int i = 0; i < KPW; ++i)
+      absorb_mfma<D, G>(st, tile[i], bm[i], qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
   }
   if (rw >= 0 && !nc) {
 #pragma unroll

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void build_kernel(BuildArgs a) {
   const uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
   const uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
   uint32_t fk[16], fv[16];
-  load_block_words<D>(kc, vc, (long)b * kBlock, n, lane, fk, fv);
+  load_block_words<D, true>(kc, vc, (long)b * kBlock, n, lane, fk, fv);
   float km[VPL], vm[VPL], dl[VPL];
   block_summary<D>(fk, fv, n, a.r, km, vm, dl);
   store_block_summary<D>(a.kbar, a.dbar, a.cnt, a.vbar, (size_t)unit * a.cap_blocks + b, a.r, n,

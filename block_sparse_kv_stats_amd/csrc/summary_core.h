@@ -17,8 +17,8 @@ namespace cknv {
 // The lane's words of n (1..16) tokens: token j of the block from the cache
 // row at tok (slots past the last valid one read the last valid token; they
 // are not used). d = 128: one word holds the lane's 2 bf16, d = 64: the low
-// half holds its 1 bf16.
-template <int D>
+// half holds its 1 bf16. NT: non-temporal loads (a bulk pass) or plain ones.
+template <int D, bool NT>
 __device__ __forceinline__ void load_block_words(const uint16_t* kc, const uint16_t* vc, long tok0,
                                                  int n, int lane, uint32_t (&fk)[16],
                                                  uint32_t (&fv)[16]) {
@@ -27,8 +27,8 @@ __device__ __forceinline__ void load_block_words(const uint16_t* kc, const uint1
   for (int j = 0; j < 16; ++j) {
     const long t = tok0 + (j < n ? j : (n > 0 ? n - 1 : 0));
     const size_t off = (size_t)t * D + lane * VPL;
-    fk[j] = VPL == 2 ? stream_load_u1(kc + off) : stream_load_h(kc + off);
-    fv[j] = VPL == 2 ? stream_load_u1(vc + off) : stream_load_h(vc + off);
+    fk[j] = VPL == 2 ? stream_load_u1<NT>(kc + off) : stream_load_h<NT>(kc + off);
+    fv[j] = VPL == 2 ? stream_load_u1<NT>(vc + off) : stream_load_h<NT>(vc + off);
   }
 }
 
