@@ -72,6 +72,8 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   off = align256(off + (size_t)q.U * G * 2 * 4);
   q.off_hdr = off;
   off = align256(off + (size_t)q.U * q.C * G * 2 * 4);
+  q.off_pcnt = off;
+  off = align256(off + (size_t)q.U * 4);
   q.total = off;
   if (max_blocks > kSelThreads * kSelKeysPerThread) return CKNV_EUNSUPPORTED;
   *p = q;
@@ -179,6 +181,7 @@ static int decode_score_impl(const Plan& p, const cknv_shape* shape, const cknv_
   a.k = cache->k; a.v = cache->v; a.new_k = new_k; a.new_v = new_v;
   a.t0_out = reinterpret_cast<int32_t*>(w + p.off_t0);
   a.finfo = reinterpret_cast<float*>(w + p.off_finfo);
+  a.pcnt = reinterpret_cast<uint32_t*>(w + p.off_pcnt);
   a.flags = (int)shape->flags;
   a.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream));
@@ -193,6 +196,7 @@ static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv
   sa.t0 = reinterpret_cast<const int32_t*>(w + p.off_t0);
   sa.q = q;
   sa.finfo = reinterpret_cast<const float*>(w + p.off_finfo);
+  sa.pcnt = reinterpret_cast<uint32_t*>(w + p.off_pcnt);
   sa.grp = reinterpret_cast<const float*>(w + p.off_grp);
   sa.u = reinterpret_cast<const float*>(w + p.off_u);
   sa.comp = reinterpret_cast<const float*>(w + p.off_comp);

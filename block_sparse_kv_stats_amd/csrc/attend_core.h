@@ -393,23 +393,28 @@ __device__ __forceinline__ float record_column(const float* recs, const float* s
 }
 
 // Merge n records of G x W words (LDS, consecutive) into one record at dst
-// (global). `scl` is LDS scratch of n*G floats.
-template <int D, int G, int NT = kThreads>
+// (global). `scl` is LDS scratch of n*G floats. COHERENT: agent-scope stores
+// (coherent across XCDs for a reader in another workgroup of this launch).
+template <int D, int G, int NT = kThreads, bool COHERENT = false>
 __device__ __forceinline__ void merge_records(const float* recs, int n, float* dst, float* scl) {
   constexpr int W = rec_words(D);
   const int tid = threadIdx.x;
+  auto st = [](float* p, float v) {
+    if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+  };
   if (tid < G) {
     float M = -INFINITY, L = 0.f;
     record_scales<D, G>(recs, n, tid, scl, M, L, nullptr);
-    dst[tid * W] = M;
-    dst[tid * W + 1] = L;
-    dst[tid * W + 2] = 0.f;
-    dst[tid * W + 3] = 0.f;
+    st(dst + tid * W, M);
+    st(dst + tid * W + 1, L);
+    st(dst + tid * W + 2, 0.f);
+    st(dst + tid * W + 3, 0.f);
   }
   lds_barrier();
   for (int col = tid; col < G * D; col += NT) {
     const int g = col / D, c = col - g * D;
-    dst[g * W + 4 + c] = record_column<D, G>(recs, scl, n, g, c);
+    st(dst + g * W + 4 + c, record_column<D, G>(recs, scl, n, g, c));
   }
 }
 

@@ -48,7 +48,8 @@ struct Plan {
   int Pf;           // fused-step workgroups per unit = ceil(Kb/kStepKeptPerPart)
   int Pd;           // dense-attend workgroups per unit
   int BPW;          // dense-attend blocks per workgroup
-  size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, off_finfo, off_hdr, total;
+  size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, off_finfo, off_hdr, off_pcnt,
+      total;
 };
 
 int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p);
@@ -77,6 +78,7 @@ struct ScoreArgs {
   uint16_t* k; uint16_t* v; const uint16_t* new_k; const uint16_t* new_v;
   int32_t* t0_out;  // seq_len before the step, per sequence
   float* finfo;     // per unit and query head: (a, factor of p̂ in S) of that block; a = -inf if none
+  uint32_t* pcnt;   // per unit: the fused step's part counter, zeroed here
   int flags;        // CKNV_FLAG_* (ablation variants)
   float isd;  // 1/sqrt(d)
 };
@@ -102,6 +104,7 @@ struct StepArgs {
   const float* grp; const float* u; const float* comp; const float* hdr;
   float* scores; int32_t* sel; int32_t* n_sel; float* out; float* lse; float* part;
   const float* finfo;  // per unit and query head: (a, factor) of the block the token landed in
+  uint32_t* pcnt;      // per unit: parts done this step (zeroed by the scoring launch)
   int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P, bpw_shift;
   int flags;  // CKNV_FLAG_* (ablation variants)
   float isd;

@@ -1,6 +1,7 @@
 // The fused decode step after the scoring pass: normalisers, selection and
 // attention of one unit in one workgroup (or in P workgroups that each
-// attend a slice of the kept list, merged by step_merge_kernel).
+// attend a slice of the kept list; the last of them to finish merges all
+// P partial records).
 //
 // CompKV page (onedev.kr/papers/157):
 //   "What differs"  -- p̂ is normalised over all blocks, S_b = sum_g p̂ σ̂²;
@@ -37,7 +38,9 @@
 //   attend     waves w < AW: kept block w of this part's slice (exact terms
 //              minus its compensation); meanwhile waves w >= AW fold this
 //              part's chunk records;
-//   merge      the waves' records -> out, lse (P == 1) or a part record.
+//   merge      the waves' records -> out, lse (P == 1) or a part record;
+//              the part that completes the unit's count merges the P part
+//              records into out and lse.
 #include "attend_core.h"
 #include "select_core.h"
 #include "step_config.h"
@@ -135,6 +138,65 @@ __device__ __forceinline__ void fold_record(WaveState<D, G>& st, const RecordReg
     st.l[g] = st.l[g] * a + r.l[g] * b;
 #pragma unroll
     for (int e = 0; e < VPL; ++e) st.acc[g][e] = st.acc[g][e] * a + r.acc[g][e] * b;
+  }
+}
+
+// The last part of a unit: merge the unit's P part records (written by the
+// other parts with agent-scope stores, so read with agent-scope loads) into
+// out and lse. Thread t owns output columns t + NT*k; records are read in
+// batches of 8, every load of a batch issued before the first use.
+template <int D, int G, int NT>
+__device__ void merge_parts(const float* parts, int P, float* out, float* lse) {
+  constexpr int W = rec_words(D);
+  constexpr int COLS = (G * D + NT - 1) / NT;  // output columns per thread
+  constexpr int PB = 8;                        // records per batch
+  const int tid = threadIdx.x;
+  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  float M[COLS], L[COLS], A[COLS];
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) { M[k] = -INFINITY; L[k] = 0.f; A[k] = 0.f; }
+  for (int p0 = 0; p0 < P; p0 += PB) {
+    float m[PB][COLS], l[PB][COLS], x[PB][COLS];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int pi = p0 + i < P ? p0 + i : P - 1;
+#pragma unroll
+      for (int k = 0; k < COLS; ++k) {
+        int col = tid + k * NT;
+        col = col < G * D ? col : G * D - 1;
+        const int g = col / D, c = col - g * D;
+        const float* r = parts + ((size_t)pi * G + g) * W;
+        m[i][k] = p0 + i < P ? ld(r) : -INFINITY;
+        l[i][k] = ld(r + 1);
+        x[i][k] = ld(r + 4 + c);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < COLS; ++k) {
+      float MM = M[k];
+#pragma unroll
+      for (int i = 0; i < PB; ++i) MM = fmaxf(MM, m[i][k]);
+      const float so = rescale(M[k], MM);
+      float LL = L[k] * so, AA = A[k] * so;
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const float f = rescale(m[i][k], MM);
+        LL += l[i][k] * f;
+        AA += x[i][k] * f;
+      }
+      M[k] = MM;
+      L[k] = LL;
+      A[k] = AA;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) {
+    const int col = tid + k * NT;
+    if (col < G * D) {
+      const bool ok = L[k] > 0.f;
+      out[col] = ok ? A[k] / L[k] : 0.f;
+      if (col % D == 0 && lse) lse[col / D] = ok ? M[k] + __logf(L[k]) : -INFINITY;
+    }
   }
 }
 
@@ -527,74 +589,27 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     finalize_records<D, G, NT>(recs, NW, a.out + (size_t)unit * G * D,
                                a.lse ? a.lse + (size_t)unit * G : nullptr, scl);
     if (h == 0 && tid == 0 && app) a.seq_len[s] = T;
-  } else {
-    merge_records<D, G, NT>(recs, NW, a.part + ((size_t)unit * P + p) * G * W, scl);
+    return;
   }
-}
-
-// P > 1: one workgroup per unit merges the unit's P part records into out
-// and lse, and the unit's first head advances seq_len. Thread t owns output
-// columns t + 256*k; the records are read in batches of 8, every load of a
-// batch issued before the first use.
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void step_merge_kernel(StepArgs a) {
-  constexpr int W = rec_words(D);
-  constexpr int COLS = (G * D + kThreads - 1) / kThreads;  // output columns per thread
-  constexpr int PB = 8;                                    // records per batch
-  const int unit = blockIdx.x, tid = threadIdx.x;
-  const int s = unit / a.H, h = unit - s * a.H;
-  const int P = a.P;
-  const float* parts = a.part + (size_t)unit * P * G * W;
-  float M[COLS], L[COLS], A[COLS];
-#pragma unroll
-  for (int k = 0; k < COLS; ++k) { M[k] = -INFINITY; L[k] = 0.f; A[k] = 0.f; }
-  for (int p0 = 0; p0 < P; p0 += PB) {
-    float m[PB][COLS], l[PB][COLS], x[PB][COLS];
-#pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int pi = p0 + i < P ? p0 + i : P - 1;
-#pragma unroll
-      for (int k = 0; k < COLS; ++k) {
-        int col = tid + k * kThreads;
-        col = col < G * D ? col : G * D - 1;
-        const int g = col / D, c = col - g * D;
-        const float* r = parts + ((size_t)pi * G + g) * W;
-        m[i][k] = p0 + i < P ? r[0] : -INFINITY;
-        l[i][k] = r[1];
-        x[i][k] = r[4 + c];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < COLS; ++k) {
-      float MM = M[k];
-#pragma unroll
-      for (int i = 0; i < PB; ++i) MM = fmaxf(MM, m[i][k]);
-      const float so = rescale(M[k], MM);
-      float LL = L[k] * so, AA = A[k] * so;
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        const float f = rescale(m[i][k], MM);
-        LL += l[i][k] * f;
-        AA += x[i][k] * f;
-      }
-      M[k] = MM;
-      L[k] = LL;
-      A[k] = AA;
-    }
+  // P > 1: this part's record goes out with agent-scope (cross-XCD coherent)
+  // stores; once every thread's stores are complete, one thread counts the
+  // part in. The part that completes the count merges all P records, read
+  // with agent-scope loads, into out and lse. No workgroup waits on another.
+  float* mine = a.part + ((size_t)unit * P + p) * G * W;
+  merge_records<D, G, NT, true>(recs, NW, mine, scl);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(a.pcnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ctl[4] = done == (uint32_t)(P - 1);
   }
-  float* out = a.out + (size_t)unit * G * D;
-#pragma unroll
-  for (int k = 0; k < COLS; ++k) {
-    const int col = tid + k * kThreads;
-    if (col < G * D) {
-      const bool ok = L[k] > 0.f;
-      out[col] = ok ? A[k] / L[k] : 0.f;
-      if (col % D == 0 && a.lse) a.lse[(size_t)unit * G + col / D] = ok ? M[k] + __logf(L[k]) : -INFINITY;
-    }
-  }
-  if (h == 0 && tid == 0) {
-    const int T0 = a.t0[s];
-    if (step_appends(T0, a.cap_blocks, a.max_blocks)) a.seq_len[s] = T0 + 1;
+  lds_barrier();
+  if (!ctl[4]) return;
+  merge_parts<D, G, NT>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
+                        a.lse ? a.lse + (size_t)unit * G : nullptr);
+  if (tid == 0) {
+    __hip_atomic_store(a.pcnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (h == 0 && app) a.seq_len[s] = T;
   }
 }
 
@@ -602,23 +617,19 @@ hipError_t launch_step(int d, int G, const StepArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const int kptb = step_kptb(a.max_blocks);
   const void* f = nullptr;
-  const void* m = nullptr;
 #define CKNV_STEP_K(DD, GG, KK) \
   if (d == DD && G == GG && kptb == KK) f = (const void*)step_kernel<DD, GG, KK>;
 #define CKNV_STEP_CASE(DD, GG)                                                       \
   CKNV_STEP_K(DD, GG, 2) CKNV_STEP_K(DD, GG, 4) CKNV_STEP_K(DD, GG, 6)              \
   CKNV_STEP_K(DD, GG, 8) CKNV_STEP_K(DD, GG, 12) CKNV_STEP_K(DD, GG, 17)            \
-  CKNV_STEP_K(DD, GG, 24)                                                           \
-  if (d == DD && G == GG) m = (const void*)step_merge_kernel<DD, GG>;
+  CKNV_STEP_K(DD, GG, 24)
   CKNV_STEP_CASE(64, 1) CKNV_STEP_CASE(64, 2) CKNV_STEP_CASE(64, 4) CKNV_STEP_CASE(64, 8)
   CKNV_STEP_CASE(128, 1) CKNV_STEP_CASE(128, 2) CKNV_STEP_CASE(128, 4) CKNV_STEP_CASE(128, 8)
 #undef CKNV_STEP_CASE
 #undef CKNV_STEP_K
-  if (!f || !m) return hipErrorInvalidValue;
+  if (!f) return hipErrorInvalidValue;
   if (a.C > 64 * step_chunks_per_lane(kptb)) return hipErrorInvalidValue;  // chunk headers per lane
-  hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(kStepThreads), args, 0, st);
-  if (e != hipSuccess || a.P == 1) return e;
-  return hipLaunchKernel(m, dim3(U), dim3(kThreads), args, 0, st);
+  return hipLaunchKernel(f, dim3(U * a.P), dim3(kStepThreads), args, 0, st);
 }
 
 }  // namespace cknv
