@@ -3,10 +3,10 @@
 
 One step = one layer's decode step for the workload's batch, through the
 fused entry point cknv_decode_step: the streaming scoring pass over the
-summaries (score_kernel), then append + refresh of the block the token lands
-in + normalisers + selection + exact attention with Mean compensation
-(step_kernel, and step_merge_kernel when a unit's kept blocks are split over
-several workgroups). Inputs are the seeded synthetic workload, resident in
+summaries with the append and the refresh of the block the token lands in
+(score_kernel), then normalisers + selection + exact attention with Mean
+compensation (step_kernel; when a unit's kept blocks are split over several
+workgroups, the last of them merges the parts). Inputs are the seeded synthetic workload, resident in
 HBM before timing. Steps rotate over R copies of the layer ("layers") at
 distinct addresses so the per-step working set cannot stay in the 256 MB
 Infinity Cache.
@@ -532,7 +532,7 @@ def main():
                      "avg_launch_us": round(main_res["score_ms"] * 1e3, 3),
                      "median_sweep_us_per_launch": round(main_res["score_ms_median"] * 1e3, 3),
                      "timing": "HIP events around back-to-back launches (one per layer)"},
-        "finish_kernels": {"kernels": "step_kernel + step_merge_kernel (cknv_decode_finish)",
+        "finish_kernels": {"kernels": "step_kernel (cknv_decode_finish)",
                            "avg_us": round(main_res["finish_ms"] * 1e3, 3),
                            "algorithmic_bytes": main_res["attend_bytes"]},
         "three_call_path": {"steps_per_s": round(1000.0 / main_res["ms_three_calls"], 2),
