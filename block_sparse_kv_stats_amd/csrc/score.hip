@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   __shared__ __align__(16) float cacc[kScoreWaves * G * D];  // per-wave compensation sums
   __shared__ float cml[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of z̄
   __shared__ float cma[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of a
+  __shared__ __align__(16) float4 q_s[G * D / 4];            // the G query heads
 
   if ((int)blockIdx.x < a.nfresh) {
     fresh_block<D, G>(a, blockIdx.x);
@@ -251,14 +252,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // Block indices are clamped into [0, MB); blocks past the scored range are
   // masked once seq_len has arrived.
   const int T = a.seq_len[s];
-  float4 qv[G][KC];
-  {
-    const float4* q4 = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D);
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < KC; ++i) qv[g][i] = q4[g * (D / 4) + j + 16 * i];
-  }
+  // the query goes to LDS (registers are what limits resident waves here)
+  static_assert(G * D / 4 <= kScoreThreads, "one float4 of q per thread");
+  const float4 qown = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : 0];
   float4 kv[ROWS][KC], vv[ROWS][KC];
   DbarTile<DM, ROWS, KC> dt;
   const float4* kbar4 = reinterpret_cast<const float4*>(a.kbar);
@@ -279,6 +275,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // Keep the load block above: without this the scheduler sinks loads next
   // to their uses and the wave pays several dependent memory round trips.
   __builtin_amdgcn_sched_barrier(0);
+  if (tid < G * D / 4) q_s[tid] = qown;
+  lds_barrier();
 
   int NB = a.closed_only ? T / kBlock : (T + kBlock - 1) / kBlock;
   NB = NB < MB ? NB : MB;
@@ -288,14 +286,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // then summed over the block's 16 lanes, transposed: lane j ends with (tb, tg).
   float x[2 * NP];
 #pragma unroll
-  for (int rw = 0; rw < ROWS; ++rw) {
+  for (int g = 0; g < G; ++g) {
+    float4 qg[KC];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int i = 0; i < KC; ++i) qg[i] = q_s[g * (D / 4) + j + 16 * i];
+#pragma unroll
+    for (int rw = 0; rw < ROWS; ++rw) {
       float zp = 0.f, sp = 0.f;
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
-        zp += dot4(kv[rw][i], qv[g][i]);
-        sp += dt.qsq_dot(qv[g][i], rw, i);
+        zp += dot4(kv[rw][i], qg[i]);
+        sp += dt.qsq_dot(qg[i], rw, i);
       }
       x[2 * (rw + ROWS * g)] = zp;
       x[2 * (rw + ROWS * g) + 1] = sp;
