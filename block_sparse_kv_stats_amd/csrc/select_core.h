@@ -8,6 +8,21 @@ namespace cknv {
 
 constexpr int kListMax = 256;  // pivot-bin keys ranked exactly; more go to the radix fallback
 
+// Inclusive prefix sum over the 64 lanes of a wave without the LDS: a
+// log-step scan inside each 16-lane row (DPP row_shr 1, 2, 4, 8; lanes
+// shifted in from outside the row read 0), then each row adds the totals of
+// the rows before it (read from lanes 15, 31, 47).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_mov_dpp(x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_mov_dpp(x, 0x118, 0xF, 0xF, true);
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
 // Wave 0: the bin of `hist` (NBINS bins, higher bin = larger keys) holding
 // the krem-th largest counted key; writes (bin, rank within the bin, count
 // in the bin) to ctl[0..2]. Lane l owns bins [l*PER, (l+1)*PER).
@@ -23,13 +38,9 @@ __device__ __forceinline__ void find_bin(const int* hist, int krem, int* ctl) {
     cs[i] = v.x + v.y + v.z + v.w;
     own += cs[i];
   }
-  int above = own;  // inclusive suffix over lanes >= lane
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_down(above, o);
-    if (lane + o < 64) above += y;
-  }
-  int cum = above - own;  // keys in bins of higher lanes
+  const int incl = wave_incl_scan(own);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  int cum = total - incl;  // keys in bins of higher lanes
   if (cum < krem && krem <= cum + own) {  // this lane holds the bin
     int ci = 0, cb = cum;                  // chunk holding it, keys above that chunk
     int c = cum;
@@ -79,12 +90,7 @@ __device__ __forceinline__ void tile_prefix(uint64_t flags, int (&before)[NTILE]
       v[k] = i < E ? cnt[i] : 0;
       own += v[k];
     }
-    int incl = own;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(own);
     int run = incl - own;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {

@@ -217,10 +217,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   constexpr int CPL = C::CPL, RPF = C::RPF, RPW = C::RPW;
   constexpr int W = rec_words(D);
   // LDS: area A holds the score-group factors during the keys, then the
-  // query and the waves' attention records; area B the selection scratch.
+  // waves' attention records; the query has its own array.
   constexpr int NBITS = (KPT * NT + 31) / 32;  // kept-block bitmap of the pivot-bin path
-  constexpr int A_WORDS = NGMAX * G > NW * G * W + G * D ? NGMAX * G : NW * G * W + G * D;
+  constexpr int A_WORDS = NGMAX * G > NW * G * W ? NGMAX * G : NW * G * W;
   __shared__ __align__(16) float areaA[A_WORDS];
+  __shared__ __align__(16) float q_l[G * D];  // the G query heads
   __shared__ __align__(16) int hist[2048];
   __shared__ uint32_t lkey[kListMax];
   __shared__ int lidx[kListMax];
@@ -232,7 +233,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   __shared__ __align__(16) float pbuf[AW * 16 * G];  // attending waves' tile probabilities
   float* fgrp = areaA;                   // [NGMAX][G] exp(group max - LSE_g)
   float* recs = areaA;                   // [NW][G][W] after the selection
-  float* q_l = areaA + NW * G * W;       // [G][D] after the selection
 
   const int P = a.P;
   const int unit = blockIdx.x / P, p = blockIdx.x - unit * P;
@@ -306,6 +306,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
+#pragma unroll
+  for (int k = 0; k < NQ4; ++k) {
+    const int i = tid + k * NT;
+    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
+  }
   const bool app = step_appends(T0, a.cap_blocks, MB);
   const int T = T0 + (app ? 1 : 0);
   int NB = (T + kBlock - 1) / kBlock;
@@ -470,15 +475,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
 
   // ================================================================ compact
-  // The query goes to LDS now, into area A (the factors are dead once every
-  // wave is past its keys); the prefix barriers below order it before the
-  // attention reads it.
-  lds_barrier();
-#pragma unroll
-  for (int k = 0; k < NQ4; ++k) {
-    const int i = tid + k * NT;
-    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
-  }
   const bool ties_by_index = count && !use_list;
   int eq_before[KPT];
   if (ties_by_index) {
