@@ -36,7 +36,8 @@ __device__ __forceinline__ void load_block_words(const uint16_t* kc, const uint1
 // dl[e] = D̄ of the group holding coordinate l*VPL + e (the same in every
 // lane of the group). Mean and variance are two passes over the tokens in
 // order; each group's variances are summed as a balanced pairwise tree
-// (in-lane pair, then lane butterflies). Every lane of the wave must call it.
+// (in-lane pair, then lane butterflies: every step adds the same two values
+// in both lanes). Every lane of the wave must call it.
 template <int D>
 __device__ __forceinline__ void block_summary(const uint32_t (&fk)[16], const uint32_t (&fv)[16],
                                               int n, int r, float (&km)[D / 64],
@@ -60,7 +61,15 @@ __device__ __forceinline__ void block_summary(const uint32_t (&fk)[16], const ui
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < VPL; ++e) part += kvr[e];
-    for (int o = 1; o < gs / VPL; o <<= 1) part += __shfl_xor(part, o);
+    switch (gs / VPL) {  // lanes per group: a butterfly sum (DPP and row swaps)
+      case 2: part = group_sum<2>(part); break;
+      case 4: part = group_sum<4>(part); break;
+      case 8: part = group_sum<8>(part); break;
+      case 16: part = group_sum<16>(part); break;
+      case 32: part = group_sum<32>(part); break;
+      case 64: part = group_sum<64>(part); break;
+      default: break;
+    }
 #pragma unroll
     for (int e = 0; e < VPL; ++e) dl[e] = part / (float)gs;
   } else {
