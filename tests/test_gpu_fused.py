@@ -262,3 +262,36 @@ def test_fused_halves_equal_one_call():
                                          cache.kbar, cache.seq_len)])
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name,prefill", [("llama8b_32k", 9999), ("qwen8b_128k", 16 * 3000 + 5)])
+def test_fused_finish_repeats_bitwise(name, prefill):
+    """With several parts per unit, the part that completes a unit's count
+    merges the parts and resets the count: cknv_decode_finish run three times
+    after one cknv_decode_score gives the same bits each time, and the same
+    bits as cknv_decode_step."""
+    w = synth.WORKLOADS[name].replace(prefill=(prefill,))
+    data = synth.gen_layer(w)
+    mb = w.max_blocks_after(0)
+    q = torch.from_numpy(data["q"][0]).cuda()
+    nk, nv = gu.new_token(data, list(data["prefill"]))
+    cache = gu.upload(w, data, max_blocks=mb)
+    dec = fused_dec(cache, mb, w.budget)
+    b = cknv.BoundStep(cache, mb, w.budget, dec.ws, dec.sel, dec.n_sel, dec.out, dec.lse, q, nk, nv,
+                       torch.cuda.current_stream(), scores=dec.scores)
+    say(f"{name}: P = {-(-w.Kb // 4)} parts per unit")
+    b.decode_score()
+    res = []
+    for rep in range(3):
+        b.decode_finish()
+        torch.cuda.synchronize()
+        res.append([t.clone() for t in (dec.out, dec.lse, dec.sel, dec.n_sel, cache.seq_len)])
+    for r in res[1:]:
+        for x, y in zip(res[0], r):
+            assert torch.equal(x, y)
+    cache2 = gu.upload(w, data, max_blocks=mb)
+    dec2 = fused_dec(cache2, mb, w.budget)
+    dec2(q, nk, nv)
+    torch.cuda.synchronize()
+    for x, y in zip(res[0], (dec2.out, dec2.lse, dec2.sel, dec2.n_sel, cache2.seq_len)):
+        assert torch.equal(x, y)
