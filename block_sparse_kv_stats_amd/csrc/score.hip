@@ -37,8 +37,13 @@ namespace cknv {
 
 namespace {
 
-// How a lane's 4 coordinates 4c..4c+3 map to D̄ entries (group size gs = d/r).
-enum DbarMode { kDbarOne = 0, kDbarPair = 1, kDbarQuad = 2 };  // gs >= 4, gs == 2, gs == 1
+// How σ̂² is formed. kDbarRow (r <= 8): per (block, head) from the block's r
+// D̄ entries and the head's r group energies E_t = sum_{i in G_t} q_i^2, the
+// page's form. Otherwise per coordinate and summed over the block's lanes
+// with z̄; then how a lane's 4 coordinates 4c..4c+3 map to D̄ entries (group
+// size gs = d/r).
+enum DbarMode { kDbarOne = 0, kDbarPair = 1, kDbarQuad = 2, kDbarRow = 3 };  // gs >= 4, gs == 2, gs == 1; r <= 8
+constexpr int kRowMaxR = 8;
 
 __device__ __forceinline__ float dot4(const float4 a, const float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
@@ -67,6 +72,11 @@ struct DbarTile<kDbarPair, ROWS, KC> {
   __device__ float qsq_dot(const float4 q, int rw, int i) const {
     return (q.x * q.x + q.y * q.y) * x[rw][i].x + (q.z * q.z + q.w * q.w) * x[rw][i].y;
   }
+};
+template <int ROWS, int KC>
+struct DbarTile<kDbarRow, ROWS, KC> {  // unused: σ̂² is formed per (block, head)
+  __device__ void load(const float*, size_t, int, int, int, int, int) {}
+  __device__ float qsq_dot(const float4, int, int) const { return 0.f; }
 };
 template <int ROWS, int KC>
 struct DbarTile<kDbarQuad, ROWS, KC> {
@@ -122,6 +132,21 @@ __device__ __forceinline__ void reduce_rows16(float (&x)[CAP], int j) {
   if constexpr (NP >= 8) transposed_step<2, (NP >= 16 ? N / 2 : N)>(x, (j & 4) != 0);
   if constexpr (NP >= 4) transposed_step<1, (NP >= 16 ? N / 4 : NP >= 8 ? N / 2 : N)>(x, (j & 2) != 0);
   transposed_step<0, 4>(x, (j & 1) != 0);
+}
+
+// Sum over the 16 lanes of each row of NP values per lane (value index i <
+// NP). Afterwards x[0] of lane j holds the sum for i = j & (NP-1).
+template <int NP, int CAP>
+__device__ __forceinline__ void reduce_rows16_1(float (&x)[CAP]) {
+  const int j = threadIdx.x & 15;
+  if constexpr (NP < 16) plain_step<3, NP>(x);
+  if constexpr (NP < 8) plain_step<2, NP>(x);
+  if constexpr (NP < 4) plain_step<1, NP>(x);
+  if constexpr (NP < 2) plain_step<0, NP>(x);
+  if constexpr (NP >= 16) transposed_step<3, 16>(x, (j & 8) != 0);
+  if constexpr (NP >= 8) transposed_step<2, 8>(x, (j & 4) != 0);
+  if constexpr (NP >= 4) transposed_step<1, 4>(x, (j & 2) != 0);
+  if constexpr (NP >= 2) transposed_step<0, 2>(x, (j & 1) != 0);
 }
 
 // Max / sum over the SEG consecutive lanes (SEG = 2 or 4) of each aligned segment.
@@ -230,6 +255,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   __shared__ float cml[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of z̄
   __shared__ float cma[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of a
   __shared__ __align__(16) float4 q_s[G * D / 4];            // the G query heads
+  __shared__ float e_s[G * kRowMaxR];                        // kDbarRow: group energies E[g][t]
 
   if ((int)blockIdx.x < a.nfresh) {
     fresh_block<D, G>(a, blockIdx.x);
@@ -271,40 +297,83 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       dt.load(a.dbar, row, c, r, D, rw, i);
     }
   }
-  const float n = a.cnt[ubase + (tb < MB ? tb : MB - 1)];
+  const size_t trow_idx = ubase + (tb < MB ? tb : MB - 1);
+  const float n = a.cnt[trow_idx];
+  float dbr[kRowMaxR];  // kDbarRow: D̄ of this lane's block tb
+  if constexpr (DM == kDbarRow) {
+#pragma unroll
+    for (int t = 0; t < kRowMaxR; ++t) dbr[t] = t < r ? a.dbar[trow_idx * r + t] : 0.f;
+  }
   // Keep the load block above: without this the scheduler sinks loads next
   // to their uses and the wave pays several dependent memory round trips.
   __builtin_amdgcn_sched_barrier(0);
   if (tid < G * D / 4) q_s[tid] = qown;
   lds_barrier();
+  if constexpr (DM == kDbarRow) {
+    // E[g][t]: thread g*r + t sums its group's squared coordinates
+    if (tid < G * r) {
+      const int g = tid / r, t = tid - g * r, gs4 = D / r / 4;
+      const float4* qg = q_s + g * (D / 4) + t * gs4;
+      float e = 0.f;
+      for (int c = 0; c < gs4; ++c) e += qg[c].x * qg[c].x + qg[c].y * qg[c].y + qg[c].z * qg[c].z + qg[c].w * qg[c].w;
+      e_s[g * kRowMaxR + t] = e;
+    }
+    lds_barrier();
+  }
 
   int NB = a.closed_only ? T / kBlock : (T + kBlock - 1) / kBlock;
   NB = NB < MB ? NB : MB;
   const float invd = 1.0f / (float)D;
 
-  // ---- z̄ and σ̂² partials over the lane's coordinates for every (row, head),
-  // then summed over the block's 16 lanes, transposed: lane j ends with (tb, tg).
-  float x[2 * NP];
+  // ---- z̄ (and, per coordinate, σ̂²) partials over the lane's coordinates for
+  // every (row, head), then summed over the block's 16 lanes, transposed: lane
+  // j ends with (tb, tg).
+  float z, s2;
+  if constexpr (DM == kDbarRow) {
+    float x[NP];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float4 qg[KC];
+    for (int g = 0; g < G; ++g) {
+      float4 qg[KC];
 #pragma unroll
-    for (int i = 0; i < KC; ++i) qg[i] = q_s[g * (D / 4) + j + 16 * i];
+      for (int i = 0; i < KC; ++i) qg[i] = q_s[g * (D / 4) + j + 16 * i];
 #pragma unroll
-    for (int rw = 0; rw < ROWS; ++rw) {
-      float zp = 0.f, sp = 0.f;
+      for (int rw = 0; rw < ROWS; ++rw) {
+        float zp = 0.f;
 #pragma unroll
-      for (int i = 0; i < KC; ++i) {
-        zp += dot4(kv[rw][i], qg[i]);
-        sp += dt.qsq_dot(qg[i], rw, i);
+        for (int i = 0; i < KC; ++i) zp += dot4(kv[rw][i], qg[i]);
+        x[rw + ROWS * g] = zp;
       }
-      x[2 * (rw + ROWS * g)] = zp;
-      x[2 * (rw + ROWS * g) + 1] = sp;
     }
+    reduce_rows16_1<NP>(x);
+    z = x[0] * a.isd;
+    float sp = 0.f;
+#pragma unroll
+    for (int t = 0; t < kRowMaxR; ++t) sp += t < r ? e_s[tg * kRowMaxR + t] * dbr[t] : 0.f;
+    s2 = sp * invd;
+  } else {
+    float x[2 * NP];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float4 qg[KC];
+#pragma unroll
+      for (int i = 0; i < KC; ++i) qg[i] = q_s[g * (D / 4) + j + 16 * i];
+#pragma unroll
+      for (int rw = 0; rw < ROWS; ++rw) {
+        float zp = 0.f, sp = 0.f;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+          zp += dot4(kv[rw][i], qg[i]);
+          sp += dt.qsq_dot(qg[i], rw, i);
+        }
+        x[2 * (rw + ROWS * g)] = zp;
+        x[2 * (rw + ROWS * g) + 1] = sp;
+      }
+    }
+    reduce_rows16<NP>(x, j);
+    z = x[0] * a.isd;
+    s2 = x[1] * invd;
   }
-  reduce_rows16<NP>(x, j);
   const bool tv = tb < NB && j < NP;  // a valid block, and not a duplicate lane (NP < 16)
-  const float z = x[0] * a.isd, s2 = x[1] * invd;
 
   // ---- scoring partials of this wave's group: a = ln|b| + z̄ + σ̂²/2, and
   // u = e^{a - group max} σ̂². The first-order-mass ablation drops σ̂²/2 from a,
@@ -436,11 +505,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const int gs = d / a.r;
-  const int dm = gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
+  const int dm = a.r <= kRowMaxR ? kDbarRow : gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
   const void* f = nullptr;
   const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
 #define CKNV_SCORE_NC(DD, GG, RR, NC)                                             \
-  f = dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR, NC>        \
+  f = dm == kDbarRow ? (const void*)score_kernel<DD, GG, kDbarRow, RR, NC>        \
+    : dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR, NC>        \
     : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair, RR, NC>      \
                       : (const void*)score_kernel<DD, GG, kDbarQuad, RR, NC>;
 #define CKNV_SCORE_R(DD, GG, RR)                                                  \
