@@ -241,10 +241,24 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
   if (h == 0 && lane == 0) a.t0_out[s] = T0;
 }
 
+// Deferred mean values: with 4 rows of 4 query heads and σ̂² per (block,
+// head), v̄ is loaded once z̄ and σ̂² are formed, so k̄ and v̄ are never live
+// together and 5 waves fit per SIMD: a grid of 4096 scoring waves plus the
+// append workgroups is then resident in one round on 256 CUs. The loads of
+// v̄ overlap the scoring partials; the memory pipe stays full with the other
+// waves' loads.
+template <int G, int DM, int ROWS, bool NC>
+constexpr bool score_defers_vbar() { return !NC && DM == kDbarRow && G == 4 && ROWS == 4; }
+template <int G, int DM, int ROWS, bool NC>
+constexpr int score_waves_per_simd() { return score_defers_vbar<G, DM, ROWS, NC>() ? 5 : 1; }
+
 // NC: the no-compensation ablation; the mean values are neither read nor summed.
 template <int D, int G, int DM, int ROWS, bool NC>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads)
+__attribute__((amdgpu_waves_per_eu(score_waves_per_simd<G, DM, ROWS, NC>())))
+void score_kernel(ScoreArgs a) {
   constexpr int KC = D / 64;              // float4 chunks per lane per block (16 lanes per block)
+  constexpr bool kDeferV = score_defers_vbar<G, DM, ROWS, NC>();
   constexpr int E = 4 * KC;               // coordinates per lane
   // ROWS: blocks per lane, base + 4*row + (lane >> 4)
   constexpr int NP = ROWS * G;            // (row, head) pairs of a 16-lane row
@@ -293,7 +307,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     for (int i = 0; i < KC; ++i) {
       const int c = j + 16 * i;  // float4 chunk: coordinates 4c..4c+3
       kv[rw][i] = stream_load4(kbar4 + row * (D / 4) + c);
-      if constexpr (!NC) vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + c);
+      if constexpr (!NC && !kDeferV) vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + c);
       dt.load(a.dbar, row, c, r, D, rw, i);
     }
   }
@@ -372,6 +386,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     reduce_rows16<NP>(x, j);
     z = x[0] * a.isd;
     s2 = x[1] * invd;
+  }
+  if constexpr (kDeferV) {
+#pragma unroll
+    for (int rw = 0; rw < ROWS; ++rw) {
+      const int b = base + 4 * rw + bg;
+      const size_t row = ubase + (b < MB ? b : MB - 1);
+#pragma unroll
+      for (int i = 0; i < KC; ++i) vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + j + 16 * i);
+    }
   }
   const bool tv = tb < NB && j < NP;  // a valid block, and not a duplicate lane (NP < 16)
 
