@@ -64,6 +64,64 @@ __device__ __forceinline__ void find_bin(const int* hist, int krem, int* ctl) {
   }
 }
 
+// A pivot-bin key and its block index as one word that orders like the
+// selection, (key desc, index asc): the key in the high half, the index's
+// complement in the low half. Every such word is nonzero, so zero words can
+// pad a list without ranking above any entry.
+__device__ __forceinline__ uint64_t rank_word(uint32_t key, int idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
+}
+
+// Append this thread's flagged items to list[*counter ..): item m (bit m of
+// `flags`) is block idx0 + m*stride with key keys[m]. One LDS atomic per
+// wave reserves the wave's slots; ballots give each lane its place. Every
+// lane of the wave calls this.
+template <int NTILE>
+__device__ __forceinline__ void list_append(uint64_t flags, const uint32_t (&keys)[NTILE], int idx0,
+                                            int stride, uint64_t* list, int* counter) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t bal[NTILE];
+  int tot = 0;
+#pragma unroll
+  for (int m = 0; m < NTILE; ++m) {
+    bal[m] = __ballot((flags >> m) & 1u);
+    tot += __popcll(bal[m]);
+  }
+  int base = 0;
+  if (lane == 0 && tot > 0) base = atomicAdd(counter, tot);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int m = 0; m < NTILE; ++m) {
+    if ((flags >> m) & 1u) list[base + __popcll(bal[m] & below)] = rank_word(keys[m], idx0 + m * stride);
+    base += __popcll(bal[m]);
+  }
+}
+
+// Ranks of the n words of `list` (followed by at least kListPad zero words):
+// an entry is kept when fewer than krem entries order above it; its block's
+// bit is set in keep_bits. Thread t ranks entries t, t+NT, ...; 32 words are
+// read per LDS round trip.
+constexpr int kListPad = 32;
+template <int NT>
+__device__ __forceinline__ void rank_list_keep(const uint64_t* list, int n, int krem, uint32_t* keep_bits) {
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint64_t ci = list[i];
+    int rank = 0;
+    for (int j0 = 0; j0 < n; j0 += kListPad) {
+      ulonglong2 v[kListPad / 2];
+#pragma unroll
+      for (int e = 0; e < kListPad / 2; ++e) v[e] = reinterpret_cast<const ulonglong2*>(list + j0)[e];
+#pragma unroll
+      for (int e = 0; e < kListPad / 2; ++e) rank += (int)(v[e].x > ci) + (int)(v[e].y > ci);
+    }
+    if (rank < krem) {
+      const int ii = (int)(0xffffffffu - (uint32_t)ci);
+      atomicOr(&keep_bits[ii >> 5], 1u << (ii & 31));
+    }
+  }
+}
+
 // Exclusive prefix over items in tile-major order: tile m holds items
 // m*NT .. m*NT+NT-1 (thread t's item of tile m is m*NT + t); bit m of
 // `flags` is this thread's flag in tile m. before[m] gets the number of

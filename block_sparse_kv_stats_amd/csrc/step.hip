@@ -223,8 +223,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   __shared__ __align__(16) float areaA[A_WORDS];
   __shared__ __align__(16) float q_l[G * D];  // the G query heads
   __shared__ __align__(16) int hist[2048];
-  __shared__ uint32_t lkey[kListMax];
-  __shared__ int lidx[kListMax];
+  __shared__ __align__(16) uint64_t plist[kListMax + kListPad];  // pivot-bin (key, index) words
   __shared__ uint32_t keep_bits[NBITS];
   __shared__ int cnt[KPT * NW + 1];
   __shared__ float scl[NW * G + 2 * G];
@@ -325,6 +324,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   const bool count = !all && krem > 0;
   for (int i = tid; i < 2048; i += NT) hist[i] = 0;
   for (int i = tid; i < NBITS; i += NT) keep_bits[i] = 0u;
+  for (int i = tid; i < kListMax + kListPad; i += NT) plist[i] = 0ull;
   if (tid == 0) ctl[3] = 0;
 
   // ================================================================ LSE
@@ -419,33 +419,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     use_list = ctl[2] <= kListMax;
     if (use_list) {
       // the pivot bin's keys, ordered exactly by (key desc, index asc); the first krem are kept
+      uint64_t pin = 0u;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        if (((candm >> j) & 1u) && (key[j] >> 21) == tau_bin) {
-          const int slot = atomicAdd(&ctl[3], 1);
-          lkey[slot] = key[j];
-          lidx[slot] = tid + j * NT;
-        }
-      }
+      for (int j = 0; j < KPT; ++j) pin |= (uint64_t)(((candm >> j) & 1u) && (key[j] >> 21) == tau_bin) << j;
+      list_append<KPT>(pin, key, tid, NT, plist, &ctl[3]);
       lds_barrier();
       const int n = ctl[3];
-      for (int i = tid; i < n; i += NT) {
-        const uint32_t ki = lkey[i];
-        const int ii = lidx[i];
-        int rank = 0;
-        for (int j0 = 0; j0 < n; j0 += 8) {
-          uint32_t kj[8];
-          int ij[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kj[e] = j0 + e < n ? lkey[j0 + e] : 0u;
-            ij[e] = j0 + e < n ? lidx[j0 + e] : 0x7fffffff;
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) rank += (kj[e] > ki) || (kj[e] == ki && ij[e] < ii);
-        }
-        if (rank < krem) atomicOr(&keep_bits[ii >> 5], 1u << (ii & 31));
-      }
+      rank_list_keep<NT>(plist, n, krem, keep_bits);
       lds_barrier();
     } else {
       // long runs of equal keys: pin the exact threshold key with two more radix passes
