@@ -206,6 +206,7 @@ static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv
   sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
   sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf;
   sa.bpw_shift = p.bpw == 8 ? 3 : 4;
+  sa.xcd = (p.U % 8) == 0;
   sa.flags = (int)shape->flags;
   sa.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_step(shape->d, shape->G, sa, p.U, (hipStream_t)stream));

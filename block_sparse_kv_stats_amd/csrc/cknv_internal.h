@@ -106,6 +106,7 @@ struct StepArgs {
   const float* finfo;  // per unit and query head: (a, factor) of the block the token landed in
   uint32_t* pcnt;      // per unit: parts done this step (zeroed by the scoring launch)
   int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P, bpw_shift;
+  int xcd;    // units a multiple of 8: a unit's parts share the XCD that scored it
   int flags;  // CKNV_FLAG_* (ablation variants)
   float isd;
 };

@@ -122,6 +122,49 @@ __device__ __forceinline__ void rank_list_keep(const uint64_t* list, int n, int 
   }
 }
 
+// The same exclusive prefix for callers that walk the tiles in rolled loops
+// (short code: every line of a long unrolled sequence is fetched once per
+// CU): returns, in lane m < NTILE of each wave, the number of flagged items
+// ahead of the wave's first item of tile m (read per tile with readlane);
+// the total goes to *total. `cnt`: LDS scratch of NTILE*NW + 1 ints. Every
+// thread calls this.
+template <int NTILE, int NW>
+__device__ __forceinline__ int tile_bases(uint64_t flags, int* cnt, int& total) {
+  static_assert(NTILE <= 64, "one lane per tile");
+  constexpr int E = NTILE * NW;
+  constexpr int PER = (E + 63) / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int mine = 0;
+#pragma unroll 1
+  for (int m = 0; m < NTILE; ++m) {
+    const int c = __popcll(__ballot((flags >> m) & 1u));
+    mine = lane == m ? c : mine;
+  }
+  if (lane < NTILE) cnt[lane * NW + wave] = mine;
+  lds_barrier();
+  if (wave == 0) {
+    int v[PER], own = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = lane * PER + k;
+      v[k] = i < E ? cnt[i] : 0;
+      own += v[k];
+    }
+    const int incl = wave_incl_scan(own);
+    int run = incl - own;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = lane * PER + k;
+      if (i < E) cnt[i] = run;
+      run += v[k];
+    }
+    if (lane == 63) cnt[E] = incl;
+  }
+  lds_barrier();
+  total = cnt[E];
+  return lane < NTILE ? cnt[lane * NW + wave] : 0;
+}
+
 // Exclusive prefix over items in tile-major order: tile m holds items
 // m*NT .. m*NT+NT-1 (thread t's item of tile m is m*NT + t); bit m of
 // `flags` is this thread's flag in tile m. before[m] gets the number of

@@ -234,7 +234,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   float* recs = areaA;                   // [NW][G][W] after the selection
 
   const int P = a.P;
-  const int unit = blockIdx.x / P, p = blockIdx.x - unit * P;
+  // the parts of a unit run on the XCD whose L2 the scoring pass wrote that
+  // unit's workspace through
+  int unit, p;
+  map_wg(blockIdx.x, a.S * a.H, P, a.xcd, unit, p);
   const int s = unit / a.H, h = unit - s * a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int MB = a.max_blocks, Kb = a.Kb, NC = a.C;
@@ -410,6 +413,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   uint32_t tau_bin = 0xffffffffu;
   bool use_list = true;
   uint32_t exact_tau = 0u;
+  uint64_t pin = 0u, gtm = 0u;  // candidates in the pivot bin / in higher bins
   if (count) {
     lds_barrier();
     if (wave == 0) find_bin<2048>(hist, krem, ctl);
@@ -419,9 +423,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     use_list = ctl[2] <= kListMax;
     if (use_list) {
       // the pivot bin's keys, ordered exactly by (key desc, index asc); the first krem are kept
-      uint64_t pin = 0u;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) pin |= (uint64_t)(((candm >> j) & 1u) && (key[j] >> 21) == tau_bin) << j;
+      for (int j = 0; j < KPT; ++j) {
+        const bool c = (candm >> j) & 1u;
+        const uint32_t kb = key[j] >> 21;
+        pin |= (uint64_t)(c && kb == tau_bin) << j;
+        gtm |= (uint64_t)(c && kb > tau_bin) << j;
+      }
       list_append<KPT>(pin, key, tid, NT, plist, &ctl[3]);
       lds_barrier();
       const int n = ctl[3];
@@ -471,11 +479,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     for (int j = 0; j < KPT; ++j) takem |= (uint64_t)(tid + j * NT < NB) << j;
   } else {
     uint64_t forced = 0u, above = 0u;
+    // blocks 0, NB-2 and NB-1, set in their owners' masks
+    const int fbl[3] = {0, NB - 2, NB - 1};
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int b = tid + j * NT;
-      forced |= (uint64_t)(b < NB && (b == 0 || b >= NB - 2)) << j;
-    }
+    for (int k = 0; k < 3; ++k)
+      if (fbl[k] >= 0 && fbl[k] % NT == tid) forced |= 1ull << (fbl[k] / NT);
     if (ties_by_index) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
@@ -483,28 +491,30 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
         above |= (uint64_t)(c && (key[j] > exact_tau || (key[j] == exact_tau && eq_before[j] < krem))) << j;
       }
     } else if (count) {
-      uint32_t kw[KPT];
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) kw[j] = keep_bits[(tid + j * NT) >> 5];
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
+      // every candidate of a higher bin, and the pivot-bin keys the rank kept
+      uint64_t kp = 0u;
+      for (uint64_t m = pin; m; m &= m - 1) {
+        const int j = __builtin_ctzll(m);
         const int b = tid + j * NT;
-        const bool c = (candm >> j) & 1u;
-        above |= (uint64_t)(c && ((key[j] >> 21) > tau_bin || ((kw[j] >> (b & 31)) & 1u))) << j;
+        kp |= (uint64_t)((keep_bits[b >> 5] >> (b & 31)) & 1u) << j;
       }
+      above = gtm | kp;
     }
     takem = forced | above;
   }
-  int before[KPT], nk;
-  tile_prefix<KPT, NW>(takem, before, cnt, nk);
+  int nk;
+  const int tbase = tile_bases<KPT, NW>(takem, cnt, nk);
   int32_t* sel = a.sel + (size_t)unit * Kb;
   const int lo = p * KPART;
-#pragma unroll
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll 1
   for (int j = 0; j < KPT; ++j) {
+    const uint64_t bal = __ballot((takem >> j) & 1u);
     if ((takem >> j) & 1u) {
-      const int pos = before[j];
-      if (p == 0 && pos < Kb) sel[pos] = tid + j * NT;
-      if (pos >= lo && pos < lo + KPART) klist[pos - lo] = tid + j * NT;
+      const int pos = __builtin_amdgcn_readlane(tbase, j) + __popcll(bal & below);
+      const int b = tid + j * NT;
+      if (p == 0 && pos < Kb) sel[pos] = b;
+      if (pos >= lo && pos < lo + KPART) klist[pos - lo] = b;
     }
   }
   nk = nk < Kb ? nk : Kb;  // the selection keeps exactly min(Kb, NB); never index past sel
