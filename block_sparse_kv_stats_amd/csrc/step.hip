@@ -278,6 +278,14 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) gp[k][g] = grp[(size_t)gc * G + g];
   }
+  constexpr int NQ4 = (G * D / 4 + NT - 1) / NT;
+  float4 q4[NQ4];
+#pragma unroll
+  for (int k = 0; k < NQ4; ++k) {
+    const int i = tid + k * NT;
+    q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
+  }
+  // the u terms last: the normalisers need only what came before them
   float uv[UB][G];
 #pragma unroll
   for (int j = 0; j < UB; ++j) {
@@ -285,13 +293,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     const int bc = b < MB ? b : MB - 1;
 #pragma unroll
     for (int g = 0; g < G; ++g) uv[j][g] = u[(size_t)bc * G + g];
-  }
-  constexpr int NQ4 = (G * D / 4 + NT - 1) / NT;
-  float4 q4[NQ4];
-#pragma unroll
-  for (int k = 0; k < NQ4; ++k) {
-    const int i = tid + k * NT;
-    q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
   }
   // This part's chunk records are folded by the waves that attend no tile
   // (w >= AW), while the others attend: wave w folds records
@@ -308,11 +309,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-#pragma unroll
-  for (int k = 0; k < NQ4; ++k) {
-    const int i = tid + k * NT;
-    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
-  }
   const bool app = step_appends(T0, a.cap_blocks, MB);
   const int T = T0 + (app ? 1 : 0);
   int NB = (T + kBlock - 1) / kBlock;
@@ -354,6 +350,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g) fgrp[gi * G + g] = __expf(gp[k][g].x - lse_g[g]);
     }
+  }
+#pragma unroll
+  for (int k = 0; k < NQ4; ++k) {
+    const int i = tid + k * NT;
+    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
   }
   WaveState<D, G> st;
   st.init();
