@@ -144,12 +144,11 @@ __device__ __forceinline__ void fold_record(WaveState<D, G>& st, const RecordReg
 // The last part of a unit: merge the unit's P part records (written by the
 // other parts with agent-scope stores, so read with agent-scope loads) into
 // out and lse. Thread t owns output columns t + NT*k; records are read in
-// batches of 8, every load of a batch issued before the first use.
-template <int D, int G, int NT>
+// batches of PB, every load of a batch issued before the first use.
+template <int D, int G, int NT, int PB>
 __device__ void merge_parts(const float* parts, int P, float* out, float* lse) {
   constexpr int W = rec_words(D);
   constexpr int COLS = (G * D + NT - 1) / NT;  // output columns per thread
-  constexpr int PB = 8;                        // records per batch
   const int tid = threadIdx.x;
   auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   float M[COLS], L[COLS], A[COLS];
@@ -592,8 +591,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
   lds_barrier();
   if (!ctl[4]) return;
-  merge_parts<D, G, NT>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
-                        a.lse ? a.lse + (size_t)unit * G : nullptr);
+  // up to 32 parts in one batch (one round trip), else batches of 8
+  if (P > 8 && P <= 32)
+    merge_parts<D, G, NT, 32>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
+                              a.lse ? a.lse + (size_t)unit * G : nullptr);
+  else
+    merge_parts<D, G, NT, 8>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
+                             a.lse ? a.lse + (size_t)unit * G : nullptr);
   if (tid == 0) {
     __hip_atomic_store(a.pcnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (h == 0 && app) a.seq_len[s] = T;
