@@ -42,8 +42,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ float red[kSelWaves * G * 2];
   __shared__ __align__(16) int hist[2048];
   __shared__ int cnt[KPT * kSelWaves + 1];
-  __shared__ uint32_t lkey[kListMax];
-  __shared__ int lidx[kListMax];
+  __shared__ __align__(16) uint64_t plist[kListMax + kListPad];  // pivot-bin (key, index) words
   __shared__ uint32_t keep_bits[NW];
   __shared__ int ctl[8];
 
@@ -82,6 +81,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   hist[tid + kSelThreads] = 0;
   if (tid < NW) keep_bits[tid] = 0u;
   if (tid == 0) ctl[3] = 0;  // list length
+  if (tid < kListMax + kListPad) plist[tid] = 0ull;
 
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < MB ? NB : MB;
@@ -176,33 +176,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   uint32_t exact_tau = 0u;  // long-tie path: exact threshold key, ties by index
   if (krem > 0 && use_list) {
     // the pivot bin's keys, ordered exactly; the first krem are kept
+    uint64_t pin = 0u;
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-      if (((candm >> m) & 1u) && (key[m] >> 21) == tau_bin) {
-        const int slot = atomicAdd(&ctl[3], 1);
-        lkey[slot] = key[m];
-        lidx[slot] = tid + m * kSelThreads;
-      }
-    }
+    for (int m = 0; m < KPT; ++m) pin |= (uint64_t)(((candm >> m) & 1u) && (key[m] >> 21) == tau_bin) << m;
+    list_append<KPT>(pin, key, tid, kSelThreads, plist, &ctl[3]);
     lds_barrier();
-    const int n = ctl[3];
-    if (tid < n) {
-      const uint32_t ki = lkey[tid];
-      const int ii = lidx[tid];
-      int rank = 0;
-      for (int j0 = 0; j0 < n; j0 += 8) {
-        uint32_t kj[8];
-        int ij[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kj[e] = j0 + e < n ? lkey[j0 + e] : 0u;
-          ij[e] = j0 + e < n ? lidx[j0 + e] : 0x7fffffff;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rank += (kj[e] > ki) || (kj[e] == ki && ij[e] < ii);
-      }
-      if (rank < krem) atomicOr(&keep_bits[ii >> 5], 1u << (ii & 31));
-    }
+    rank_list_keep<kSelThreads>(plist, ctl[3], krem, keep_bits);
     lds_barrier();
   } else if (krem > 0) {
     uint32_t prefix = tau_bin << 21;
