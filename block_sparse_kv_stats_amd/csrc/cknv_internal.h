@@ -14,16 +14,15 @@ constexpr int kBlock = 16;          // tokens per block (CompKV page, "Assumptio
 constexpr int kThreads = 256;       // threads per workgroup of the score and attend kernels
 constexpr int kWaves = kThreads / 64;
 // Score-kernel geometry: a wave covers 4 blocks per row (16 lanes each) and
-// 2 or 4 rows (a score group of 8 or 16 blocks). Up to 4 query heads it is 4
-// rows: fewer, longer score groups and chunk records for the step kernel to
-// read, and measured a little faster than 2 rows even on the 32K grid; 8
-// query heads take 2 rows (registers). The selection works with either group
-// size.
+// 2 or 4 rows (a score group of 8 or 16 blocks; 2 rows at G = 8). Fewer rows
+// give more waves, which pays while the grid is small (measured at 32K with
+// the deferred mean values: 2 rows end the scoring pass 0.4 us sooner); the
+// workspace plan picks the rows. The selection works with either group size.
 constexpr int kScoreThreads = 256;  // score kernel: 4 waves per workgroup (one chunk record each)
 constexpr int kScoreWaves = kScoreThreads / 64;
 constexpr int kScoreMinGroup = 8;  // blocks of the smaller score group
-__host__ __device__ constexpr int score_rows(int G, int /*max_blocks*/, int /*units*/) {
-  return G >= 8 ? 2 : 4;
+__host__ __device__ constexpr int score_rows(int G, int max_blocks, int units) {
+  return G >= 8 ? 2 : G <= 2 ? 4 : ((long)units * ((max_blocks + 7) / 8) <= 4096 ? 2 : 4);
 }
 constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup

@@ -241,16 +241,16 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
   if (h == 0 && lane == 0) a.t0_out[s] = T0;
 }
 
-// Deferred mean values: with 4 rows of 4 query heads and σ̂² per (block,
-// head), v̄ is loaded once z̄ and σ̂² are formed, so k̄ and v̄ are never live
-// together and 5 waves fit per SIMD: a grid of 4096 scoring waves plus the
-// append workgroups is then resident in one round on 256 CUs. The loads of
-// v̄ overlap the scoring partials; the memory pipe stays full with the other
-// waves' loads.
+// Deferred mean values: at 4 query heads with σ̂² per (block, head), v̄ is
+// loaded once z̄ and σ̂² are formed. The first loads (k̄, D̄, |b|) then return
+// sooner, and the v̄ loads overlap the scoring partials (measured faster at
+// 32K and 128K). At 4 rows k̄ and v̄ are never live together, so 5 waves fit
+// per SIMD: a grid of 4096 scoring waves plus the append workgroups is then
+// resident in one round on 256 CUs.
 template <int G, int DM, int ROWS, bool NC>
-constexpr bool score_defers_vbar() { return !NC && DM == kDbarRow && G == 4 && ROWS == 4; }
+constexpr bool score_defers_vbar() { return !NC && DM == kDbarRow && G == 4; }
 template <int G, int DM, int ROWS, bool NC>
-constexpr int score_waves_per_simd() { return score_defers_vbar<G, DM, ROWS, NC>() ? 5 : 1; }
+constexpr int score_waves_per_simd() { return score_defers_vbar<G, DM, ROWS, NC>() && ROWS == 4 ? 5 : 1; }
 
 // NC: the no-compensation ablation; the mean values are neither read nor summed.
 template <int D, int G, int DM, int ROWS, bool NC>
