@@ -377,3 +377,32 @@ class BoundStep:
         st = self._dfinish(*self.dfinish_args)
         if st:
             raise CknvError(st, "cknv_decode_finish")
+
+
+class DecodeGraph:
+    """Decode steps of several layers captured as one HIP graph.
+
+    `steps` are BoundStep objects created on `stream`; each one's `method`
+    ("fused_step" for cknv_decode_step, "step" for the three calls) is
+    recorded once, in order, and replay() re-issues the whole sweep with one
+    launch. The kernels read the context length from the device-resident
+    seq_len, so every replay is the next decode step of every layer, with
+    whatever the bound q, new_k and new_v tensors hold at replay time; the
+    captured max_blocks bounds how many replays still append. Capture records
+    kernels only (no memset: the step's counters are reset by its kernels).
+    """
+
+    def __init__(self, steps, stream, method="fused_step"):
+        import torch
+        if method not in ("fused_step", "step"):
+            raise ValueError(f"method {method!r}: expected 'fused_step' or 'step'")
+        self.steps = list(steps)
+        self.graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.graph, stream=stream):
+            for b in self.steps:
+                getattr(b, method)()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()

@@ -295,3 +295,71 @@ def test_fused_finish_repeats_bitwise(name, prefill):
     torch.cuda.synchronize()
     for x, y in zip(res[0], (dec2.out, dec2.lse, dec2.sel, dec2.n_sel, cache2.seq_len)):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("method", ["fused_step", "step"])
+def test_graph_replay_of_layer_sweep_matches_eager(method):
+    """A HIP graph of one decode step per layer (three layers, several parts
+    per unit), replayed three times with new tokens and queries written into
+    the bound buffers between replays, gives the same bits as the same calls
+    issued eagerly on a twin set of layers, at every replay (eager work and
+    synchronisations run between the replays); the last replay also matches
+    the oracle."""
+    stream = torch.cuda.Stream()
+    reps, L = 3, 3
+    ws_ = [synth.WORKLOADS["llama8b_32k"].replace(cfg_id=90 + li, prefill=(3000 + 53 * li,),
+                                                   steps=reps) for li in range(L)]
+    datas = [synth.gen_layer(w) for w in ws_]
+
+    def make_twin():
+        layers = []
+        for w, data in zip(ws_, datas):
+            mb = w.max_blocks_after(reps - 1)
+            cache = gu.upload(w, data, max_blocks=mb)
+            dec = fused_dec(cache, mb, w.budget, want_scores=False)
+            q = torch.from_numpy(data["q"][0]).cuda()
+            nk, nv = gu.new_token(data, list(data["prefill"]))
+            b = cknv.BoundStep(cache, mb, w.budget, dec.ws, dec.sel, dec.n_sel, dec.out, dec.lse,
+                               q, nk, nv, stream)
+            layers.append((cache, dec, q, nk, nv, b))
+        return layers
+
+    def feed(layers, rep):
+        for (cache, dec, q, nk, nv, b), data in zip(layers, datas):
+            q.copy_(torch.from_numpy(data["q"][rep]))
+            k1, v1 = gu.new_token(data, [p + rep for p in data["prefill"]])
+            nk.copy_(k1)
+            nv.copy_(v1)
+        torch.cuda.synchronize()
+
+    def state(layers):
+        return [[t.clone() for t in (dec.out, dec.lse, dec.sel, dec.n_sel, cache.seq_len,
+                                     cache.kbar, cache.dbar, cache.cnt, cache.vbar, cache.k)]
+                for (cache, dec, q, nk, nv, b) in layers]
+
+    eager, graphed = make_twin(), make_twin()
+    g = cknv.DecodeGraph([x[5] for x in graphed], stream, method=method)
+    say(f"graph of {L} layers ({method}) captured")
+    for rep in range(reps):
+        feed(eager, rep)
+        with torch.cuda.stream(stream):
+            for x in eager:
+                getattr(x[5], method)()
+        torch.cuda.synchronize()
+        feed(graphed, rep)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        for la, lb in zip(state(eager), state(graphed)):
+            for a, b in zip(la, lb):
+                assert torch.equal(a, b), f"replay {rep}"
+        say(f"  replay {rep} equals eager")
+    w, data = ws_[-1], datas[-1]
+    cache, dec = graphed[-1][0], graphed[-1][1]
+    T = data["prefill"][0] + reps
+    assert int(cache.seq_len[0]) == T
+    sel, nsel = dec.sel.cpu().numpy(), dec.n_sel.cpu().numpy()
+    out, lse = dec.out.cpu().numpy(), dec.lse.cpu().numpy()
+    for h in (0, w.H - 1):
+        gu.check_unit(w, data, 0, h, T, reps - 1, data["q"][reps - 1], sel, nsel, out, lse, None,
+                      w.budget)
