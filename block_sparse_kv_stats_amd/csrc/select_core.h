@@ -122,6 +122,45 @@ __device__ __forceinline__ void rank_list_keep(const uint64_t* list, int n, int 
   }
 }
 
+// Append the flagged entries of this thread's run of blocks b0, b0+1, ...
+// (bit i of `flags`: block b0 + i, key keys[i]) to list[*counter ..): one
+// LDS atomic per wave reserves the wave's entries, a wave scan of the
+// per-thread counts places each thread's. Every lane of the wave calls this.
+template <int N>
+__device__ __forceinline__ void run_append(uint64_t flags, const uint32_t (&keys)[N], int b0,
+                                           uint64_t* list, int* counter) {
+  const int lane = threadIdx.x & 63;
+  const int n = __popcll(flags);
+  const int incl = wave_incl_scan(n);
+  const int tot = __builtin_amdgcn_readlane(incl, 63);
+  int base = 0;
+  if (lane == 0 && tot > 0) base = atomicAdd(counter, tot);
+  base = __builtin_amdgcn_readfirstlane(base) + incl - n;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if ((flags >> i) & 1u) list[base++] = rank_word(keys[i], b0 + i);
+}
+
+// Exclusive prefix sum of x over the workgroup's threads in thread order;
+// the sum of all goes to *total. `tmp`: LDS scratch of NW ints, free on entry
+// (the caller puts a barrier between two calls). Every thread calls this.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int x, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) tmp[wave] = incl;
+  lds_barrier();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = tmp[w];
+    before += w < wave ? c : 0;
+    tot += c;
+  }
+  total = tot;
+  return before + incl - x;
+}
+
 // The same exclusive prefix for callers that walk the tiles in rolled loops
 // (short code: every line of a long unrolled sequence is fetched once per
 // CU): returns, in lane m < NTILE of each wave, the number of flagged items

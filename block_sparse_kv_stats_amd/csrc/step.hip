@@ -223,6 +223,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   __shared__ __align__(16) float q_l[G * D];  // the G query heads
   __shared__ __align__(16) int hist[2048];
   __shared__ __align__(16) uint64_t plist[kListMax + kListPad];  // pivot-bin (key, index) words
+  __shared__ uint32_t keys_l[KPT * NT];                            // every block's key, block order
   __shared__ uint32_t keep_bits[NBITS];
   __shared__ int cnt[KPT * NW + 1];
   __shared__ float scl[NW * G + 2 * G];
@@ -369,7 +370,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     for (int g = 0; g < G; ++g) Sfresh += __expf(fa[g] - lse_g[g]) * fi[g].y;
   }
   uint32_t key[KPT];
-  uint64_t candm = 0u;  // bit j: block tid + NT*j is a Top-K candidate
   float* scores = (a.scores && p == 0) ? a.scores + ubase : nullptr;
 #pragma unroll
   for (int bt = 0; bt < C::NBATCH; ++bt) {
@@ -402,12 +402,26 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       const float S = b < NBa ? Sc : (b == fb ? Sfresh : 0.f);
       const bool inr = b < NB;
       key[j] = (inr && S > 0.f) ? __float_as_uint(S) : 0u;
-      const bool c = inr && b >= 1 && b <= NB - 3;
-      candm |= (uint64_t)c << j;
+      const bool c = inr && b >= 1 && b <= NB - 3;  // a Top-K candidate
       if (scores && inr) scores[b] = S;
       if (c && count) atomicAdd(&hist[key[j] >> 21], 1);
     }
   }
+
+  // The keys go through LDS so that from here on thread t holds the run of
+  // KPT consecutive blocks b0 = t*KPT .. b0+KPT-1: block order is thread
+  // order, and the list, the tie ranks and the compaction are per-thread
+  // counts and one scan instead of a pass per block slot.
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) keys_l[tid + j * NT] = key[j];
+  lds_barrier();
+  const int b0 = tid * KPT;
+  uint32_t kr[KPT];  // keys of the thread's run
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) kr[i] = keys_l[b0 + i];
+  uint64_t cand = 0u;  // bit i: block b0 + i is a Top-K candidate
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) cand |= (uint64_t)(b0 + i >= 1 && b0 + i <= NB - 3) << i;
 
   // ================================================================ select
   uint32_t tau_bin = 0xffffffffu;
@@ -415,7 +429,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   uint32_t exact_tau = 0u;
   uint64_t pin = 0u, gtm = 0u;  // candidates in the pivot bin / in higher bins
   if (count) {
-    lds_barrier();
     if (wave == 0) find_bin<2048>(hist, krem, ctl);
     lds_barrier();
     tau_bin = (uint32_t)ctl[0];
@@ -424,13 +437,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     if (use_list) {
       // the pivot bin's keys, ordered exactly by (key desc, index asc); the first krem are kept
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const bool c = (candm >> j) & 1u;
-        const uint32_t kb = key[j] >> 21;
-        pin |= (uint64_t)(c && kb == tau_bin) << j;
-        gtm |= (uint64_t)(c && kb > tau_bin) << j;
+      for (int i = 0; i < KPT; ++i) {
+        const bool c = (cand >> i) & 1u;
+        const uint32_t kb = kr[i] >> 21;
+        pin |= (uint64_t)(c && kb == tau_bin) << i;
+        gtm |= (uint64_t)(c && kb > tau_bin) << i;
       }
-      list_append<KPT>(pin, key, tid, NT, plist, &ctl[3]);
+      run_append<KPT>(pin, kr, b0, plist, &ctl[3]);
       lds_barrier();
       const int n = ctl[3];
       rank_list_keep<NT>(plist, n, krem, keep_bits);
@@ -441,8 +454,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       for (int i = tid; i < 2048; i += NT) hist[i] = 0;
       lds_barrier();
 #pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (((candm >> j) & 1u) && (key[j] >> 21) == (prefix >> 21)) atomicAdd(&hist[(key[j] >> 10) & 2047u], 1);
+      for (int i = 0; i < KPT; ++i)
+        if (((cand >> i) & 1u) && (kr[i] >> 21) == (prefix >> 21)) atomicAdd(&hist[(kr[i] >> 10) & 2047u], 1);
       lds_barrier();
       if (wave == 0) find_bin<2048>(hist, krem, ctl);
       lds_barrier();
@@ -451,8 +464,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       for (int i = tid; i < 1024; i += NT) hist[i] = 0;
       lds_barrier();
 #pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (((candm >> j) & 1u) && (key[j] >> 10) == (prefix >> 10)) atomicAdd(&hist[key[j] & 1023u], 1);
+      for (int i = 0; i < KPT; ++i)
+        if (((cand >> i) & 1u) && (kr[i] >> 10) == (prefix >> 10)) atomicAdd(&hist[kr[i] & 1023u], 1);
       lds_barrier();
       if (wave == 0) find_bin<1024>(hist, krem, ctl);
       lds_barrier();
@@ -463,59 +476,51 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
 
   // ================================================================ compact
-  const bool ties_by_index = count && !use_list;
-  int eq_before[KPT];
-  if (ties_by_index) {
-    uint64_t eqm = 0u;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) eqm |= (uint64_t)(((candm >> j) & 1u) && key[j] == exact_tau) << j;
-    int tot;
-    tile_prefix<KPT, NW>(eqm, eq_before, cnt, tot);
-    lds_barrier();
-  }
   uint64_t takem = 0u;
   if (all) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) takem |= (uint64_t)(tid + j * NT < NB) << j;
+    for (int i = 0; i < KPT; ++i) takem |= (uint64_t)(b0 + i < NB) << i;
   } else {
     uint64_t forced = 0u, above = 0u;
     // blocks 0, NB-2 and NB-1, set in their owners' masks
     const int fbl[3] = {0, NB - 2, NB - 1};
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-      if (fbl[k] >= 0 && fbl[k] % NT == tid) forced |= 1ull << (fbl[k] / NT);
-    if (ties_by_index) {
+      if (fbl[k] >= 0 && fbl[k] / KPT == tid) forced |= 1ull << (fbl[k] - b0);
+    if (count && !use_list) {
+      // keys equal to the threshold key are kept in index order: the first krem of them
+      uint64_t eqm = 0u;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const bool c = (candm >> j) & 1u;
-        above |= (uint64_t)(c && (key[j] > exact_tau || (key[j] == exact_tau && eq_before[j] < krem))) << j;
+      for (int i = 0; i < KPT; ++i) eqm |= (uint64_t)(((cand >> i) & 1u) && kr[i] == exact_tau) << i;
+      int tot;
+      const int eq0 = block_excl_scan<NW>(__popcll(eqm), cnt, tot);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const bool c = (cand >> i) & 1u;
+        const int eb = eq0 + __popcll(eqm & ((1ull << i) - 1ull));
+        above |= (uint64_t)(c && (kr[i] > exact_tau || (kr[i] == exact_tau && eb < krem))) << i;
       }
+      lds_barrier();  // cnt is scanned again below
     } else if (count) {
       // every candidate of a higher bin, and the pivot-bin keys the rank kept
       uint64_t kp = 0u;
       for (uint64_t m = pin; m; m &= m - 1) {
-        const int j = __builtin_ctzll(m);
-        const int b = tid + j * NT;
-        kp |= (uint64_t)((keep_bits[b >> 5] >> (b & 31)) & 1u) << j;
+        const int i = __builtin_ctzll(m);
+        const int b = b0 + i;
+        kp |= (uint64_t)((keep_bits[b >> 5] >> (b & 31)) & 1u) << i;
       }
       above = gtm | kp;
     }
     takem = forced | above;
   }
   int nk;
-  const int tbase = tile_bases<KPT, NW>(takem, cnt, nk);
+  int pos = block_excl_scan<NW>(__popcll(takem), cnt, nk);
   int32_t* sel = a.sel + (size_t)unit * Kb;
   const int lo = p * KPART;
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll 1
-  for (int j = 0; j < KPT; ++j) {
-    const uint64_t bal = __ballot((takem >> j) & 1u);
-    if ((takem >> j) & 1u) {
-      const int pos = __builtin_amdgcn_readlane(tbase, j) + __popcll(bal & below);
-      const int b = tid + j * NT;
-      if (p == 0 && pos < Kb) sel[pos] = b;
-      if (pos >= lo && pos < lo + KPART) klist[pos - lo] = b;
-    }
+  for (uint64_t m = takem; m; m &= m - 1, ++pos) {
+    const int b = b0 + __builtin_ctzll(m);
+    if (p == 0 && pos < Kb) sel[pos] = b;
+    if (pos >= lo && pos < lo + KPART) klist[pos - lo] = b;
   }
   nk = nk < Kb ? nk : Kb;  // the selection keeps exactly min(Kb, NB); never index past sel
   if (p == 0 && tid == 0) a.n_sel[unit] = nk;
