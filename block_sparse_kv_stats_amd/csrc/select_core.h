@@ -123,11 +123,11 @@ __device__ __forceinline__ void rank_list_keep(const uint64_t* list, int n, int 
 }
 
 // Append the flagged entries of this thread's run of blocks b0, b0+1, ...
-// (bit i of `flags`: block b0 + i, key keys[i]) to list[*counter ..): one
-// LDS atomic per wave reserves the wave's entries, a wave scan of the
-// per-thread counts places each thread's. Every lane of the wave calls this.
-template <int N>
-__device__ __forceinline__ void run_append(uint64_t flags, const uint32_t (&keys)[N], int b0,
+// (bit i of `flags`: block b0 + i, whose key is keys[b0 + i], keys in LDS)
+// to list[*counter ..): one LDS atomic per wave reserves the wave's entries,
+// a wave scan of the per-thread counts places each thread's, and a thread
+// visits only its flagged blocks. Every lane of the wave calls this.
+__device__ __forceinline__ void run_append(uint64_t flags, const uint32_t* keys, int b0,
                                            uint64_t* list, int* counter) {
   const int lane = threadIdx.x & 63;
   const int n = __popcll(flags);
@@ -136,9 +136,10 @@ __device__ __forceinline__ void run_append(uint64_t flags, const uint32_t (&keys
   int base = 0;
   if (lane == 0 && tot > 0) base = atomicAdd(counter, tot);
   base = __builtin_amdgcn_readfirstlane(base) + incl - n;
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    if ((flags >> i) & 1u) list[base++] = rank_word(keys[i], b0 + i);
+  for (uint64_t m = flags; m; m &= m - 1) {
+    const int b = b0 + (int)__builtin_ctzll(m);
+    list[base++] = rank_word(keys[b], b);
+  }
 }
 
 // Exclusive prefix sum of x over the workgroup's threads in thread order;

@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
         pin |= (uint64_t)(c && kb == tau_bin) << i;
         gtm |= (uint64_t)(c && kb > tau_bin) << i;
       }
-      run_append<KPT>(pin, kr, b0, plist, &ctl[3]);
+      run_append(pin, keys_l, b0, plist, &ctl[3]);
       lds_barrier();
       const int n = ctl[3];
       rank_list_keep<NT>(plist, n, krem, keep_bits);
