@@ -246,35 +246,43 @@ def time_kernel_events(torch, timer, stream, bench, n, which):
 
 def cpu_baseline(w, seconds: float):
     """The fp64 oracle's per-step path (open-block update, score, select,
-    attend) for one (sequence, KV head) unit, single thread, scaled to a step
-    over all units."""
+    attend), single thread, on every (sequence, KV head) unit of sequence 0 in
+    turn: each unit runs up to `seconds`/H of consecutive steps from the
+    workload's context, and a step over all units costs the sum of the units'
+    mean step times, scaled by S."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from block_sparse_kv_stats_amd import synth
     from oracle import compkv as ok
 
-    n_max = 4000
-    u = synth.gen_unit(w.replace(steps=max(w.steps, 1), extra_cap=n_max), 0, 0,
-                       ntok=w.prefill[0] + n_max)
+    n_max = 2500  # per unit: the context grows by at most this many tokens
     T0 = w.prefill[0]
-    q = u["q"][0]
+    wl = w.replace(steps=max(w.steps, 1), extra_cap=n_max)
+    per_step, steps, timed = 0.0, 0, 0.0
     with threadpool_limits(limits=1):
-        su = ok.StreamingUnit(u["k"], u["v"], T0, w.r, cap_tokens=T0 + n_max)
-        t0 = time.perf_counter()
-        n = 0
-        while n < n_max:
-            su.append(u["k"][T0 + n], u["v"][T0 + n])
-            su.step(q, w.budget)
-            n += 1
-            if time.perf_counter() - t0 > seconds:
-                break
-        dt = time.perf_counter() - t0
-    per_unit = dt / n
-    U = w.S * w.H
-    return {"value": 1.0 / (per_unit * U), "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} consecutive steps of one (sequence, KV head) unit of {w.name} "
-                      f"({dt:.1f} s, fp64 NumPy, 1 thread), scaled x{U} units per step"}
+        for h in range(w.H):
+            u = synth.gen_unit(wl, 0, h, ntok=T0 + n_max)
+            q = u["q"][0]
+            su = ok.StreamingUnit(u["k"], u["v"], T0, w.r, cap_tokens=T0 + n_max)
+            t0 = time.perf_counter()
+            n = 0
+            while n < n_max:
+                su.append(u["k"][T0 + n], u["v"][T0 + n])
+                su.step(q, w.budget)
+                n += 1
+                if time.perf_counter() - t0 > seconds / w.H:
+                    break
+            dt = time.perf_counter() - t0
+            per_step += dt / n
+            steps += n
+            timed += dt
+    per_step *= w.S
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} steps over the {w.H} (sequence, KV head) units of sequence 0 of "
+                      f"{w.name}, up to {n_max} consecutive steps each from {T0} tokens "
+                      f"({timed:.1f} s, fp64 NumPy, 1 thread); a step is the sum of the units' "
+                      f"mean step times" + (f", x{w.S} sequences" if w.S > 1 else "")}
 
 
 def traffic_from_profile(workload):
