@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   __shared__ __align__(16) int hist[2048];
   __shared__ int cnt[KPT * kSelWaves + 1];
   __shared__ __align__(16) uint64_t plist[kListMax + kListPad];  // pivot-bin (key, index) words
+  __shared__ uint32_t keys_l[KPT * kSelThreads];                   // every block's key, block order
   __shared__ uint32_t keep_bits[NW];
   __shared__ int ctl[8];
 
@@ -68,7 +69,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       gl[k][g] = v.y;
     }
   }
-  constexpr int UB0 = 4;  // blocks of u per thread per batch
+  // blocks of u per thread per batch: all of them up to 4 query heads (one round trip)
+  constexpr int UB0 = 48 / G < 4 ? 4 : (48 / G > KPT ? KPT : 48 / G);
   float ub[UB0][G];
 #pragma unroll
   for (int m = 0; m < UB0; ++m) {
@@ -127,7 +129,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
   // ---- S_b, its key, and the histogram of the candidates' key top 11 bits
   uint32_t key[KPT];
-  uint32_t candm = 0u;  // bit m: block tid + 1024*m is a candidate (not forced, in range)
   const bool count = !all && krem > 0;
   float* scores = a.scores ? a.scores + (size_t)unit * a.cap_blocks : nullptr;
 #pragma unroll
@@ -149,8 +150,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g) S += ub[m][g] * f[(bc >> a.bpw_shift) * G + g];
       key[m0 + m] = (b < NB && S > 0.f) ? __float_as_uint(S) : 0u;
-      const bool c = b >= 1 && b <= NB - 3;
-      candm |= (uint32_t)c << (m0 + m);
+      const bool c = b >= 1 && b <= NB - 3;  // a candidate (not forced, in range)
       if (scores && b < NB) scores[b] = S;
       if (c && count) atomicAdd(&hist[key[m0 + m] >> 21], 1);
     }
@@ -161,11 +161,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     return;
   }
 
+  // ---- the keys go through LDS so that from here on thread t holds the run
+  // of KPT consecutive blocks b0 = t*KPT ..: block order is thread order, and
+  // the list, the tie ranks and the compaction are per-thread counts and one
+  // scan instead of a pass per block slot
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) keys_l[tid + m * kSelThreads] = key[m];
+  lds_barrier();  // also completes the histogram
+  const int b0 = tid * KPT;
+  uint32_t kr[KPT];  // keys of the thread's run
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) kr[i] = keys_l[b0 + i];
+  uint64_t cand = 0u;  // bit i: block b0 + i is a candidate (not forced, in range)
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) cand |= (uint64_t)(b0 + i >= 1 && b0 + i <= NB - 3) << i;
+
   // ---- threshold bin: keys whose top 11 bits exceed tau_bin are kept
   uint32_t tau_bin = 0xffffffffu;
   bool use_list = true;
   if (krem > 0) {
-    lds_barrier();
     if (wave == 0) find_bin<2048>(hist, krem, ctl);
     lds_barrier();
     tau_bin = (uint32_t)ctl[0];
@@ -174,12 +188,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   }
 
   uint32_t exact_tau = 0u;  // long-tie path: exact threshold key, ties by index
+  uint64_t pin = 0u, gtm = 0u;  // candidates in the pivot bin / in higher bins
   if (krem > 0 && use_list) {
     // the pivot bin's keys, ordered exactly; the first krem are kept
-    uint64_t pin = 0u;
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) pin |= (uint64_t)(((candm >> m) & 1u) && (key[m] >> 21) == tau_bin) << m;
-    list_append<KPT>(pin, key, tid, kSelThreads, plist, &ctl[3]);
+    for (int i = 0; i < KPT; ++i) {
+      const bool c = (cand >> i) & 1u;
+      const uint32_t kb = kr[i] >> 21;
+      pin |= (uint64_t)(c && kb == tau_bin) << i;
+      gtm |= (uint64_t)(c && kb > tau_bin) << i;
+    }
+    run_append(pin, keys_l, b0, plist, &ctl[3]);
     lds_barrier();
     rank_list_keep<kSelThreads>(plist, ctl[3], krem, keep_bits);
     lds_barrier();
@@ -190,8 +209,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     hist[tid + kSelThreads] = 0;
     lds_barrier();
 #pragma unroll
-    for (int m = 0; m < KPT; ++m)
-      if (((candm >> m) & 1u) && (key[m] >> 21) == (prefix >> 21)) atomicAdd(&hist[(key[m] >> 10) & 2047u], 1);
+    for (int i = 0; i < KPT; ++i)
+      if (((cand >> i) & 1u) && (kr[i] >> 21) == (prefix >> 21)) atomicAdd(&hist[(kr[i] >> 10) & 2047u], 1);
     lds_barrier();
     if (wave == 0) find_bin<2048>(hist, krem, ctl);
     lds_barrier();
@@ -201,8 +220,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     hist[tid] = 0;
     lds_barrier();
 #pragma unroll
-    for (int m = 0; m < KPT; ++m)
-      if (((candm >> m) & 1u) && (key[m] >> 10) == (prefix >> 10)) atomicAdd(&hist[key[m] & 1023u], 1);
+    for (int i = 0; i < KPT; ++i)
+      if (((cand >> i) & 1u) && (kr[i] >> 10) == (prefix >> 10)) atomicAdd(&hist[kr[i] & 1023u], 1);
     lds_barrier();
     if (wave == 0) find_bin<1024>(hist, krem, ctl);
     lds_barrier();
@@ -212,36 +231,40 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   }
 
   // ---- ascending compaction of the kept blocks
-  int before[KPT];
-  uint32_t eqm = 0u;
-  const bool ties_by_index = !use_list && krem > 0;
-  if (ties_by_index) {
+  uint64_t forced = 0u, above = 0u;
+  const int fbl[3] = {0, NB - 2, NB - 1};
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) eqm |= (uint32_t)(((candm >> m) & 1u) && key[m] == exact_tau) << m;
-    lds_barrier();
-    int tot_eq;
-    tile_prefix<KPT, kSelWaves>(eqm, before, cnt, tot_eq);
-    lds_barrier();
-  }
-  uint32_t takem = 0u;
+  for (int k = 0; k < 3; ++k)
+    if (fbl[k] >= 0 && fbl[k] / KPT == tid) forced |= 1ull << (fbl[k] - b0);
+  if (krem > 0 && !use_list) {
+    // keys equal to the threshold key are kept in index order: the first krem of them
+    uint64_t eqm = 0u;
 #pragma unroll
-  for (int m = 0; m < KPT; ++m) {
-    const int b = tid + m * kSelThreads;
-    const bool forced = b == 0 || (b >= NB - 2 && b < NB);
-    const bool c = (candm >> m) & 1u;
-    bool t = forced;
-    if (ties_by_index || !use_list) {
-      t = t || (c && key[m] > exact_tau) || (((eqm >> m) & 1u) && before[m] < krem);
-    } else {
-      t = t || (c && (key[m] >> 21) > tau_bin) || ((keep_bits[b >> 5] >> (b & 31)) & 1u);
+    for (int i = 0; i < KPT; ++i) eqm |= (uint64_t)(((cand >> i) & 1u) && kr[i] == exact_tau) << i;
+    int tot;
+    const int eq0 = block_excl_scan<kSelWaves>(__popcll(eqm), cnt, tot);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const bool c = (cand >> i) & 1u;
+      const int eb = eq0 + __popcll(eqm & ((1ull << i) - 1ull));
+      above |= (uint64_t)(c && (kr[i] > exact_tau || (kr[i] == exact_tau && eb < krem))) << i;
     }
-    takem |= (uint32_t)t << m;
+    lds_barrier();  // cnt is scanned again below
+  } else if (krem > 0) {
+    // every candidate of a higher bin, and the pivot-bin keys the rank kept
+    uint64_t kp = 0u;
+    for (uint64_t m = pin; m; m &= m - 1) {
+      const int i = __builtin_ctzll(m);
+      const int b = b0 + i;
+      kp |= (uint64_t)((keep_bits[b >> 5] >> (b & 31)) & 1u) << i;
+    }
+    above = gtm | kp;
   }
-  int tot_take;
-  tile_prefix<KPT, kSelWaves>(takem, before, cnt, tot_take);
-#pragma unroll
-  for (int m = 0; m < KPT; ++m)
-    if ((takem >> m) & 1u) sel[before[m]] = tid + m * kSelThreads;
+  const uint64_t takem = forced | above;
+  int nk;
+  int pos = block_excl_scan<kSelWaves>(__popcll(takem), cnt, nk);
+  for (uint64_t m = takem; m; m &= m - 1, ++pos)
+    if (pos < Kb) sel[pos] = b0 + __builtin_ctzll(m);
   if (tid == 0) a.n_sel[unit] = Kb;
 }
 

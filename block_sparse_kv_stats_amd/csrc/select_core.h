@@ -72,32 +72,6 @@ __device__ __forceinline__ uint64_t rank_word(uint32_t key, int idx) {
   return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
 }
 
-// Append this thread's flagged items to list[*counter ..): item m (bit m of
-// `flags`) is block idx0 + m*stride with key keys[m]. One LDS atomic per
-// wave reserves the wave's slots; ballots give each lane its place. Every
-// lane of the wave calls this.
-template <int NTILE>
-__device__ __forceinline__ void list_append(uint64_t flags, const uint32_t (&keys)[NTILE], int idx0,
-                                            int stride, uint64_t* list, int* counter) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint64_t bal[NTILE];
-  int tot = 0;
-#pragma unroll
-  for (int m = 0; m < NTILE; ++m) {
-    bal[m] = __ballot((flags >> m) & 1u);
-    tot += __popcll(bal[m]);
-  }
-  int base = 0;
-  if (lane == 0 && tot > 0) base = atomicAdd(counter, tot);
-  base = __builtin_amdgcn_readfirstlane(base);
-#pragma unroll
-  for (int m = 0; m < NTILE; ++m) {
-    if ((flags >> m) & 1u) list[base + __popcll(bal[m] & below)] = rank_word(keys[m], idx0 + m * stride);
-    base += __popcll(bal[m]);
-  }
-}
-
 // Ranks of the n words of `list` (followed by at least kListPad zero words):
 // an entry is kept when fewer than krem entries order above it; its block's
 // bit is set in keep_bits. Thread t ranks entries t, t+NT, ...; 32 words are
@@ -160,91 +134,6 @@ __device__ __forceinline__ int block_excl_scan(int x, int* tmp, int& total) {
   }
   total = tot;
   return before + incl - x;
-}
-
-// The same exclusive prefix for callers that walk the tiles in rolled loops
-// (short code: every line of a long unrolled sequence is fetched once per
-// CU): returns, in lane m < NTILE of each wave, the number of flagged items
-// ahead of the wave's first item of tile m (read per tile with readlane);
-// the total goes to *total. `cnt`: LDS scratch of NTILE*NW + 1 ints. Every
-// thread calls this.
-template <int NTILE, int NW>
-__device__ __forceinline__ int tile_bases(uint64_t flags, int* cnt, int& total) {
-  static_assert(NTILE <= 64, "one lane per tile");
-  constexpr int E = NTILE * NW;
-  constexpr int PER = (E + 63) / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int mine = 0;
-#pragma unroll 1
-  for (int m = 0; m < NTILE; ++m) {
-    const int c = __popcll(__ballot((flags >> m) & 1u));
-    mine = lane == m ? c : mine;
-  }
-  if (lane < NTILE) cnt[lane * NW + wave] = mine;
-  lds_barrier();
-  if (wave == 0) {
-    int v[PER], own = 0;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = lane * PER + k;
-      v[k] = i < E ? cnt[i] : 0;
-      own += v[k];
-    }
-    const int incl = wave_incl_scan(own);
-    int run = incl - own;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = lane * PER + k;
-      if (i < E) cnt[i] = run;
-      run += v[k];
-    }
-    if (lane == 63) cnt[E] = incl;
-  }
-  lds_barrier();
-  total = cnt[E];
-  return lane < NTILE ? cnt[lane * NW + wave] : 0;
-}
-
-// Exclusive prefix over items in tile-major order: tile m holds items
-// m*NT .. m*NT+NT-1 (thread t's item of tile m is m*NT + t); bit m of
-// `flags` is this thread's flag in tile m. before[m] gets the number of
-// flagged items ahead of this thread's item of tile m; the total goes to
-// *total. `cnt`: LDS scratch of NTILE*NW + 1 ints. Every thread calls this.
-template <int NTILE, int NW>
-__device__ __forceinline__ void tile_prefix(uint64_t flags, int (&before)[NTILE], int* cnt,
-                                            int& total) {
-  constexpr int E = NTILE * NW;       // (tile, wave) entries in item order
-  constexpr int PER = (E + 63) / 64;  // entries per lane of wave 0
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 0; m < NTILE; ++m) {
-    const unsigned long long bal = __ballot((flags >> m) & 1u);
-    before[m] = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) cnt[m * NW + wave] = __popcll(bal);
-  }
-  lds_barrier();
-  if (wave == 0) {  // exclusive scan of the E counts, in place; total after them
-    int v[PER], own = 0;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = lane * PER + k;
-      v[k] = i < E ? cnt[i] : 0;
-      own += v[k];
-    }
-    const int incl = wave_incl_scan(own);
-    int run = incl - own;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int i = lane * PER + k;
-      if (i < E) cnt[i] = run;
-      run += v[k];
-    }
-    if (lane == 63) cnt[E] = incl;
-  }
-  lds_barrier();
-#pragma unroll
-  for (int m = 0; m < NTILE; ++m) before[m] += cnt[m * NW + wave];
-  total = cnt[E];
 }
 
 }  // namespace cknv
