@@ -8,7 +8,9 @@
 // blocks are always kept and count against the budget; the remaining slots
 // go to the largest S_b (ties: lower block index).
 //
-// One 1024-thread workgroup per unit; thread t owns blocks t + 1024*m. The
+// One 1024-thread workgroup per unit; thread t computes the keys of blocks
+// t + 1024*m (coalesced) and, once they have passed through LDS, selects on
+// the run of kSelKeysPerThread consecutive blocks it then owns. The
 // score kernel left, per 16-block group, the partial (max, sum) of
 // a = ln|b| + z̄ + σ̂²/2 per query head and, per block,
 // u_{g,b} = exp(a - group max) σ̂². Here:
@@ -22,7 +24,8 @@
 //      If B holds more than kListMax keys (long runs of equal scores), two
 //      more radix passes (11 and 10 bits) pin the exact threshold key instead
 //      and equal keys are taken in index order.
-//   4. The kept blocks are written in ascending order (ballot prefix).
+//   4. The kept blocks are written in ascending order (one workgroup scan of
+//      the per-thread counts of the contiguous runs).
 #include "select_core.h"
 
 namespace cknv {

@@ -21,8 +21,9 @@
 // sums of all its blocks and the chunk's (max, sum) of a, and T0 per
 // sequence. The fresh block is in none of the sums: it is always kept.
 //
-// Phases of a workgroup (NT threads; thread t owns blocks t + NT*j of the
-// unit):
+// Phases of a workgroup (NT threads; for the loads and the keys thread t
+// owns blocks t + NT*j of the unit, coalesced; from the selection on it owns
+// the run of KPTB consecutive blocks t*KPTB ..):
 //   loads      T0, finfo, the chunk headers, the thread's score groups and
 //              u terms, the query, and (waves AW..NW-1) their first chunk
 //              records;
@@ -31,10 +32,12 @@
 //              e^{group max - LSE} of the thread's score groups to LDS;
 //   keys       S_b per block (fp32 bits order like the values, S_b >= 0);
 //              scores; 2048-bin histogram of the candidates' top 11 bits;
+//              the keys through LDS into the threads' contiguous runs;
 //   select     the bin holding the (Kb-3)-th largest candidate key; keys
 //              in that bin are ranked exactly (or, for long runs of equal
 //              keys, pinned by two more radix passes, ties by index);
-//   compact    kept blocks in ascending order -> sel, and this part's slice;
+//   compact    kept blocks in ascending order (one workgroup scan of the
+//              per-thread counts) -> sel, and this part's slice;
 //   attend     waves w < AW: kept block w of this part's slice (exact terms
 //              minus its compensation); meanwhile waves w >= AW fold this
 //              part's chunk records;
