@@ -51,6 +51,14 @@ def test_fused_single_step(name):
     run_steps(w.replace(steps=1), summaries_every=1)
 
 
+def test_fused_longest_bucket_150k():
+    """One KV head at 150K tokens (9376 blocks): the step kernel's largest
+    bucket (24 blocks per thread) and 32 parts per unit, against the oracle."""
+    w = synth.WORKLOADS["qwen8b_128k"].replace(name="one head 150K", H=1, prefill=(150000,),
+                                              steps=2)
+    run_steps(w, summaries_every=1)
+
+
 def test_fused_partial_open_block():
     w = synth.WORKLOADS["llama8b_32k"].replace(prefill=(32768 + 6,), extra_cap=16, steps=1)
     run_steps(w, summaries_every=1)

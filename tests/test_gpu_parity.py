@@ -42,6 +42,12 @@ def test_llama8b_32k_step():
     run_single_step(synth.WORKLOADS["llama8b_32k"])
 
 
+def test_one_head_150k_step():
+    """9376 blocks: the selection kernel's runs of 12 blocks nearly full."""
+    run_single_step(synth.WORKLOADS["qwen8b_128k"].replace(name="one head 150K", H=1,
+                                                           prefill=(150000,), steps=1))
+
+
 def test_llama8b_32k_partial_open_block():
     w = synth.WORKLOADS["llama8b_32k"].replace(prefill=(32768 + 6,), extra_cap=16)
     run_single_step(w)
