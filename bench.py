@@ -202,6 +202,23 @@ def time_eager_steps(torch, timer, stream, bench, n):
     return e0.elapsed_time(e1) / n
 
 
+def time_step_percentiles(torch, timer, stream, bench, n):
+    """Per-step durations (ms) of eager fused steps, each between two HIP
+    events on the launch stream (the launches queued behind a spin kernel,
+    so host launch latency stays out): p10, median and p90."""
+    evs = [(timer.event(), timer.event()) for _ in range(n)]
+    with torch.cuda.stream(stream):
+        timer.head_start(5.0 + 0.08 * n)
+        for i in range(n):
+            evs[i][0].record(stream)
+            bench.bound[i % bench.R].fused_step()
+            evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(c) for a, c in evs)
+    pick = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
+    return pick(0.1), pick(0.5), pick(0.9)
+
+
 def time_score_kernel(torch, timer, stream, bench, sweeps):
     """Average duration (ms) of the streaming score kernel: sweeps of
     back-to-back cknv_decode_score launches over the R layers, each sweep
@@ -307,7 +324,7 @@ def run_workload(torch, timer, wname, args, stream, want_dense=True):
     steps, warm = args.steps, args.warmup
     n_e = min(steps, 256)
     kernel_n = min(max(2 * R, 64), 256)
-    appends = (math.ceil(warm / R) + math.ceil(steps / R) + math.ceil(n_e / R)
+    appends = (math.ceil(warm / R) + math.ceil(steps / R) + 2 * math.ceil(n_e / R)
                + 2 * math.ceil(kernel_n / R) + math.ceil(max(R, steps // 4) / R) + 4)
     bench = Bench(w, R, appends, stream)
     log(f"{wname}: {R} layers, {warm} warm-up + {steps} timed steps")
@@ -317,6 +334,7 @@ def run_workload(torch, timer, wname, args, stream, want_dense=True):
     torch.cuda.synchronize()
     ms_step = time_graph_steps(torch, timer, stream, bench, steps, which="fused_step")
     ms_eager = time_eager_steps(torch, timer, stream, bench, n_e)
+    pct = time_step_percentiles(torch, timer, stream, bench, n_e)
     k_avg, k_med = time_score_kernel(torch, timer, stream, bench, max(8, 256 // R))
     f_avg, f_med = time_kernel_events(torch, timer, stream, bench, kernel_n, "decode_finish")
     ms_three = time_graph_steps(torch, timer, stream, bench, max(R, steps // 4), which="step")
@@ -324,7 +342,7 @@ def run_workload(torch, timer, wname, args, stream, want_dense=True):
     T = bench.seq_len()
     sb, ab = step_bytes(w, T)
     res = {"w": w, "R": R, "steps": steps, "warmup": warm, "ms_step": ms_step,
-           "ms_eager": ms_eager, "T": T, "score_bytes": sb, "attend_bytes": ab,
+           "ms_eager": ms_eager, "step_us_p10_p50_p90": [round(x * 1e3, 2) for x in pct], "T": T, "score_bytes": sb, "attend_bytes": ab,
            "score_ms": k_avg, "score_ms_median": k_med, "finish_ms": f_avg,
            "ms_three_calls": ms_three, "build_ms": ms_build, "build_bytes": build_bytes(w, T)}
     if want_dense:
@@ -532,6 +550,7 @@ def main():
                    "launch": "hipGraph replay of layer sweeps of cknv_decode_step"},
         "step_GBps": round(step_gbps, 1),
         "eager_ms_per_step": round(main_res["ms_eager"], 5),
+        "eager_step_us_p10_p50_p90": main_res["step_us_p10_p50_p90"],
         "roofline": {"bound": "hbm", "kernel": "score_kernel (cknv_decode_score)",
                      "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
@@ -558,6 +577,7 @@ def main():
         line["also"] = {
             "workload": we.name, "steps_per_s": round(1000.0 / extra["ms_step"], 2),
             "ms_per_step": round(extra["ms_step"], 5), "context_tokens": extra["T"],
+            "eager_step_us_p10_p50_p90": extra["step_us_p10_p50_p90"],
             "layers_rotated": extra["R"],
             "step_GBps": round((extra["score_bytes"] + extra["attend_bytes"]) / (extra["ms_step"] * 1e-3) / 1e9, 1),
             "score_kernel_GBps": round(e_score, 1), "score_frac": round(e_score / PEAK_HBM_GBPS, 4),
