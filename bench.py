@@ -390,6 +390,10 @@ PROFILE_COMMANDS = {
              'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --also ""',
     "write": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/write -o write -- '
              'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --also ""',
+    "fetch128": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/fetch128 -o fetch128 -- '
+                'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --workload qwen8b_128k --also ""',
+    "write128": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/write128 -o write128 -- '
+                'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --workload qwen8b_128k --also ""',
     "copy_fetch": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/copy_fetch -o cf -- '
                   'python3 bench.py --copy-probe 268435456',
     "copy_write": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/copy_write -o cw -- '
@@ -446,38 +450,42 @@ def summarize_profiles(out_dir):
                      f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
     with open(os.path.join(prof, "kernels_llama8b_32k_qwen8b_128k_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    # ---- HBM traffic of score_kernel at 32K, calibrated on a plain copy
-    w = synth.WORKLOADS["llama8b_32k"]
-    fetch = _counter_per_dispatch(os.path.join(out_dir, "fetch"), "FETCH_SIZE", "score_kernel")
-    write = _counter_per_dispatch(os.path.join(out_dir, "write"), "WRITE_SIZE", "score_kernel")
+    # ---- HBM traffic of score_kernel per workload, calibrated on a plain copy
     cf = _counter_per_dispatch(os.path.join(out_dir, "copy_fetch"), "FETCH_SIZE", "copy")
     cw = _counter_per_dispatch(os.path.join(out_dir, "copy_write"), "WRITE_SIZE", "copy")
-    if not (fetch and write and cf and cw):
-        print("missing counter data", file=sys.stderr)
+    if not (cf and cw):
+        print("missing copy calibration data", file=sys.stderr)
         return
     kib = COPY_PROBE_BYTES / 1024.0
     f_cal = kib / statistics.median(cf)   # bytes per counted KiB, read side
     w_cal = kib / statistics.median(cw)   # ... write side
-    fb = statistics.median(fetch) * 1024.0 * f_cal
-    wb = statistics.median(write) * 1024.0 * w_cal
-    T = w.prefill[0] + 1
-    sb, _ = step_bytes(w, T)
-    rec = {"kernel": "score_kernel", "workload": w.name,
-           "source_hash": kernel_source_hash(SCORE_SOURCES),
-           "fetch_KiB_per_dispatch_median": statistics.median(fetch),
-           "write_KiB_per_dispatch_median": statistics.median(write),
-           "dispatches": [len(fetch), len(write)],
-           "copy_probe_bytes": COPY_PROBE_BYTES,
-           "copy_fetch_KiB": statistics.median(cf), "copy_write_KiB": statistics.median(cw),
-           "calibration_fetch": round(f_cal, 4), "calibration_write": round(w_cal, 4),
-           "hbm_read_bytes_per_launch": int(fb), "hbm_write_bytes_per_launch": int(wb),
-           "hbm_bytes_per_launch": int(fb + wb),
-           "algorithmic_bytes_per_launch_first_step": sb,
-           "commands": [PROFILE_COMMANDS[k] for k in ("fetch", "write", "copy_fetch",
-                                                      "copy_write", "summary")]}
-    with open(os.path.join(prof, "score_kernel_llama8b_32k_pmc.json"), "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec))
+    for wname, kf, kw in (("llama8b_32k", "fetch", "write"), ("qwen8b_128k", "fetch128", "write128")):
+        w = synth.WORKLOADS[wname]
+        fetch = _counter_per_dispatch(os.path.join(out_dir, kf), "FETCH_SIZE", "score_kernel")
+        write = _counter_per_dispatch(os.path.join(out_dir, kw), "WRITE_SIZE", "score_kernel")
+        if not (fetch and write):
+            print(f"missing counter data for {wname}", file=sys.stderr)
+            continue
+        fb = statistics.median(fetch) * 1024.0 * f_cal
+        wb = statistics.median(write) * 1024.0 * w_cal
+        T = w.prefill[0] + 1
+        sb, _ = step_bytes(w, T)
+        rec = {"kernel": "score_kernel", "workload": w.name,
+               "source_hash": kernel_source_hash(SCORE_SOURCES),
+               "fetch_KiB_per_dispatch_median": statistics.median(fetch),
+               "write_KiB_per_dispatch_median": statistics.median(write),
+               "dispatches": [len(fetch), len(write)],
+               "copy_probe_bytes": COPY_PROBE_BYTES,
+               "copy_fetch_KiB": statistics.median(cf), "copy_write_KiB": statistics.median(cw),
+               "calibration_fetch": round(f_cal, 4), "calibration_write": round(w_cal, 4),
+               "hbm_read_bytes_per_launch": int(fb), "hbm_write_bytes_per_launch": int(wb),
+               "hbm_bytes_per_launch": int(fb + wb),
+               "algorithmic_bytes_per_launch_first_step": sb,
+               "commands": [PROFILE_COMMANDS[k] for k in (kf, kw, "copy_fetch", "copy_write",
+                                                          "summary")]}
+        with open(os.path.join(prof, f"score_kernel_{wname}_pmc.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
 
 
 def build_line(res):
@@ -582,6 +590,7 @@ def main():
             "step_GBps": round((extra["score_bytes"] + extra["attend_bytes"]) / (extra["ms_step"] * 1e-3) / 1e9, 1),
             "score_kernel_GBps": round(e_score, 1), "score_frac": round(e_score / PEAK_HBM_GBPS, 4),
             "score_avg_launch_us": round(extra["score_ms"] * 1e3, 3),
+            "score_traffic": traffic_from_profile(args.also),
             "finish_avg_us": round(extra["finish_ms"] * 1e3, 3),
             "three_call_steps_per_s": round(1000.0 / extra["ms_three_calls"], 2),
             "bulk_build": build_line(extra)}
