@@ -599,9 +599,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
   lds_barrier();
   if (!ctl[4]) return;
-  // up to 32 parts in one batch (one round trip), else batches of 8
-  if (P > 8 && P <= 32)
-    merge_parts<D, G, NT, 32>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
+  // up to 32 parts in one batch (one round trip) while a thread owns one
+  // output column (more would spill), else batches of 8
+  if (G * D <= NT && P > 8 && P <= 32)
+    merge_parts<D, G, NT, (G * D <= NT ? 32 : 8)>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
                               a.lse ? a.lse + (size_t)unit * G : nullptr);
   else
     merge_parts<D, G, NT, 8>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
