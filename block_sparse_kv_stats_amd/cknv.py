@@ -223,15 +223,15 @@ def attend(cache: LayerCache, q, sel, n_sel, budget: int, max_blocks: int, out, 
         _ptr(ws, what="ws"), ws.numel(), _stream(stream)), "cknv_attend")
 
 
-def dense_attend(cache: LayerCache, q, max_blocks: int, budget: int, out, ws, lse=None,
+def dense_attend(cache: LayerCache, q, budget: int, max_blocks: int, out, ws, lse=None,
                  stream=None):
     import torch
     s = cache.shape
     nq = s.S * s.H * s.G
     c = cache.c_struct()
     _check(lib().cknv_dense_attend(
-        ctypes.byref(s), ctypes.byref(c), _ptr(q, (torch.float32,), nq * s.d, "q"), max_blocks,
-        budget, _ptr(out, (torch.float32,), nq * s.d, "out"),
+        ctypes.byref(s), ctypes.byref(c), _ptr(q, (torch.float32,), nq * s.d, "q"), budget,
+        max_blocks, _ptr(out, (torch.float32,), nq * s.d, "out"),
         _ptr(lse, (torch.float32,), nq, "lse"), _ptr(ws, what="ws"), ws.numel(),
         _stream(stream)), "cknv_dense_attend")
 
@@ -322,7 +322,7 @@ class BoundStep:
         self.attend_args = (self.shape, cp, qp, self.score_args[6], self.score_args[7], budget,
                             max_blocks, _ptr(out, (torch.float32,), s.S * s.H * s.G * s.d, "out"),
                             _ptr(lse, (torch.float32,), s.S * s.H * s.G, "lse"), w, wn, st)
-        self.dense_args = (self.shape, cp, qp, max_blocks, budget, self.attend_args[7],
+        self.dense_args = (self.shape, cp, qp, budget, max_blocks, self.attend_args[7],
                            self.attend_args[8], w, wn, st)
         self.fused_args = (self.shape, cp, self.append_args[2], self.append_args[3], qp, budget,
                            max_blocks, self.score_args[5], self.score_args[6], self.score_args[7],

@@ -294,7 +294,7 @@ int cknv_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q
 }
 
 int cknv_dense_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q,
-                      int32_t max_blocks, int32_t budget_tokens, float* out, float* lse,
+                      int32_t budget_tokens, int32_t max_blocks, float* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream) {
   return attend_common(shape, cache, q, nullptr, nullptr, budget_tokens, max_blocks, out, lse,
                        ws, ws_bytes, stream, true);

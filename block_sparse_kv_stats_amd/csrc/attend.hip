@@ -8,9 +8,9 @@
 // their tokens' exact terms, and both parts are normalised together.
 //
 // The score kernel already summed the compensation of ALL blocks, per
-// 64-block chunk. Here workgroup p of a unit
-//   * adds the exact terms of its slice of the kept list (each wave two
-//     blocks: 16 tokens x d BF16 keys and values, 4 tokens per load),
+// chunk (one score workgroup: 32 or 64 blocks). Here workgroup p of a unit
+//   * adds the exact terms of its slice of the kept list (each wave one
+//     block: 16 tokens x d BF16 keys and values, 4 tokens per load),
 //   * subtracts those blocks' own compensation terms |b| e^{z̄_b}(1, v̄_b),
 //   * folds in up to 8 of the score kernel's chunk records,
 // and writes one record; merge_kernel then combines a unit's P records into

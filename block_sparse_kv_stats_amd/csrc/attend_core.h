@@ -63,35 +63,6 @@ struct Tile {
       v[t] = t < nt ? w : 0u;
     }
   }
-  // The block a decode step appends to: np (0..15) tokens from the cache at
-  // tok0.. and the appended token (rows nk, nv of D bf16, not yet in the
-  // cache) as token np. Every load reads a valid address; tokens past np are
-  // zeroed afterwards.
-  __device__ void load_fresh(const uint16_t* kc, const uint16_t* vc, long tok0, int np,
-                             const uint16_t* nk, const uint16_t* nv, int lane) {
-    const int tq = lane >> 4, cc = lane & 15;
-    nt = np + 1;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = 4 * m + tq;
-      tv[m] = t < nt;
-      const uint16_t* src = (t < np ? kc + (size_t)(tok0 + t) * D : nk) + cc * EPL;
-      if (EPL == 8) {
-        const uint4 kk = stream_load_u4<false>(src);
-        k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
-        k[m][2] = tv[m] ? kk.z : 0u; k[m][3] = tv[m] ? kk.w : 0u;
-      } else {
-        const uint2 kk = stream_load_u2<false>(src);
-        k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint16_t* src = (t < np ? vc + (size_t)(tok0 + t) * D : nv) + lane * VPL;
-      const uint32_t w = VPL == 2 ? stream_load_u1<false>(src) : stream_load_h<false>(src);
-      v[t] = t < nt ? w : 0u;
-    }
-  }
 };
 
 // Mean-compensation inputs of one kept block (to be subtracted): the lane's

@@ -164,7 +164,7 @@ int cknv_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q
 
 /* One whole decode step, fused: the same results as cknv_append, then
  * cknv_score_select, then cknv_attend on the same arguments, in two kernel
- * launches (three when the budget exceeds 512 tokens) instead of five or six.
+ * launches instead of five.
  *   - new_k, new_v: bfloat16 [S][H][d], the step's token ("How to use it":
  *     the new K/V are stored and the current block's statistics refreshed);
  *   - q, budget_tokens, scores, sel, n_sel: as for cknv_score_select, with
@@ -203,7 +203,7 @@ int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const f
  * page compares CompKV with ("Assumptions and limits"). Same q/out/lse
  * layouts as cknv_attend. Uses its own region of the workspace. */
 int cknv_dense_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q,
-                      int32_t max_blocks, int32_t budget_tokens, float* out, float* lse,
+                      int32_t budget_tokens, int32_t max_blocks, float* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Name of a status code (static string). */

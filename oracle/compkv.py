@@ -49,11 +49,6 @@ def num_blocks(T: int, block: int = BLOCK) -> int:
     return (T + block - 1) // block
 
 
-def block_ranges(T: int, block: int = BLOCK):
-    """Token ranges [start, end) of the blocks of a T-token context."""
-    return [(s, min(s + block, T)) for s in range(0, T, block)]
-
-
 def _summaries_equal_blocks(kb: np.ndarray, vb: np.ndarray, r: int):
     """Summaries of n blocks that all hold m tokens: kb, vb are [n][m][d]."""
     n, m, d = kb.shape

@@ -125,8 +125,14 @@ def test_entry_points_reject_before_launch():
                          None, FAKE, need - 1, None) == cknv.ENOSPACE
     assert L.cknv_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, None, FAKE, 512, 2048, FAKE,
                          None, FAKE, need, None) == cknv.EINVAL
-    assert L.cknv_dense_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, 2048, 512, None, None,
+    assert L.cknv_dense_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, 512, 2048, None, None,
                                FAKE, need, None) == cknv.EINVAL
+    # (budget_tokens, max_blocks) in that order, as in every other call: a
+    # budget below the forced set is rejected, a max_blocks beyond capacity too
+    assert L.cknv_dense_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, 32, 2048, FAKE, None,
+                               FAKE, need, None) == cknv.EINVAL
+    assert L.cknv_dense_attend(ctypes.byref(sh), ctypes.byref(c), FAKE, 512, 5000, FAKE, None,
+                               FAKE, need, None) == cknv.ENOSPACE
     assert L.cknv_append(ctypes.byref(sh), ctypes.byref(c), None, FAKE, None) == cknv.EINVAL
     assert L.cknv_append(ctypes.byref(sh), None, FAKE, FAKE, None) == cknv.EINVAL
     assert L.cknv_workspace_init(ctypes.byref(sh), 2048, 512, None, need, None) == cknv.EINVAL

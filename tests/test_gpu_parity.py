@@ -276,7 +276,7 @@ def test_dense_attend(name):
     out = torch.zeros((w.S, w.H * w.G, w.d), dtype=torch.float32, device="cuda")
     lse = torch.zeros((w.S, w.H * w.G), dtype=torch.float32, device="cuda")
     q = torch.from_numpy(data["q"][0]).cuda()
-    cknv.dense_attend(cache, q, mb, w.budget, out, ws, lse)
+    cknv.dense_attend(cache, q, w.budget, mb, out, ws, lse)
     torch.cuda.synchronize()
     T = w.prefill[0]
     for h in range(w.H):

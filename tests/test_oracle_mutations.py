@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import compkv as ok
+from tests import test_bf16_pins as bf16
 from tests import test_oracle_pins as pins
 
 
@@ -106,6 +107,16 @@ def _attention_always_compensates(q, k, v, T, sel, cnt, kbar, vbar, block=16, co
 
 P9 = lambda: pins.test_p9_second_order_mass_estimate_converges_at_fourth_order()
 
+
+def _decode_as_fp16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _decode_truncated(bits):
+    b = np.asarray(bits, dtype=np.uint16) & np.uint16(0xFFF0)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 MUTATIONS = {
     "sample variance": (("_summaries_equal_blocks", _summ_sample_variance),
                         [lambda: pins.test_p3_single_coordinate_keys_give_exact_logit_variance(192)]),
@@ -137,6 +148,9 @@ MUTATIONS = {
          lambda: pins.test_p7_ablation_mass_score_without_compensation_is_optimal(0)]),
     "compensation without block size": (("compensated_attention", _attention_no_count),
                                         [lambda: pins.test_p5_log_partition_identity_and_token_level_output(0)]),
+    "bf16 read as fp16": (("decode_bf16", _decode_as_fp16), [bf16.test_decode_every_bit_pattern]),
+    "bf16 low mantissa bits dropped": (("decode_bf16", _decode_truncated),
+                                       [bf16.test_decode_every_bit_pattern]),
 }
 
 
