@@ -151,24 +151,33 @@ def gen_unit(w: Workload, s: int, h: int, ntok: int | None = None) -> dict:
     return {"k": bf16_bits(k), "v": bf16_bits(v), "q": q}
 
 
-def gen_layer(w: Workload, units=None) -> dict:
+def gen_layer(w: Workload, units=None, threads: int = 1) -> dict:
     """Draw every unit of a layer into cache-shaped arrays.
 
     Returns k, v: uint16 [S][H][cap_tokens][d] (tokens beyond each sequence's
     prefill + steps are zero), q: fp32 [steps][S][H*G][d],
-    prefill: int32 [S].
+    prefill: int32 [S]. `threads` > 1 draws units concurrently (each unit has
+    its own generator, so the result does not depend on it).
     """
     S, H, G, d, cap = w.S, w.H, w.G, w.d, w.cap_tokens
     k = np.zeros((S, H, cap, d), dtype=np.uint16)
     v = np.zeros((S, H, cap, d), dtype=np.uint16)
     q = np.zeros((max(w.steps, 1), S, H * G, d), dtype=np.float32)
-    for s in range(S):
-        for h in range(H):
-            if units is not None and (s, h) not in units:
-                continue
-            u = gen_unit(w, s, h)
-            n = u["k"].shape[0]
-            k[s, h, :n] = u["k"]
-            v[s, h, :n] = u["v"]
-            q[:, s, h * G:(h + 1) * G] = u["q"]
+    todo = [(s, h) for s in range(S) for h in range(H) if units is None or (s, h) in units]
+
+    def one(sh):
+        s, h = sh
+        u = gen_unit(w, s, h)
+        n = u["k"].shape[0]
+        k[s, h, :n] = u["k"]
+        v[s, h, :n] = u["v"]
+        q[:, s, h * G:(h + 1) * G] = u["q"]
+
+    if threads > 1 and len(todo) > 1:
+        import concurrent.futures as cf
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, todo))
+    else:
+        for sh in todo:
+            one(sh)
     return {"k": k, "v": v, "q": q, "prefill": np.asarray(w.prefill, dtype=np.int32)}

@@ -50,7 +50,35 @@ def test_step_bytes_partial_open_block():
 
 def test_cpu_baseline_record():
     w = synth.WORKLOADS["tiny"]
-    rec = bench.cpu_baseline(w, 0.3)
+    rec = bench.cpu_baseline(w, 0.3, pool=False)
     assert rec["kind"] == "oracle" and rec["cores"] == 1 and rec["unit"] == "steps/s"
     assert rec["value"] > 0
     assert "steps over the 1 (sequence, KV head) units" in rec["sample"]
+    assert rec["host_cpu_count"] == os.cpu_count()
+
+
+def test_cpu_baseline_pool_record():
+    """Two units, one spawned process each, released together."""
+    w = synth.WORKLOADS["tiny"].replace(H=2)
+    rec = bench.cpu_baseline(w, 0.6)
+    assert rec["cores"] == min(2, bench.host_cpu()["usable"])
+    assert rec["value"] > 0 and rec["single_thread_steps_per_s"] > 0
+    assert "one spawned process per unit" in rec["sample"]
+
+
+def test_ragged_step_bytes_sum_over_sequences():
+    w = synth.WORKLOADS["tiny"].replace(S=2, prefill=(1023, 1029))
+    s2, a2 = bench.step_bytes(w, [1024, 1030])
+    s0, a0 = bench.step_bytes(w, 1024)
+    s1, a1 = bench.step_bytes(w, 1030)
+    assert (s2, a2) == ((s0 + s1) // 2, (a0 + a1) // 2)
+    assert bench.dense_bytes(w, [1024, 1030]) == (1024 + 1030) * 2 * 64 * 2
+
+
+def test_timed_regions_start_at_the_least_recently_used_layer():
+    b = bench.Bench.__new__(bench.Bench)
+    b.R, b.cursor = 5, 0
+    warm = b.order(3)
+    timed = b.order(4)
+    assert warm == [0, 1, 2] and timed == [3, 4, 0, 1]
+    assert b.order(1) == [2]
