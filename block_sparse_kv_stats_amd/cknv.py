@@ -58,7 +58,10 @@ SIGNATURES = {
                           P],
     "cknv_decode_finish": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, I32, I32, P, P, P, P,
                            P, P, SZ, P],
+    "cknv_decode_step_noalloc": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P, I32, I32,
+                                 P, P, P, P, P, P],
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20  # CKNV_NOALLOC_SCRATCH_BYTES
 
 
 def lib():
@@ -253,6 +256,26 @@ def decode_step(cache: LayerCache, new_k, new_v, q, budget: int, max_blocks: int
         _ptr(n_sel, (torch.int32,), s.S * s.H, "n_sel"),
         _ptr(out, (torch.float32,), nq * s.d, "out"), _ptr(lse, (torch.float32,), nq, "lse"),
         _ptr(ws, what="ws"), ws.numel(), _stream(stream)), "cknv_decode_step")
+
+
+def decode_step_noalloc(cache: LayerCache, new_k, new_v, q, budget: int, max_blocks: int, sel,
+                        n_sel, out, lse=None, scores=None, stream=None):
+    """cknv_decode_step_noalloc: cknv_decode_step in the library's own per-GPU
+    scratch array (no workspace argument; nothing is allocated)."""
+    import torch
+    s = cache.shape
+    Kb = budget // BLOCK
+    nq = s.S * s.H * s.G
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    c = cache.c_struct()
+    _check(lib().cknv_decode_step_noalloc(
+        ctypes.byref(s), ctypes.byref(c), _ptr(new_k, bf, s.S * s.H * s.d, "new_k"),
+        _ptr(new_v, bf, s.S * s.H * s.d, "new_v"), _ptr(q, (torch.float32,), nq * s.d, "q"),
+        budget, max_blocks, _ptr(scores, (torch.float32,), s.S * s.H * s.cap_blocks, "scores"),
+        _ptr(sel, (torch.int32,), s.S * s.H * Kb, "sel"),
+        _ptr(n_sel, (torch.int32,), s.S * s.H, "n_sel"),
+        _ptr(out, (torch.float32,), nq * s.d, "out"), _ptr(lse, (torch.float32,), nq, "lse"),
+        _stream(stream)), "cknv_decode_step_noalloc")
 
 
 class DecodeStep:

@@ -2,6 +2,8 @@
 // Validation runs before any HIP call; on error nothing is enqueued.
 #include <math.h>
 
+#include <mutex>
+
 #include "cknv_internal.h"
 #include "step_config.h"
 
@@ -259,6 +261,55 @@ int cknv_decode_step(const cknv_shape* shape, const cknv_cache* cache, const uin
                             stream);
 }
 
+// ---------------------------------------------------------------- no-allocation step
+// cknv_decode_step_noalloc keeps its workspace in this file-scope device
+// array instead of a caller's buffer. Each GPU the library runs on holds its
+// own copy for the life of the process. In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address is taken
+// once per device with hipGetSymbolAddress (that device current) and kept.
+constexpr size_t kNoAllocScratchBytes = CKNV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct DeviceScratch {
+  void* ptr = nullptr;   // device address of this device's copy of `scratch`
+  size_t plan_total = 0; // plan the step counters were last laid out for
+  int plan_U = -1, plan_S = -1;
+  size_t plan_pcnt = 0;
+};
+std::mutex g_scratch_mutex;
+DeviceScratch g_scratch[kMaxDevices];
+}  // namespace
+
+// The current device's scratch address; on first use per device, or when the
+// workspace layout changes, zero the step counters (by kernel, so that a
+// caller may capture the call in a graph).
+static int noalloc_workspace(const Plan& p, const cknv_shape* sh, void* stream, char** ws) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CKNV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return CKNV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  DeviceScratch& d = g_scratch[dev];
+  if (!d.ptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CKNV_EHIP;
+    d.ptr = ptr;
+  }
+  char* base = static_cast<char*>(d.ptr);
+  if (d.plan_total != p.total || d.plan_U != p.U || d.plan_S != sh->S || d.plan_pcnt != p.off_pcnt) {
+    const hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t*>(base + p.off_pcnt),
+                                         (size_t)p.U, (hipStream_t)stream);
+    if (e != hipSuccess) return CKNV_EHIP;
+    d.plan_total = p.total;
+    d.plan_U = p.U;
+    d.plan_S = sh->S;
+    d.plan_pcnt = p.off_pcnt;
+  }
+  *ws = base;
+  return CKNV_OK;
+}
+
 static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const float* q,
                          const int32_t* sel, const int32_t* n_sel, int32_t budget_tokens,
                          int32_t max_blocks, float* out, float* lse, void* ws, size_t ws_bytes,
@@ -298,6 +349,23 @@ int cknv_dense_attend(const cknv_shape* shape, const cknv_cache* cache, const fl
                       void* ws, size_t ws_bytes, void* stream) {
   return attend_common(shape, cache, q, nullptr, nullptr, budget_tokens, max_blocks, out, lse,
                        ws, ws_bytes, stream, true);
+}
+
+int cknv_decode_step_noalloc(const cknv_shape* shape, const cknv_cache* cache,
+                             const uint16_t* new_k, const uint16_t* new_v, const float* q,
+                             int32_t budget_tokens, int32_t max_blocks, float* scores,
+                             int32_t* sel, int32_t* n_sel, float* out, float* lse, void* stream) {
+  Plan p;
+  int st = make_plan(shape, max_blocks, budget_tokens, &p);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!new_k || !new_v || !q || !sel || !n_sel || !out) return CKNV_EINVAL;
+  if (p.total > kNoAllocScratchBytes) return CKNV_ENOSPACE;
+  char* w = nullptr;
+  if ((st = noalloc_workspace(p, shape, stream, &w))) return st;
+  if ((st = decode_score_impl(p, shape, cache, new_k, new_v, q, max_blocks, w, stream))) return st;
+  return decode_finish_impl(p, shape, cache, q, max_blocks, scores, sel, n_sel, out, lse, w,
+                            stream);
 }
 
 const char* cknv_status_str(int status) {

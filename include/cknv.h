@@ -60,6 +60,9 @@ extern "C" {
 #define CKNV_ENOSPACE (-3)      /* workspace smaller than cknv_workspace_size, or max_blocks > cap_blocks */
 #define CKNV_EHIP (-4)          /* a HIP call or kernel launch failed */
 
+/* Size of the per-GPU device array cknv_decode_step_noalloc works in. */
+#define CKNV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
 /* Problem shape. */
 typedef struct cknv_shape {
   int32_t S;          /* sequences */
@@ -205,6 +208,23 @@ int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const f
 int cknv_dense_attend(const cknv_shape* shape, const cknv_cache* cache, const float* q,
                       int32_t budget_tokens, int32_t max_blocks, float* out, float* lse,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* cknv_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid allocation): the same
+ * arguments and results without `ws`/`ws_bytes`. Its workspace is a
+ * library-owned device array of CKNV_NOALLOC_SCRATCH_BYTES (32 MiB), one per
+ * GPU, held until the process ends; the call itself allocates and
+ * frees nothing. A shape, max_blocks and budget whose workspace
+ * (cknv_workspace_size) exceeds it return CKNV_ENOSPACE with nothing
+ * enqueued. Every call on a GPU shares that GPU's array, so calls that
+ * overlap on one GPU (other streams, other host threads) race: issue them
+ * in order on one stream. When the workspace layout changes from the
+ * previous call on the device, the call first clears the step counters with
+ * a kernel (no memset). */
+int cknv_decode_step_noalloc(const cknv_shape* shape, const cknv_cache* cache,
+                             const uint16_t* new_k, const uint16_t* new_v, const float* q,
+                             int32_t budget_tokens, int32_t max_blocks, float* scores,
+                             int32_t* sel, int32_t* n_sel, float* out, float* lse, void* stream);
 
 /* Name of a status code (static string). */
 const char* cknv_status_str(int status);

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = cknv.lib()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
 
@@ -187,3 +187,28 @@ def test_decode_halves_reject_before_launch():
         assert finish(**kw) == cknv.EINVAL, kw
     assert finish(ws_bytes=need - 1) == cknv.ENOSPACE
     assert finish(mb=2101) == cknv.ENOSPACE
+
+
+def test_noalloc_step_rejects_before_any_hip_call():
+    """The no-allocation step validates like cknv_decode_step, and a
+    workspace beyond its per-GPU array is refused (all before any HIP call)."""
+    L = cknv.lib()
+    c = cknv.Cache(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    sh = shape()
+    args = lambda sh_, mb, budget: (ctypes.byref(sh_), ctypes.byref(c), FAKE, FAKE, FAKE, budget,
+                                    mb, None, FAKE, FAKE, FAKE, None, None)
+    assert L.cknv_decode_step_noalloc(None, *args(sh, 2048, 512)[1:]) == cknv.EINVAL
+    assert L.cknv_decode_step_noalloc(*args(sh, 2048, 32)) == cknv.EINVAL
+    assert L.cknv_decode_step_noalloc(*args(sh, 5000, 512)) == cknv.ENOSPACE
+    a = list(args(sh, 2048, 512))
+    a[2] = None  # new_k
+    assert L.cknv_decode_step_noalloc(*a) == cknv.EINVAL
+    big = shape(S=16, cap_blocks=8300)
+    assert wsize(big, 8300, 2048)[1] > cknv.NOALLOC_SCRATCH_BYTES
+    assert L.cknv_decode_step_noalloc(*args(big, 8300, 2048)) == cknv.ENOSPACE
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define CKNV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == cknv.NOALLOC_SCRATCH_BYTES
