@@ -53,7 +53,8 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   bpw = bpw > kDenseBlocksPerWG ? bpw : kDenseBlocksPerWG;
   q.BPW = bpw;
   q.Pd = (max_blocks + bpw - 1) / bpw;
-  q.Pf = (q.Kb + step_kept_per_part(G) - 1) / step_kept_per_part(G);
+  q.kpw = step_kept_per_wave(q.U, q.Kb);
+  q.Pf = (q.Kb + kStepAttendWaves * q.kpw - 1) / (kStepAttendWaves * q.kpw);
   const size_t W = (size_t)rec_words(d);
   size_t off = 0;
   q.off_grp = off;
@@ -206,7 +207,7 @@ static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv
   sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel; sa.out = out; sa.lse = lse;
   sa.part = reinterpret_cast<float*>(w + p.off_fpart);
   sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
-  sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf;
+  sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf; sa.kpw = p.kpw;
   sa.bpw_shift = p.bpw == 8 ? 3 : 4;
   sa.xcd = (p.U % 8) == 0;
   sa.flags = (int)shape->flags;

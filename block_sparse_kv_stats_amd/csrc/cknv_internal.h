@@ -46,7 +46,8 @@ struct Plan {
   int Kb;           // block slots of the budget
   int C;            // score workgroups per unit = ceil(NBmax/(4*bpw))
   int P;            // attend workgroups per unit
-  int Pf;           // fused-step workgroups per unit = ceil(Kb/kStepKeptPerPart)
+  int Pf;           // fused-step workgroups per unit = ceil(Kb/(kStepAttendWaves*kpw))
+  int kpw;          // fused step: kept blocks per attending wave
   int Pd;           // dense-attend workgroups per unit
   int BPW;          // dense-attend blocks per workgroup
   size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, off_finfo, off_hdr, off_pcnt,
@@ -107,6 +108,7 @@ struct StepArgs {
   const float* finfo;  // per unit and query head: (a, factor) of the block the token landed in
   uint32_t* pcnt;      // per unit: parts done this step (zeroed by the scoring launch)
   int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P, bpw_shift;
+  int kpw;    // kept blocks per attending wave (a part attends kStepAttendWaves*kpw)
   int xcd;    // units a multiple of 8: a unit's parts share the XCD that scored it
   int flags;  // CKNV_FLAG_* (ablation variants)
   float isd;
@@ -228,6 +230,33 @@ __device__ __forceinline__ uint32_t stream_load_u1(const uint16_t* p) {
 template <bool NT = true>
 __device__ __forceinline__ uint32_t stream_load_h(const uint16_t* p) {
   return (uint32_t)ldg<NT>(p);
+}
+
+// N consecutive floats (N = 1, 2 or a multiple of 4) from a 4N-byte aligned
+// address, in vector loads of up to 16 bytes.
+template <int N>
+__device__ __forceinline__ void load_row(const float* p, float (&x)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 v = reinterpret_cast<const float4*>(p)[i / 4];
+      x[i] = v.x; x[i + 1] = v.y; x[i + 2] = v.z; x[i + 3] = v.w;
+    }
+  } else if constexpr (N == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    x[0] = v.x; x[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = p[i];
+  }
+}
+// N float2 (the (max, sum) pairs of N query heads) from a 8N-byte aligned address.
+template <int N>
+__device__ __forceinline__ void load_pairs(const float2* p, float2 (&x)[N]) {
+  float f[2 * N];
+  load_row<2 * N>(reinterpret_cast<const float*>(p), f);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = make_float2(f[2 * i], f[2 * i + 1]);
 }
 
 // Workgroup barrier for data exchanged through LDS only. __syncthreads()

@@ -16,8 +16,11 @@
 //
 // Grid: C workgroups ("chunks") per unit of kScoreWaves waves, 4*ROWS blocks
 // per wave; a block is read by 16 lanes (d/64 float4 of k̄, D̄ and v̄ each), so
-// the wave reads 4 blocks' rows per load instruction. Every load is issued before
-// seq_len is known; blocks past the context are masked afterwards. Per wave
+// the wave reads 4 blocks' rows per load instruction. For one sequence every
+// load is issued before seq_len is known (max_blocks bounds the block index);
+// a batch of several waits for it, so that a short sequence's chunks past its
+// end re-read one row instead of unused summaries. Blocks past the context
+// are masked afterwards. Per wave
 // (a 16-block group) the kernel writes the LSE partial of
 // a = ln|b| + z̄ + σ̂²/2 and per block u_{g,b} = exp(a - group max) σ̂²; per
 // chunk it writes the Mean-compensation sums of ALL its blocks,
@@ -295,29 +298,41 @@ void score_kernel(ScoreArgs a) {
   // the query goes to LDS (registers are what limits resident waves here)
   static_assert(G * D / 4 <= kScoreThreads, "one float4 of q per thread");
   const float4 qown = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : 0];
+  int NB = a.closed_only ? T / kBlock : (T + kBlock - 1) / kBlock;
+  NB = NB < MB ? NB : MB;
   float4 kv[ROWS][KC], vv[ROWS][KC];
   DbarTile<DM, ROWS, KC> dt;
+  float n;
+  float dbr[kRowMaxR];  // kDbarRow: D̄ of this lane's block tb
   const float4* kbar4 = reinterpret_cast<const float4*>(a.kbar);
   const float4* vbar4 = reinterpret_cast<const float4*>(a.vbar);
+  // lim: the highest block index read (indices are clamped to it)
+  auto issue_loads = [&](int lim) {
 #pragma unroll
-  for (int rw = 0; rw < ROWS; ++rw) {
-    const int b = base + 4 * rw + bg;
-    const size_t row = ubase + (b < MB ? b : MB - 1);
+    for (int rw = 0; rw < ROWS; ++rw) {
+      const int b = base + 4 * rw + bg;
+      const size_t row = ubase + (b < lim ? b : lim);
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = j + 16 * i;  // float4 chunk: coordinates 4c..4c+3
-      kv[rw][i] = stream_load4(kbar4 + row * (D / 4) + c);
-      if constexpr (!NC && !kDeferV) vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + c);
-      dt.load(a.dbar, row, c, r, D, rw, i);
+      for (int i = 0; i < KC; ++i) {
+        const int c = j + 16 * i;  // float4 chunk: coordinates 4c..4c+3
+        kv[rw][i] = stream_load4(kbar4 + row * (D / 4) + c);
+        if constexpr (!NC && !kDeferV) vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + c);
+        dt.load(a.dbar, row, c, r, D, rw, i);
+      }
     }
-  }
-  const size_t trow_idx = ubase + (tb < MB ? tb : MB - 1);
-  const float n = a.cnt[trow_idx];
-  float dbr[kRowMaxR];  // kDbarRow: D̄ of this lane's block tb
-  if constexpr (DM == kDbarRow) {
+    const size_t trow_idx = ubase + (tb < lim ? tb : lim);
+    n = a.cnt[trow_idx];
+    if constexpr (DM == kDbarRow) {
 #pragma unroll
-    for (int t = 0; t < kRowMaxR; ++t) dbr[t] = t < r ? a.dbar[trow_idx * r + t] : 0.f;
-  }
+      for (int t = 0; t < kRowMaxR; ++t) dbr[t] = t < r ? a.dbar[trow_idx * r + t] : 0.f;
+    }
+  };
+  // One sequence: the addresses do not wait for seq_len (max_blocks bounds
+  // it). A batch of several: a chunk past its sequence's end reads one row
+  // again and again (cached) instead of max_blocks' worth of unused rows.
+  if (a.S == 1) issue_loads(MB - 1);
+  else issue_loads(NB > 0 ? NB - 1 : 0);
+  const int lim = a.S == 1 ? MB - 1 : (NB > 0 ? NB - 1 : 0);
   // Keep the load block above: without this the scheduler sinks loads next
   // to their uses and the wave pays several dependent memory round trips.
   __builtin_amdgcn_sched_barrier(0);
@@ -335,8 +350,6 @@ void score_kernel(ScoreArgs a) {
     lds_barrier();
   }
 
-  int NB = a.closed_only ? T / kBlock : (T + kBlock - 1) / kBlock;
-  NB = NB < MB ? NB : MB;
   const float invd = 1.0f / (float)D;
 
   // ---- z̄ (and, per coordinate, σ̂²) partials over the lane's coordinates for
@@ -391,7 +404,7 @@ void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int rw = 0; rw < ROWS; ++rw) {
       const int b = base + 4 * rw + bg;
-      const size_t row = ubase + (b < MB ? b : MB - 1);
+      const size_t row = ubase + (b < lim ? b : lim);
 #pragma unroll
       for (int i = 0; i < KC; ++i) vv[rw][i] = stream_load4(vbar4 + row * (D / 4) + j + 16 * i);
     }

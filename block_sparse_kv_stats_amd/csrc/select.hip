@@ -65,11 +65,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   for (int k = 0; k < GPT; ++k) {
     const int gi = tid + k * kSelThreads;
     const int gc = gi < a.NG ? gi : a.NG - 1;
+    float2 v[G];
+    load_pairs<G>(reinterpret_cast<const float2*>(grp) + (size_t)gc * G, v);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float2 v = reinterpret_cast<const float2*>(grp)[(size_t)gc * G + g];
-      gr[k][g] = v.x;
-      gl[k][g] = v.y;
+      gr[k][g] = v[g].x;
+      gl[k][g] = v[g].y;
     }
   }
   // blocks of u per thread per batch: all of them up to 4 query heads (one round trip)
@@ -79,8 +80,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   for (int m = 0; m < UB0; ++m) {
     const int b = tid + m * kSelThreads;
     const int bc = b < MB ? b : MB - 1;
-#pragma unroll
-    for (int g = 0; g < G; ++g) ub[m][g] = u[(size_t)bc * G + g];
+    load_row<G>(u + (size_t)bc * G, ub[m]);
   }
   hist[tid] = 0;
   hist[tid + kSelThreads] = 0;
@@ -141,8 +141,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
       for (int m = 0; m < UB0; ++m) {
         const int b = tid + (m0 + m) * kSelThreads;
         const int bc = b < NB ? b : NB - 1;
-#pragma unroll
-        for (int g = 0; g < G; ++g) ub[m][g] = u[(size_t)bc * G + g];
+        load_row<G>(u + (size_t)bc * G, ub[m]);
       }
     }
 #pragma unroll

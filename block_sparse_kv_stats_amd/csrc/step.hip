@@ -62,8 +62,7 @@ struct StepCfg {
   static constexpr int UMAX = G >= 8 ? 64 / G : 128 / G;
   static constexpr int UB = KPT < UMAX ? KPT : UMAX;               // blocks per u load batch
   static constexpr int NBATCH = (KPT + UB - 1) / UB;
-  static constexpr int KPW = step_kept_per_wave(G);                // kept blocks per wave
-  static constexpr int KPART = step_kept_per_part(G);              // kept blocks per workgroup
+  static constexpr int KPART = kStepAttendWaves * kStepMaxKeptPerWave;  // kept blocks per workgroup, at most
   static constexpr int CPL = step_chunks_per_lane(KPTB);           // chunk headers per lane
   // Chunk records per record-folding wave loaded with the inputs (what the
   // registers left by the other inputs hold, 1..4), and per later batch.
@@ -73,7 +72,7 @@ struct StepCfg {
   static constexpr int RPW = 32 / RWORDS < 1 ? 1 : (32 / RWORDS > 4 ? 4 : 32 / RWORDS);
   static constexpr int AW = kStepAttendWaves;                      // attending waves
   static constexpr int RW = NW - AW;                               // record-folding waves
-  static_assert(KPART == AW * KPW && AW < NW, "kept slice of a workgroup");
+  static_assert(AW < NW, "record-folding waves");
 };
 
 // The lane's part of one chunk record of the scoring pass: (m, l) and the
@@ -214,7 +213,7 @@ template <int D, int G, int KPTB>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   using C = StepCfg<D, G, KPTB>;
   constexpr int NT = C::NT, NW = C::NW, KPT = C::KPT, UB = C::UB;
-  constexpr int GPT = C::GPT, NGMAX = C::NGMAX, KPW = C::KPW, KPART = C::KPART, AW = C::AW;
+  constexpr int GPT = C::GPT, NGMAX = C::NGMAX, KPART = C::KPART, AW = C::AW;
   constexpr int RW = C::RW;
   constexpr int CPL = C::CPL, RPF = C::RPF, RPW = C::RPW;
   constexpr int W = rec_words(D);
@@ -260,8 +259,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   // ================================================================ loads
   const int T0 = a.t0[s];
   float2 fi[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) fi[g] = reinterpret_cast<const float2*>(a.finfo)[(size_t)unit * G + g];
+  load_pairs<G>(reinterpret_cast<const float2*>(a.finfo) + (size_t)unit * G, fi);
   float2 hd[CPL][G];  // chunk lane + 64k: (max, sum) of a
   {
     const float2* hp = reinterpret_cast<const float2*>(a.hdr) + (size_t)unit * NC * G;
@@ -269,8 +267,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     for (int k = 0; k < CPL; ++k) {
       const int c = lane + 64 * k;
       const int cc = c < NC ? c : NC - 1;
-#pragma unroll
-      for (int g = 0; g < G; ++g) hd[k][g] = hp[(size_t)cc * G + g];
+      load_pairs<G>(hp + (size_t)cc * G, hd[k]);
     }
   }
   float2 gp[GPT][G];
@@ -278,8 +275,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   for (int k = 0; k < GPT; ++k) {
     const int gi = tid + k * NT;
     const int gc = gi < NG ? gi : NG - 1;
-#pragma unroll
-    for (int g = 0; g < G; ++g) gp[k][g] = grp[(size_t)gc * G + g];
+    load_pairs<G>(grp + (size_t)gc * G, gp[k]);
   }
   constexpr int NQ4 = (G * D / 4 + NT - 1) / NT;
   float4 q4[NQ4];
@@ -294,8 +290,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   for (int j = 0; j < UB; ++j) {
     const int b = tid + j * NT;
     const int bc = b < MB ? b : MB - 1;
-#pragma unroll
-    for (int g = 0; g < G; ++g) uv[j][g] = u[(size_t)bc * G + g];
+    load_row<G>(u + (size_t)bc * G, uv[j]);
   }
   // This part's chunk records are folded by the waves that attend no tile
   // (w >= AW), while the others attend: wave w folds records
@@ -381,8 +376,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       for (int m = 0; m < UB; ++m) {
         const int b = tid + (bt * UB + m) * NT;
         const int bc = b < MB ? b : MB - 1;
-#pragma unroll
-        for (int g = 0; g < G; ++g) uv[m][g] = u[(size_t)bc * G + g];
+        load_row<G>(u + (size_t)bc * G, uv[m]);
       }
     }
     float fr[UB][G];
@@ -519,45 +513,61 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   int nk;
   int pos = block_excl_scan<NW>(__popcll(takem), cnt, nk);
   int32_t* sel = a.sel + (size_t)unit * Kb;
-  const int lo = p * KPART;
+  const int kpart = AW * a.kpw;  // kept-list positions of this part: lo .. lo + kpart - 1
+  const int lo = p * kpart;
   for (uint64_t m = takem; m; m &= m - 1, ++pos) {
     const int b = b0 + __builtin_ctzll(m);
     if (p == 0 && pos < Kb) sel[pos] = b;
-    if (pos >= lo && pos < lo + KPART) klist[pos - lo] = b;
+    if (pos >= lo && pos < lo + kpart) klist[pos - lo] = b;
   }
   nk = nk < Kb ? nk : Kb;  // the selection keeps exactly min(Kb, NB); never index past sel
   if (p == 0 && tid == 0) a.n_sel[unit] = nk;
   lds_barrier();
 
   // ================================================================ attend
-  // Wave w < AW: kept blocks lo + w + AW*i of this part's slice (exact terms,
-  // minus their compensation where the scoring pass counted them); every
-  // tile is loaded before the first is absorbed.
+  // Wave w < AW: kept blocks lo + w + AW*i (i < kpw) of this part's slice
+  // (exact terms, minus their compensation where the scoring pass counted
+  // them), up to 4 query heads one tile ahead: the next tile's loads are
+  // issued before the current one is absorbed.
   if (wave < AW) {
-    int bk[KPW];
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int e = lo + wave + AW * i;
-      bk[i] = e < nk ? klist[wave + AW * i] : -1;
-    }
-    TileM<D> tile[KPW];
-    BlockMean<D> bm[KPW];
-#pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      const int b = bk[i] >= 0 ? bk[i] : 0;
-      tile[i].load(kc, vc, (long)b * kBlock, bk[i] >= 0 ? (long)T : 0, lane);
-      bm[i].load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
+    const int kpw = a.kpw;
+    auto load_block = [&](TileM<D>& t, BlockMean<D>& m, int i) {
+      const int e = wave + AW * i;
+      const int bk = lo + e < nk ? klist[e] : -1;
+      const int b = bk >= 0 ? bk : 0;
+      // an empty slot (bk < 0) holds no valid token and n = 0: it adds nothing
+      t.load(kc, vc, (long)b * kBlock, bk >= 0 ? (long)T : 0, lane);
+      m.load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
       // one code path: a block whose compensation the scoring pass did not
       // count removes a zero-mass term
-      if (!(bk[i] >= 0 && bk[i] < NBa && !nc)) bm[i].n = 0.f;
-    }
+      if (!(bk >= 0 && bk < NBa && !nc)) m.n = 0.f;
+    };
+    TileM<D> t0;
+    BlockMean<D> m0;
+    load_block(t0, m0, 0);
     QMfma<D> qm;
     qm.template build<G>(q_l, lane);
-    __builtin_amdgcn_sched_barrier(0);  // every tile load issued before the first use
-    // an empty slot (bk < 0) holds no valid token and n = 0: it adds nothing
-#pragma unroll
-    for (int i = 0; i < KPW; ++i)
-      absorb_mfma<D, G>(st, tile[i], bm[i], qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
+    if constexpr (G <= 4) {
+      TileM<D> t1;
+      BlockMean<D> m1;
+      for (int i = 0; i < kpw; i += 2) {
+        const bool more = i + 1 < kpw;
+        if (more) load_block(t1, m1, i + 1);
+        __builtin_amdgcn_sched_barrier(0);  // the next tile's loads issued before this one is used
+        absorb_mfma<D, G>(st, t0, m0, qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
+        if (!more) break;
+        if (i + 2 < kpw) load_block(t0, m0, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        absorb_mfma<D, G>(st, t1, m1, qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
+      }
+    } else {
+      // 8 query heads: one tile at a time (a second would not fit the registers)
+      for (int i = 0; i < kpw; ++i) {
+        if (i > 0) load_block(t0, m0, i);
+        __builtin_amdgcn_sched_barrier(0);
+        absorb_mfma<D, G>(st, t0, m0, qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
+      }
+    }
   }
   if (rw >= 0 && !nc) {
 #pragma unroll

@@ -178,6 +178,19 @@ def test_fused_ablation_variants_many_parts(flags):
     run_steps(w, flags=flags)
 
 
+@pytest.mark.parametrize("G,budget", [(4, 2048), (8, 512), (4, 320)])
+def test_fused_many_units_several_blocks_per_wave(G, budget):
+    """More units than the step kernel's resident workgroups: fewer parts per
+    unit, each attending wave taking several kept blocks in turn (16, 2 and
+    3 of them here; the last part's slots run past the kept list), every
+    unit checked against the oracle at two steps."""
+    rng = np.random.default_rng(11)
+    pre = tuple(int(x) for x in rng.integers(300, 6000, 16))
+    w = synth.Workload(f"many units G={G}", 84, S=16, H=8 if G == 4 else 4, G=G, d=128, r=4,
+                       budget=budget, prefill=pre, steps=2)
+    run_steps(w, check_every=1)
+
+
 @pytest.mark.parametrize("flags", [0, 1, 6])
 def test_fused_equals_three_calls(flags):
     """Same inputs through cknv_decode_step and through append + score_select
