@@ -51,7 +51,6 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   q.P = q.P > pc ? q.P : pc;
   int bpw = (max_blocks + kDenseMaxWGs - 1) / kDenseMaxWGs;
   bpw = bpw > kDenseBlocksPerWG ? bpw : kDenseBlocksPerWG;
-  q.BPW = bpw;
   q.Pd = (max_blocks + bpw - 1) / bpw;
   q.kpw = step_kept_per_wave(q.U, q.Kb);
   q.Pf = (q.Kb + kStepAttendWaves * q.kpw - 1) / (kStepAttendWaves * q.kpw);
@@ -330,7 +329,7 @@ static int attend_common(const cknv_shape* shape, const cknv_cache* cache, const
   a.comp = reinterpret_cast<const float*>(w + p.off_comp);
   a.part = reinterpret_cast<float*>(w + (dense ? p.off_dense : p.off_attp));
   a.S = shape->S; a.H = shape->H; a.cap_blocks = shape->cap_blocks; a.max_blocks = max_blocks;
-  a.Kb = p.Kb; a.C = p.C; a.P = dense ? p.Pd : p.P; a.BPW = p.BPW;
+  a.Kb = p.Kb; a.C = p.C; a.P = dense ? p.Pd : p.P;
   a.xcd = (p.U % 8) == 0;
   a.flags = (int)shape->flags;
   a.isd = 1.0f / sqrtf((float)shape->d);

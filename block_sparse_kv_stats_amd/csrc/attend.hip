@@ -21,7 +21,8 @@
 // the subtraction stays relative to the result.
 //
 // dense_kernel is the full-attention baseline: every block exact, no
-// compensation, a contiguous block range per workgroup.
+// compensation, the unit's blocks dealt round-robin over the waves of its
+// workgroups.
 #include "attend_core.h"
 
 namespace cknv {
@@ -101,72 +102,108 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   merge_records<D, G>(recs, kWaves + nrec, po, scl);
 }
 
+// Full attention, every block exact, no compensation: P workgroups of
+// kDenseThreads threads per unit, the unit's blocks dealt round-robin over
+// all their waves, each wave keeping several tiles of non-temporal loads in
+// flight, logits on MFMA; the waves' records merge into the workgroup's part
+// record, and merge_kernel merges the P part records.
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void dense_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   constexpr int W = rec_words(D);
-  constexpr int CAP = stage_cap<G>();
+  constexpr int NWV = kDenseThreads / 64;
   __shared__ __align__(16) float q_l[G * D];
-  __shared__ __align__(16) float recs[CAP * G * W];
-  __shared__ float scl[CAP * G + 3 * G];
+  __shared__ __align__(16) float recs[NWV * G * W];
+  __shared__ float scl[NWV * G + 3 * G];
+  __shared__ __align__(16) float pbuf[NWV * 16 * G];
 
   int unit, p;
   map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
   const int s = unit / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = a.seq_len[s];
+  static_assert(G * D / 4 <= kDenseThreads, "one float4 of q per thread");
   const float4 qv = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : G * D / 4 - 1];
-  if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
-  lds_barrier();
+  const int T = a.seq_len[s];
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < a.max_blocks ? NB : a.max_blocks;
   const long cap_tok = (long)a.cap_blocks * kBlock;
   const uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
   const uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
-  const int lo = p * a.BPW, hi = min(lo + a.BPW, NB);
+  // The unit's blocks are dealt round-robin over all its workgroups' waves
+  // (wave w of part p takes blocks p*NWV + w + k*P*NWV): at any moment the
+  // unit's waves read one contiguous stretch of the cache, spread over every
+  // memory channel, rather than P far-apart streams in lockstep.
+  const int stride = a.P * NWV;
+  // NBUF tiles per wave in flight: the loads of the wave's tile j + NBUF-1
+  // are issued before its tile j is absorbed (eight query heads leave room
+  // for one). The first tiles' loads go out before the query is staged.
+  constexpr int NBUF = G >= 8 ? 1 : kDenseTilesInFlight;
+  int b = p * NWV + wave;
+  TileM<D> t[NBUF];
+#pragma unroll
+  for (int i = 0; i + 1 < NBUF; ++i)
+    if (b + i * stride < NB) load_tile_whole<D>(t[i], kc, vc, (long)(b + i * stride) * kBlock, T, lane);
+  if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
+  lds_barrier();
   WaveState<D, G> st;
   st.init();
   BlockMean<D> none;
-  for (int b = lo + 2 * wave; b < hi; b += 2 * kWaves) {
-    Tile<D> t0, t1;
-    const bool u1 = b + 1 < hi;
-    t0.template load<true>(kc, vc, (long)b * kBlock, T, lane);
-    t1.template load<true>(kc, vc, (long)(u1 ? b + 1 : b) * kBlock, u1 ? (long)T : 0, lane);  // a valid block even when unused
-    absorb<D, G, false>(st, t0, none, q_l, lane, a.isd);
-    if (u1) absorb<D, G, false>(st, t1, none, q_l, lane, a.isd);
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) none.kb[e] = none.vb[e] = 0.f;
+  none.n = 0.f;
+  none.on = false;
+  QMfma<D> qm;
+  qm.template build<G>(q_l, lane);
+  float* pw = pbuf + wave * 16 * G;
+  for (; b < NB; b += NBUF * stride) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      const int bi = b + i * stride;
+      if (bi >= NB) break;
+      const int bn = bi + (NBUF - 1) * stride;
+      if (bn < NB) load_tile_whole<D>(t[(i + NBUF - 1) % NBUF], kc, vc, (long)bn * kBlock, T, lane);
+      __builtin_amdgcn_sched_barrier(0);  // the later tiles' loads issued before this one is used
+      absorb_mfma<D, G, false>(st, t[i], none, qm, q_l, pw, lane, a.isd);
+    }
   }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
   lds_barrier();
-  merge_records<D, G>(recs, kWaves, a.part + ((size_t)unit * a.P + p) * G * W, scl);
+  merge_records<D, G, kDenseThreads>(recs, NWV, a.part + ((size_t)unit * a.P + p) * G * W, scl);
 }
 
-// One workgroup per unit: merge the unit's P part records into out and lse.
+// Merge each unit's P part records into out and lse: kMergeCols workgroups
+// per unit, one output column per thread, all of a column's records loaded
+// in one round trip (up to 32 parts).
+constexpr int kMergeCols = kThreads;
+template <int D, int G>
+constexpr int merge_wgs() { return (G * D + kMergeCols - 1) / kMergeCols; }
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttendArgs a) {
-  constexpr int W = rec_words(D);
-  constexpr int CAP = stage_cap<G>();
-  __shared__ __align__(16) float recs[CAP * G * W];
-  __shared__ float scl[CAP * G + 3 * G];
-  const int unit = blockIdx.x;
-  finish_unit<D, G>(a.part + (size_t)unit * a.P * G * W, a.P, a.out + (size_t)unit * G * D,
-                    a.lse ? a.lse + (size_t)unit * G : nullptr, recs, CAP, scl);
+  constexpr int W = rec_words(D), CB = merge_wgs<D, G>();
+  const int unit = blockIdx.x / CB, cb = blockIdx.x - unit * CB;
+  merge_parts<D, G, kMergeCols, 32, 1, false>(a.part + (size_t)unit * a.P * G * W, a.P,
+                                              a.out + (size_t)unit * G * D,
+                                              a.lse ? a.lse + (size_t)unit * G : nullptr, cb * kMergeCols);
 }
 
 hipError_t launch_attend(int d, int G, bool dense, const AttendArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const void* f = nullptr;
   const void* m = nullptr;
+  int mw = 0;
 #define CKNV_ATT_CASE(DD, GG)                                                                  \
   if (d == DD && G == GG) {                                                                    \
     f = dense ? (const void*)dense_kernel<DD, GG> : (const void*)attend_kernel<DD, GG>;        \
     m = (const void*)merge_kernel<DD, GG>;                                                     \
+    mw = merge_wgs<DD, GG>();                                                                  \
   }
   CKNV_ATT_CASE(64, 1) CKNV_ATT_CASE(64, 2) CKNV_ATT_CASE(64, 4) CKNV_ATT_CASE(64, 8)
   CKNV_ATT_CASE(128, 1) CKNV_ATT_CASE(128, 2) CKNV_ATT_CASE(128, 4) CKNV_ATT_CASE(128, 8)
 #undef CKNV_ATT_CASE
   if (!f || !m) return hipErrorInvalidValue;
-  hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(kThreads), args, 0, st);
+  hipError_t e = hipLaunchKernel(f, dim3(U * a.P), dim3(dense ? kDenseThreads : kThreads), args, 0, st);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(m, dim3(U), dim3(kThreads), args, 0, st);
+  return hipLaunchKernel(m, dim3(U * mw), dim3(kThreads), args, 0, st);
 }
 
 }  // namespace cknv

@@ -71,6 +71,7 @@ template <int D>
 struct BlockMean {
   static constexpr int VPL = D / 64;
   float kb[VPL], vb[VPL], n;
+  bool on;  // false: the block removes no compensation (n is then not used)
   __device__ void load(const float* kbar_row, const float* vbar_row, const float* cnt, int lane) {
 #pragma unroll
     for (int e = 0; e < VPL; ++e) {
@@ -78,7 +79,11 @@ struct BlockMean {
       vb[e] = vbar_row[lane * VPL + e];
     }
     n = *cnt;
+    on = true;
   }
+  // n, or 0 where the block removes nothing (taken at use, so that setting
+  // `on` does not wait for the load of n)
+  __device__ __forceinline__ float mass() const { return on ? n : 0.f; }
 };
 
 // p of token 4*m + R (held by the lanes of row R) for R = 0..3, in every lane.
@@ -126,7 +131,7 @@ __device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, co
   for (int g = 0; g < G; ++g) {
     float bmax = fmaxf(fmaxf(z[0][g], z[1][g]), fmaxf(z[2][g], z[3][g]));
     bmax = rows_max(bmax);
-    if (COMP && bm.n > 0.f) bmax = fmaxf(bmax, zbar[g]);
+    if (COMP && bm.mass() > 0.f) bmax = fmaxf(bmax, zbar[g]);
     const float M = fmaxf(st.m[g], bmax);
     const float sc = rescale(st.m[g], M);
     float l = st.l[g] * sc;
@@ -151,7 +156,7 @@ __device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, co
       }
     }
     if (COMP) {
-      const float w = bm.n > 0.f ? bm.n * __expf(zbar[g] - M) : 0.f;
+      const float w = bm.mass() > 0.f ? bm.mass() * __expf(zbar[g] - M) : 0.f;
       l -= w;
 #pragma unroll
       for (int e = 0; e < VPL; ++e) acc[e] -= w * bm.vb[e];
@@ -185,23 +190,44 @@ struct TileM {
   u32x4_t k[NI];   // keys, MFMA A layout
   uint32_t v[16];  // values: lane's VPL coordinates of every token (as Tile)
   int nt;          // valid tokens
+  // NT: non-temporal loads (a streaming pass) or plain ones (a latency-bound gather)
+  template <bool NT = false>
   __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
     const long left = T - tok0;
     nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
-    const int last = nt > 0 ? nt - 1 : 0;  // loads read token min(t, last), masked after
+    const int last = nt > 0 ? nt - 1 : 0;  // loads read token min(t, last), values masked at use
     const int t = lane & 15, c = lane >> 4;
     const uint16_t* ks = kc + (size_t)(tok0 + (t < last ? t : last)) * D + (D / 4) * c;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      k[i] = *reinterpret_cast<const u32x4_t*>(ks + 8 * i);
+    for (int i = 0; i < NI; ++i) k[i] = ldg<NT>(reinterpret_cast<const u32x4_t*>(ks + 8 * i));
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint16_t* src = vc + (size_t)(tok0 + (j < last ? j : last)) * D + lane * VPL;
-      const uint32_t w = VPL == 2 ? stream_load_u1<false>(src) : stream_load_h<false>(src);
-      v[j] = j < nt ? w : 0u;
+      v[j] = VPL == 2 ? stream_load_u1<NT>(src) : stream_load_h<NT>(src);  // masked at use
     }
   }
 };
+
+// A TileM of block tok0/16 read whole (all 16 token slots; the block must lie
+// inside the cache's capacity): the addresses are one base plus fixed
+// offsets; slots at or past T are masked at use. Non-temporal (a streaming
+// pass).
+template <int D>
+__device__ __forceinline__ void load_tile_whole(TileM<D>& t, const uint16_t* kc, const uint16_t* vc,
+                                                long tok0, long T, int lane) {
+  constexpr int NI = D / 32, VPL = D / 64;
+  const long left = T - tok0;
+  t.nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+  const int tk = lane & 15, c = lane >> 4;
+  const uint16_t* ks = kc + (size_t)(tok0 + tk) * D + (D / 4) * c;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) t.k[i] = ldg<true>(reinterpret_cast<const u32x4_t*>(ks + 8 * i));
+  const uint16_t* vs = vc + (size_t)tok0 * D + lane * VPL;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    t.v[j] = VPL == 2 ? stream_load_u1<true>(vs + j * D) : stream_load_h<true>(vs + j * D);  // masked at use
+  }
+}
 
 // The query heads as MFMA B operands (head l%16 < G, zero columns after).
 template <int D>
@@ -228,10 +254,10 @@ __device__ __forceinline__ float lane_value(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// absorb<D, G, true> with the logits on MFMA: add one block's exact terms and
-// remove its compensation terms (none when bm.n = 0). `pw`: this wave's LDS
+// absorb<D, G, COMP> with the logits on MFMA: add one block's exact terms and
+// (COMP) remove its compensation terms (none when bm.mass() = 0). `pw`: this wave's LDS
 // scratch of 16*G floats (the probabilities, read back as broadcasts).
-template <int D, int G>
+template <int D, int G, bool COMP = true>
 __device__ __forceinline__ void absorb_mfma(WaveState<D, G>& st, const TileM<D>& t, const BlockMean<D>& bm,
                                             const QMfma<D>& qm, const float* q_l, float* pw, int lane,
                                             float isd) {
@@ -241,10 +267,13 @@ __device__ __forceinline__ void absorb_mfma(WaveState<D, G>& st, const TileM<D>&
   float zbar[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float zp = 0.f;
+    zbar[g] = -INFINITY;
+    if constexpr (COMP) {
+      float zp = 0.f;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) zp += bm.kb[e] * q_l[g * D + lane * VPL + e];
-    zbar[g] = group_sum<64>(zp) * isd;
+      for (int e = 0; e < VPL; ++e) zp += bm.kb[e] * q_l[g * D + lane * VPL + e];
+      zbar[g] = group_sum<64>(zp) * isd;
+    }
   }
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -262,10 +291,10 @@ __device__ __forceinline__ void absorb_mfma(WaveState<D, G>& st, const TileM<D>&
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float bmax = lane_value(cmax, g);
-    if (bm.n > 0.f) bmax = fmaxf(bmax, zbar[g]);
+    if (COMP && bm.mass() > 0.f) bmax = fmaxf(bmax, zbar[g]);
     M[g] = fmaxf(st.m[g], bmax);
     sc[g] = rescale(st.m[g], M[g]);
-    w[g] = bm.n > 0.f ? bm.n * __expf(zbar[g] - M[g]) : 0.f;
+    w[g] = COMP && bm.mass() > 0.f ? bm.mass() * __expf(zbar[g] - M[g]) : 0.f;
     Mj = j == g ? M[g] : Mj;
   }
   float p[4];
@@ -283,23 +312,33 @@ __device__ __forceinline__ void absorb_mfma(WaveState<D, G>& st, const TileM<D>&
 #pragma unroll
     for (int e = 0; e < VPL; ++e) st.acc[g][e] *= sc[g];
   }
-  // the wave reads back its own LDS writes (LDS operations of a wave run in order)
+  // the wave reads back its own LDS writes (LDS operations of a wave run in
+  // order), four tokens at a time: LDS reads do not move across the groups,
+  // so at most 4*G probabilities are held at once
 #pragma unroll
-  for (int tk = 0; tk < 16; ++tk) {
-    float pv[G];
+  for (int t4 = 0; t4 < 16; t4 += 4) {
+    if (t4 > 0) __builtin_amdgcn_sched_barrier(0x7F);  // ALU and global memory may cross, LDS may not
 #pragma unroll
-    for (int g = 0; g < G; ++g) pv[g] = pw[tk * G + g];
-    const uint32_t vw = t.v[tk];
+    for (int tk = t4; tk < t4 + 4; ++tk) {
+      float pv[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      st.acc[g][0] += pv[g] * bf16_lo(vw);
-      if (VPL == 2) st.acc[g][1 % VPL] += pv[g] * bf16_hi(vw);
+      for (int g = 0; g < G; ++g) pv[g] = pw[tk * G + g];
+      // tokens past nt may hold anything: their values are masked here, at
+      // use, so that the tile's loads need not complete when issued
+      const uint32_t vw = tk < t.nt ? t.v[tk] : 0u;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        st.acc[g][0] += pv[g] * bf16_lo(vw);
+        if (VPL == 2) st.acc[g][1 % VPL] += pv[g] * bf16_hi(vw);
+      }
     }
   }
+  if constexpr (COMP) {
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) st.acc[g][e] -= w[g] * bm.vb[e];
+      for (int e = 0; e < VPL; ++e) st.acc[g][e] -= w[g] * bm.vb[e];
+  }
 }
 
 // Write the wave's record [m, l, 0, 0, acc[D]] per g.
@@ -414,51 +453,63 @@ __device__ __forceinline__ void stage_records(const float* src, int n, float* ld
   }
 }
 
-// The unit's last workgroup: merge its P part records into out and lse.
-// `stage` holds `cap` records of LDS, `scl` cap*G + 3*G floats.
-template <int D, int G, int NT = kThreads>
-__device__ void finish_unit(const float* parts, int P, float* out, float* lse, float* stage,
-                            int cap, float* scl) {
+// Merge a unit's P part records into out and lse. Thread t owns output
+// columns col0 + t + NT*k (k < COLS); records are read in batches of PB,
+// every load of a batch issued before the first use. COHERENT: agent-scope
+// loads (records written by other workgroups of the same launch with
+// agent-scope stores).
+template <int D, int G, int NT, int PB, int COLS, bool COHERENT>
+__device__ void merge_parts(const float* parts, int P, float* out, float* lse, int col0) {
   constexpr int W = rec_words(D);
-  constexpr int COLS = (G * D + NT - 1) / NT;
   const int tid = threadIdx.x;
-  float* Mrun = scl + cap * G;  // [G] running max
-  float* Lrun = Mrun + G;       // [G] running normaliser
-  float* Srun = Lrun + G;       // [G] factor applied to the running sums this round
-  float Ar[COLS];
+  auto ld = [](const float* p) {
+    if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+  };
+  float M[COLS], L[COLS], A[COLS];
 #pragma unroll
-  for (int k = 0; k < COLS; ++k) Ar[k] = 0.f;
-  if (tid < G) { Mrun[tid] = -INFINITY; Lrun[tid] = 0.f; }
-  for (int p0 = 0; p0 < P; p0 += cap) {
-    const int n = P - p0 < cap ? P - p0 : cap;
-    stage_records<D, G, NT>(parts + (size_t)p0 * G * W, n, stage);
-    lds_barrier();
-    if (tid < G) {
-      float M = Mrun[tid], L = Lrun[tid];
-      record_scales<D, G>(stage, n, tid, scl, M, L, Srun + tid);
-      Mrun[tid] = M;
-      Lrun[tid] = L;
-    }
-    lds_barrier();
+  for (int k = 0; k < COLS; ++k) { M[k] = -INFINITY; L[k] = 0.f; A[k] = 0.f; }
+  for (int p0 = 0; p0 < P; p0 += PB) {
+    float m[PB][COLS], l[PB][COLS], x[PB][COLS];
 #pragma unroll
-    for (int k = 0; k < COLS; ++k) {
-      const int col = tid + k * NT;
-      if (col < G * D) {
+    for (int i = 0; i < PB; ++i) {
+      const int pi = p0 + i < P ? p0 + i : P - 1;
+#pragma unroll
+      for (int k = 0; k < COLS; ++k) {
+        int col = col0 + tid + k * NT;
+        col = col < G * D ? col : G * D - 1;
         const int g = col / D, c = col - g * D;
-        Ar[k] = Ar[k] * Srun[g] + record_column<D, G>(stage, scl, n, g, c);
+        const float* r = parts + ((size_t)pi * G + g) * W;
+        m[i][k] = p0 + i < P ? ld(r) : -INFINITY;
+        l[i][k] = ld(r + 1);
+        x[i][k] = ld(r + 4 + c);
       }
     }
-    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < COLS; ++k) {
+      float MM = M[k];
+#pragma unroll
+      for (int i = 0; i < PB; ++i) MM = fmaxf(MM, m[i][k]);
+      const float so = rescale(M[k], MM);
+      float LL = L[k] * so, AA = A[k] * so;
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const float f = rescale(m[i][k], MM);
+        LL += l[i][k] * f;
+        AA += x[i][k] * f;
+      }
+      M[k] = MM;
+      L[k] = LL;
+      A[k] = AA;
+    }
   }
 #pragma unroll
   for (int k = 0; k < COLS; ++k) {
-    const int col = tid + k * NT;
+    const int col = col0 + tid + k * NT;
     if (col < G * D) {
-      const int g = col / D, c = col - g * D;
-      const float L = Lrun[g];
-      const bool ok = L > 0.f;
-      out[col] = ok ? Ar[k] / L : 0.f;
-      if (c == 0 && lse) lse[g] = ok ? Mrun[g] + __logf(L) : -INFINITY;
+      const bool ok = L[k] > 0.f;
+      out[col] = ok ? A[k] / L[k] : 0.f;
+      if (col % D == 0 && lse) lse[col / D] = ok ? M[k] + __logf(L[k]) : -INFINITY;
     }
   }
 }

@@ -26,8 +26,10 @@ __host__ __device__ constexpr int score_rows(int G, int max_blocks, int units) {
 }
 constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
-constexpr int kDenseBlocksPerWG = 32;     // dense attention: blocks per workgroup (at least)
-constexpr int kDenseMaxWGs = 64;          // dense attention: workgroups per unit (at most)
+constexpr int kDenseThreads = 512;        // dense attention: 8 waves per workgroup
+constexpr int kDenseBlocksPerWG = 64;     // dense attention: blocks per workgroup (at least, on average)
+constexpr int kDenseMaxWGs = 32;          // dense attention: workgroups per unit (at most)
+constexpr int kDenseTilesInFlight = 3;   // dense attention: tiles per wave in flight (fewer than eight heads)
 constexpr int kSelThreads = 1024;       // selection: one workgroup per unit
 constexpr int kSelKeysPerThread = 12;   // blocks per selection thread: max_blocks <= 12288
 
@@ -49,7 +51,6 @@ struct Plan {
   int Pf;           // fused-step workgroups per unit = ceil(Kb/(kStepAttendWaves*kpw))
   int kpw;          // fused step: kept blocks per attending wave
   int Pd;           // dense-attend workgroups per unit
-  int BPW;          // dense-attend blocks per workgroup
   size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, off_finfo, off_hdr, off_pcnt,
       total;
 };
@@ -95,7 +96,7 @@ struct AttendArgs {
   const uint16_t* k; const uint16_t* v; const float* kbar; const float* vbar; const float* cnt;
   const int32_t* seq_len; const float* q; const int32_t* sel; const int32_t* n_sel;
   float* out; float* lse; const float* comp; float* part;
-  int S, H, cap_blocks, max_blocks, Kb, C, P, BPW, xcd;  // BPW: dense blocks per workgroup
+  int S, H, cap_blocks, max_blocks, Kb, C, P, xcd;
   int flags;  // CKNV_FLAG_* (ablation variants)
   float isd;
 };

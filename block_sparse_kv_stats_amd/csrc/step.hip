@@ -143,64 +143,6 @@ __device__ __forceinline__ void fold_record(WaveState<D, G>& st, const RecordReg
   }
 }
 
-// The last part of a unit: merge the unit's P part records (written by the
-// other parts with agent-scope stores, so read with agent-scope loads) into
-// out and lse. Thread t owns output columns t + NT*k; records are read in
-// batches of PB, every load of a batch issued before the first use.
-template <int D, int G, int NT, int PB>
-__device__ void merge_parts(const float* parts, int P, float* out, float* lse) {
-  constexpr int W = rec_words(D);
-  constexpr int COLS = (G * D + NT - 1) / NT;  // output columns per thread
-  const int tid = threadIdx.x;
-  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  float M[COLS], L[COLS], A[COLS];
-#pragma unroll
-  for (int k = 0; k < COLS; ++k) { M[k] = -INFINITY; L[k] = 0.f; A[k] = 0.f; }
-  for (int p0 = 0; p0 < P; p0 += PB) {
-    float m[PB][COLS], l[PB][COLS], x[PB][COLS];
-#pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int pi = p0 + i < P ? p0 + i : P - 1;
-#pragma unroll
-      for (int k = 0; k < COLS; ++k) {
-        int col = tid + k * NT;
-        col = col < G * D ? col : G * D - 1;
-        const int g = col / D, c = col - g * D;
-        const float* r = parts + ((size_t)pi * G + g) * W;
-        m[i][k] = p0 + i < P ? ld(r) : -INFINITY;
-        l[i][k] = ld(r + 1);
-        x[i][k] = ld(r + 4 + c);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < COLS; ++k) {
-      float MM = M[k];
-#pragma unroll
-      for (int i = 0; i < PB; ++i) MM = fmaxf(MM, m[i][k]);
-      const float so = rescale(M[k], MM);
-      float LL = L[k] * so, AA = A[k] * so;
-#pragma unroll
-      for (int i = 0; i < PB; ++i) {
-        const float f = rescale(m[i][k], MM);
-        LL += l[i][k] * f;
-        AA += x[i][k] * f;
-      }
-      M[k] = MM;
-      L[k] = LL;
-      A[k] = AA;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < COLS; ++k) {
-    const int col = tid + k * NT;
-    if (col < G * D) {
-      const bool ok = L[k] > 0.f;
-      out[col] = ok ? A[k] / L[k] : 0.f;
-      if (col % D == 0 && lse) lse[col / D] = ok ? M[k] + __logf(L[k]) : -INFINITY;
-    }
-  }
-}
-
 }  // namespace
 
 // A sequence appends (and its seq_len advances) when its cache has room and
@@ -540,7 +482,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       m.load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
       // one code path: a block whose compensation the scoring pass did not
       // count removes a zero-mass term
-      if (!(bk >= 0 && bk < NBa && !nc)) m.n = 0.f;
+      m.on = bk >= 0 && bk < NBa && !nc;
     };
     TileM<D> t0;
     BlockMean<D> m0;
@@ -611,12 +553,16 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   if (!ctl[4]) return;
   // up to 32 parts in one batch (one round trip) while a thread owns one
   // output column (more would spill), else batches of 8
+  // (the other parts' records were written with agent-scope stores, so they
+  // are read with agent-scope loads)
+  constexpr int COLS = (G * D + NT - 1) / NT;
   if (G * D <= NT && P > 8 && P <= 32)
-    merge_parts<D, G, NT, (G * D <= NT ? 32 : 8)>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
-                              a.lse ? a.lse + (size_t)unit * G : nullptr);
+    merge_parts<D, G, NT, (G * D <= NT ? 32 : 8), COLS, true>(
+        a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
+        a.lse ? a.lse + (size_t)unit * G : nullptr, 0);
   else
-    merge_parts<D, G, NT, 8>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
-                             a.lse ? a.lse + (size_t)unit * G : nullptr);
+    merge_parts<D, G, NT, 8, COLS, true>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
+                                         a.lse ? a.lse + (size_t)unit * G : nullptr, 0);
   if (tid == 0) {
     __hip_atomic_store(a.pcnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (h == 0 && app) a.seq_len[s] = T;
