@@ -20,7 +20,9 @@ one host thread and on a process pool over the layer's (sequence, KV head)
 units (run before the first GPU call). The three-call path (cknv_append,
 cknv_score_select, cknv_attend), the dense full-attention kernel and the
 other workloads (64K r = 128, the 16-sequence ragged batch) are reported
-beside it.
+beside it, and so is the host-offload placement (`host_offload`: the same
+step and the dense baseline with the KV cache in pinned host memory, with
+the bytes each step moves over the host link).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_32k]
 """
@@ -86,6 +88,19 @@ def step_bytes(w, T, budget=None):
         score += w.H * (closed * (w.d + w.r + 1) * 4 + (closed - kept_closed) * w.d * 4 + append)
         attend += w.H * ((kept - 1) * 16 + open_n) * 2 * w.d * 2
     return score, attend
+
+
+def host_link_bytes(w, T, budget=None) -> int:
+    """Bytes one fused step moves over the host link when the KV cache lives
+    in pinned host memory (summaries in HBM): the kept blocks' BF16 K and V
+    read by step_kernel, the open block's cached tokens read for its
+    summary, and the step's token written."""
+    _, attend = step_bytes(w, T, budget)
+    extra = 0
+    for Ts in _per_seq(w, T):
+        open_n = Ts - 16 * (math.ceil(Ts / 16) - 1)
+        extra += w.H * ((open_n - 1) * 2 * w.d * 2 + 2 * w.d * 2)
+    return attend + extra
 
 
 def dense_bytes(w, T) -> int:
@@ -218,7 +233,7 @@ def cpu_baseline(w, seconds: float, pool: bool = True):
 
 # ---------------------------------------------------------------- GPU side
 class Bench:
-    def __init__(self, w, R, appends, stream, budgets=None):
+    def __init__(self, w, R, appends, stream, budgets=None, kv_on_host=False):
         import numpy as np
         import torch
         from block_sparse_kv_stats_amd import cknv, synth
@@ -237,7 +252,7 @@ class Bench:
         def dev_bf16(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
 
-        base = cknv.LayerCache.allocate(shape)
+        base = cknv.LayerCache.allocate(shape, kv_on_host=kv_on_host)
         for s, T0 in enumerate(pre):  # each sequence's prefill, later slots zero
             base.k[s, :, :T0].copy_(dev_bf16(data["k"][s, :, :T0]))
             base.v[s, :, :T0].copy_(dev_bf16(data["v"][s, :, :T0]))
@@ -245,9 +260,7 @@ class Bench:
         cknv.build_summaries(base, self.max_blocks)
         torch.cuda.synchronize()
         log(f"replicating {R} layers")
-        self.layers = [base] + [cknv.LayerCache(shape, *(t.clone() for t in (
-            base.k, base.v, base.kbar, base.dbar, base.cnt, base.vbar, base.seq_len)))
-            for _ in range(R - 1)]
+        self.layers = [base] + [base.replicate() for _ in range(R - 1)]
         nq = w.steps if w.steps > 1 else 1
         self.q = [torch.from_numpy(data["q"][i % nq]).cuda() for i in range(R)]
         tok = lambda a: np.stack([a[s, :, pre[s]] for s in range(w.S)])
@@ -437,9 +450,10 @@ def layers_for(step_total_bytes, args):
     return max(2, math.ceil(2 * MALL_BYTES / step_total_bytes))
 
 
-def run_workload(torch, timer, wname, args, stream, full=True):
+def run_workload(torch, timer, wname, args, stream, full=True, kv_on_host=False):
     """The main workload (full=True: every figure) or an extra one (steps/s,
-    kernel durations and the dense baseline)."""
+    kernel durations and the dense baseline). kv_on_host: the KV cache in
+    pinned host memory (the host-offload placement)."""
     from block_sparse_kv_stats_amd import synth
 
     w = synth.WORKLOADS[wname]
@@ -456,11 +470,12 @@ def run_workload(torch, timer, wname, args, stream, full=True):
     per_budget = (math.ceil(warm / R) + math.ceil(steps / R) + 2 * math.ceil(n_e / R)
                   + 2 * sweeps + math.ceil(max(R, steps // 4) / R) * (2 if full else 1) + 2)
     appends = per_budget * len(budgets) + 4
-    bench = Bench(w, R, appends, stream, budgets)
+    bench = Bench(w, R, appends, stream, budgets, kv_on_host=kv_on_host)
     res = {"w": w, "R": R, "steps": steps, "warmup": warm, "by_budget": {}}
     for b in budgets:
         bench.use_budget(b)
-        log(f"{wname} budget {b}: {R} layers, {warm} warm-up + {steps} timed steps")
+        log(f"{wname} budget {b}: {R} layers, {warm} warm-up + {steps} timed steps"
+            + (" (KV cache in pinned host memory)" if kv_on_host else ""))
         with torch.cuda.stream(stream):
             for li in bench.order(warm):
                 bench.bound[li].fused_step()
@@ -494,15 +509,15 @@ def run_workload(torch, timer, wname, args, stream, full=True):
 # ---------------------------------------------------------------- profiles
 PROFILE_COMMANDS = {
     "trace": 'rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace -o trace -- '
-             'python3 bench.py --no-cpu --no-dense --also ""',
+             'python3 bench.py --no-cpu --no-dense --no-host-offload --also ""',
     "fetch": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/fetch -o fetch -- '
-             'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --also ""',
+             'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --no-host-offload --also ""',
     "write": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/write -o write -- '
-             'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --also ""',
+             'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --no-host-offload --also ""',
     "fetch128": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/fetch128 -o fetch128 -- '
-                'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --workload qwen8b_128k --also ""',
+                'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --no-host-offload --workload qwen8b_128k --also ""',
     "write128": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/write128 -o write128 -- '
-                'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --workload qwen8b_128k --also ""',
+                'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --no-host-offload --workload qwen8b_128k --also ""',
     "copy_fetch": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/copy_fetch -o cf -- '
                   'python3 bench.py --copy-probe 268435456',
     "copy_write": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/copy_write -o cw -- '
@@ -690,6 +705,29 @@ def extra_line(res, wkey):
     return out
 
 
+def host_line(res):
+    """The host-offload placement's figures: the fused step and the dense
+    baseline with the KV cache in pinned host memory."""
+    w = res["w"]
+    r = res["by_budget"][w.budget]
+    link = host_link_bytes(w, r["T"], w.budget)
+    out = {"workload": w.name, "budget_tokens": w.budget,
+           "placement": "BF16 K/V in pinned host memory (torch pin_memory, i.e. hipHostMalloc), "
+                        "mapped at the same address; summaries, workspace and outputs in HBM",
+           "layers_rotated": res["R"], "steps": res["steps"],
+           "steps_per_s": round(1000.0 / r["ms_step"], 2), "us_per_step": round(r["ms_step"] * 1e3, 3),
+           "host_link_bytes_per_step": link,
+           "host_link_GBps": round(gbps(link, r["ms_step"]), 2),
+           "eager_step_us_p10_p50_p90": [round(x * 1e3, 2) for x in r["pct"]],
+           "kernels_us": {"score_kernel": round(r["score_ms"] * 1e3, 3),
+                          "step_kernel": round(r["finish_ms"] * 1e3, 3)}}
+    if "dense_ms" in r:
+        out["dense_steps_per_s"] = round(1000.0 / r["dense_ms"], 2)
+        out["dense_host_link_GBps"] = round(gbps(r["dense_bytes"], r["dense_ms"]), 2)
+        out["speedup_of_compkv"] = round(r["dense_ms"] / r["ms_step"], 3)
+    return out
+
+
 def build_line(res):
     g = gbps(res["build_bytes"], res["build_ms"])
     return {"kernel": "build_kernel (cknv_build_summaries)", "avg_us": round(res["build_ms"] * 1e3, 2),
@@ -709,6 +747,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-host-offload", action="store_true",
+                    help="skip the host-offload placement (KV cache in pinned host memory)")
     ap.add_argument("--copy-probe", type=int, default=0, help="run only a device copy of this many bytes")
     ap.add_argument("--summarize-profiles", default="",
                     help="write profiles/ summaries from rocprofv3 output in this directory")
@@ -745,6 +785,10 @@ def main():
     extras = [x for x in args.also.split(",") if x and x != args.workload]
     extra_res = {x: run_workload(torch, timer, x, args, stream, full=(x == "qwen8b_128k"))
                  for x in extras}
+    host_res = None
+    if not args.no_host_offload:
+        host_res = run_workload(torch, timer, args.workload, args, stream, full=False,
+                                kv_on_host=True)
 
     w = main_res["w"]
     r = main_res["by_budget"][w.budget]
@@ -783,6 +827,8 @@ def main():
             "speedup_of_compkv": round(r["dense_ms"] / r["ms_step"], 3)}
     if extra_res:
         line["also"] = {x: extra_line(res, x) for x, res in extra_res.items()}
+    if host_res is not None:
+        line["host_offload"] = host_line(host_res)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

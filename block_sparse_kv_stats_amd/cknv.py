@@ -60,7 +60,10 @@ SIGNATURES = {
                            P, P, SZ, P],
     "cknv_decode_step_noalloc": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), P, P, P, I32, I32,
                                  P, P, P, P, P, P],
+    "cknv_kv_placement": [ctypes.POINTER(Shape), ctypes.POINTER(Cache), ctypes.POINTER(I32)],
 }
+KV_ON_HOST = 0x1          # CKNV_KV_ON_HOST
+SUMMARIES_ON_HOST = 0x2   # CKNV_SUMMARIES_ON_HOST
 NOALLOC_SCRATCH_BYTES = 32 << 20  # CKNV_NOALLOC_SCRATCH_BYTES
 
 
@@ -100,11 +103,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _ptr(t, dtype=None, numel=None, what=""):
+def _ptr(t, dtype=None, numel=None, what="", host_ok=False):
+    """The address of tensor t, after checking its dtype, size and layout.
+    host_ok: pinned host memory is accepted too (a cache's arrays in the
+    host-offload placement); pageable host memory never is."""
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError(f"{what}: expected a device tensor")
+    if not t.is_cuda and not (host_ok and t.is_pinned()):
+        raise ValueError(f"{what}: expected a device tensor" + (" or pinned host memory" if host_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{what}: expected a contiguous tensor")
     if dtype is not None and t.dtype not in dtype:
@@ -126,7 +132,9 @@ def make_shape(S, H, G, d, r, cap_blocks, flags=0) -> Shape:
 
 @dataclasses.dataclass
 class LayerCache:
-    """Device tensors of one layer's KV cache and summary store (see cknv.h)."""
+    """Tensors of one layer's KV cache and summary store (see cknv.h): device
+    tensors, or for k/v (and the summaries) pinned host tensors in the
+    host-offload placement (cknv_kv_placement)."""
     shape: Shape
     k: object        # bf16 [S][H][cap_blocks*16][d]
     v: object
@@ -135,33 +143,74 @@ class LayerCache:
     cnt: object      # fp32 [S][H][cap_blocks]
     vbar: object     # fp32 [S][H][cap_blocks][d]
     seq_len: object  # int32 [S]
+    _placement: object = dataclasses.field(default=None, repr=False, compare=False)
 
     @staticmethod
-    def allocate(shape: Shape, device="cuda"):
+    def allocate(shape: Shape, device="cuda", kv_on_host=False, summaries_on_host=False):
+        """Zeroed arrays; kv_on_host / summaries_on_host put k and v / the
+        four summary arrays in pinned host memory (torch's pin_memory, which
+        allocates with hipHostMalloc), seq_len always on the device."""
         import torch
         S, H, d, r, cb = shape.S, shape.H, shape.d, shape.r, shape.cap_blocks
-        f32 = dict(dtype=torch.float32, device=device)
-        return LayerCache(
-            shape,
-            torch.zeros((S, H, cb * BLOCK, d), dtype=torch.bfloat16, device=device),
-            torch.zeros((S, H, cb * BLOCK, d), dtype=torch.bfloat16, device=device),
-            torch.zeros((S, H, cb, d), **f32), torch.zeros((S, H, cb, r), **f32),
-            torch.zeros((S, H, cb), **f32), torch.zeros((S, H, cb, d), **f32),
-            torch.zeros((S,), dtype=torch.int32, device=device))
 
-    def c_struct(self) -> Cache:
+        def zeros(size, dtype, host):
+            if host:
+                return torch.zeros(size, dtype=dtype, pin_memory=True)
+            return torch.zeros(size, dtype=dtype, device=device)
+
+        kv = lambda: zeros((S, H, cb * BLOCK, d), torch.bfloat16, kv_on_host)
+        sm = lambda last: zeros((S, H, cb) + last, torch.float32, summaries_on_host)
+        c = LayerCache(shape, kv(), kv(), sm((d,)), sm((r,)), sm(()), sm((d,)),
+                       torch.zeros((S,), dtype=torch.int32, device=device))
+        want = (KV_ON_HOST if kv_on_host else 0) | (SUMMARIES_ON_HOST if summaries_on_host else 0)
+        if c.placement() != want:
+            raise RuntimeError(f"cache placement {c.placement()} is not the requested {want}")
+        return c
+
+    def like(self):
+        """A zeroed cache of the same shape and placement."""
+        p = self.placement()
+        return LayerCache.allocate(self.shape, self.seq_len.device, bool(p & KV_ON_HOST),
+                                   bool(p & SUMMARIES_ON_HOST))
+
+    def replicate(self):
+        """A copy of this cache (same shape and placement, distinct memory)."""
+        c = self.like()
+        for a, b in zip(c.tensors(), self.tensors()):
+            a.copy_(b)
+        return c
+
+    def tensors(self):
+        return (self.k, self.v, self.kbar, self.dbar, self.cnt, self.vbar, self.seq_len)
+
+    def placement(self) -> int:
+        """cknv_kv_placement of this cache (checked once; host arrays are
+        verified before any kernel can touch them)."""
+        if self._placement is None:
+            pl = I32(0)
+            _check(lib().cknv_kv_placement(ctypes.byref(self.shape), ctypes.byref(self._raw_struct()),
+                                           ctypes.byref(pl)), "cknv_kv_placement")
+            self._placement = int(pl.value)
+        return self._placement
+
+    def _raw_struct(self) -> Cache:
         import torch
         s = self.shape
         n_tok = s.S * s.H * s.cap_blocks * BLOCK * s.d
         n_row = s.S * s.H * s.cap_blocks
         bf = (torch.bfloat16, torch.int16, torch.uint16)
         f32 = (torch.float32,)
-        return Cache(_ptr(self.k, bf, n_tok, "k"), _ptr(self.v, bf, n_tok, "v"),
-                     _ptr(self.kbar, f32, n_row * s.d, "kbar"),
-                     _ptr(self.dbar, f32, n_row * s.r, "dbar"),
-                     _ptr(self.cnt, f32, n_row, "cnt"),
-                     _ptr(self.vbar, f32, n_row * s.d, "vbar"),
+        return Cache(_ptr(self.k, bf, n_tok, "k", True), _ptr(self.v, bf, n_tok, "v", True),
+                     _ptr(self.kbar, f32, n_row * s.d, "kbar", True),
+                     _ptr(self.dbar, f32, n_row * s.r, "dbar", True),
+                     _ptr(self.cnt, f32, n_row, "cnt", True),
+                     _ptr(self.vbar, f32, n_row * s.d, "vbar", True),
                      _ptr(self.seq_len, (torch.int32,), s.S, "seq_len"))
+
+    def c_struct(self) -> Cache:
+        if any(not t.is_cuda for t in self.tensors()):
+            self.placement()  # host arrays: the device must map them at the same address
+        return self._raw_struct()
 
 
 def workspace_size(shape: Shape, max_blocks: int, budget: int) -> int:
@@ -289,7 +338,7 @@ class DecodeStep:
         import torch
         self.fused = fused
         s = cache.shape
-        dev = cache.k.device
+        dev = cache.seq_len.device  # k and v may be host-resident (host-offload placement)
         self.cache, self.max_blocks, self.budget = cache, max_blocks, budget
         self.Kb = budget // BLOCK
         self.ws = allocate_workspace(s, max_blocks, budget, device=dev, stream=stream)

@@ -368,6 +368,38 @@ int cknv_decode_step_noalloc(const cknv_shape* shape, const cknv_cache* cache,
                             stream);
 }
 
+int cknv_kv_placement(const cknv_shape* shape, const cknv_cache* cache, int32_t* placement) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if ((st = check_cache(cache))) return st;
+  if (!placement) return CKNV_EINVAL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return CKNV_EHIP;
+  }
+  // 0: device memory of this device, 1: pinned host memory this device maps
+  // at the same address, -1: anything else
+  auto where = [dev](const void* ptr) {
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, ptr) != hipSuccess) {
+      (void)hipGetLastError();  // unknown to the runtime: pageable host memory
+      return -1;
+    }
+    if (at.type == hipMemoryTypeDevice) return at.device == dev ? 0 : -1;
+    if (at.type == hipMemoryTypeHost) return at.devicePointer == ptr ? 1 : -1;
+    return -1;
+  };
+  const int k = where(cache->k), v = where(cache->v);
+  if (k < 0 || k != v) return CKNV_EINVAL;
+  const int sm = where(cache->kbar);
+  if (sm < 0 || where(cache->dbar) != sm || where(cache->cnt) != sm || where(cache->vbar) != sm)
+    return CKNV_EINVAL;
+  if (where(cache->seq_len) != 0) return CKNV_EINVAL;
+  *placement = (k ? CKNV_KV_ON_HOST : 0) | (sm ? CKNV_SUMMARIES_ON_HOST : 0);
+  return CKNV_OK;
+}
+
 const char* cknv_status_str(int status) {
   switch (status) {
     case CKNV_OK: return "CKNV_OK";

@@ -21,7 +21,10 @@
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer owned by the caller, except the
  *     cknv_shape / cknv_cache structs themselves (host memory, read during
- *     the call only) and the `bytes` out-parameter of cknv_workspace_size.
+ *     the call only) and the out-parameters of cknv_workspace_size and
+ *     cknv_kv_placement. The KV and summary arrays of a cknv_cache may
+ *     instead be pinned host memory that the device reads and writes at
+ *     the same address (the host-offload placement, see cknv_kv_placement).
  *     The library never allocates, frees or synchronises.
  *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
  *     asynchronously; results are ready when the stream reaches them.
@@ -201,6 +204,27 @@ int cknv_decode_finish(const cknv_shape* shape, const cknv_cache* cache, const f
                        int32_t budget_tokens, int32_t max_blocks, float* scores, int32_t* sel,
                        int32_t* n_sel, float* out, float* lse, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* Where a cache's arrays live, checked before any of them is used on the
+ * device. The page keeps the BF16 KV cache and the FP32 summaries in pinned
+ * CPU memory and moves what a step needs over the host link ("How to use
+ * it"); here every entry point also accepts k and v, and the four summary
+ * arrays, in pinned host memory (hipHostMalloc, as torch's pin_memory
+ * allocates it) mapped for the current device at the same address: the
+ * kernels then read the kept blocks' tokens (and the summaries) through the
+ * host link and write the step's token there, with no host round trip.
+ * On CKNV_OK, *placement = CKNV_KV_ON_HOST if k and v are such host memory
+ * (0: device memory of the current device), plus CKNV_SUMMARIES_ON_HOST
+ * if kbar, dbar, cnt and vbar are. Host-only: HIP pointer queries, no
+ * enqueue.
+ * Errors: CKNV_EINVAL if a pointer is null, k and v (or the four summary
+ * arrays) are placed differently, an array is pageable host memory, device
+ * memory of another device, or host memory the device sees at another
+ * address, or seq_len is not device memory; CKNV_EHIP if the runtime
+ * cannot be queried (no device). */
+#define CKNV_KV_ON_HOST 0x1
+#define CKNV_SUMMARIES_ON_HOST 0x2
+int cknv_kv_placement(const cknv_shape* shape, const cknv_cache* cache, int32_t* placement);
 
 /* Full (dense) softmax attention over every cached token, the baseline the
  * page compares CompKV with ("Assumptions and limits"). Same q/out/lse

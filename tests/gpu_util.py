@@ -25,13 +25,16 @@ def oracle_variant(flags: int) -> dict:
                 mass_order=1 if flags & cknv.FLAG_FIRST_ORDER_MASS else 2)
 
 
-def upload(w: synth.Workload, data: dict, cap_blocks=None, max_blocks=None, flags=0):
+def upload(w: synth.Workload, data: dict, cap_blocks=None, max_blocks=None, flags=0,
+           kv_on_host=False, summaries_on_host=False):
     """LayerCache holding each sequence's prefill tokens (later slots zero),
-    seq_len = prefill, summaries built on the GPU."""
+    seq_len = prefill, summaries built on the GPU. kv_on_host /
+    summaries_on_host: the host-offload placement (pinned host memory)."""
     import torch
     cb = cap_blocks or w.cap_blocks
     shape = cknv.make_shape(w.S, w.H, w.G, w.d, w.r, cb, flags)
-    cache = cknv.LayerCache.allocate(shape)
+    cache = cknv.LayerCache.allocate(shape, kv_on_host=kv_on_host,
+                                     summaries_on_host=summaries_on_host)
     k = np.zeros((w.S, w.H, cb * 16, w.d), dtype=np.uint16)
     v = np.zeros_like(k)
     n = min(cb * 16, data["k"].shape[2])

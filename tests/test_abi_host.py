@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = cknv.lib()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
 
@@ -212,3 +212,24 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define CKNV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == cknv.NOALLOC_SCRATCH_BYTES
+
+
+def test_kv_placement_rejects_before_any_hip_call():
+    """cknv_kv_placement validates its arguments before querying the runtime."""
+    L = cknv.lib()
+    sh = shape()
+    out = ctypes.c_int32(-7)
+    assert L.cknv_kv_placement(ctypes.byref(sh), ctypes.byref(cache_struct()), None) == cknv.EINVAL
+    assert L.cknv_kv_placement(ctypes.byref(sh), ctypes.byref(cache_struct("vbar")),
+                               ctypes.byref(out)) == cknv.EINVAL
+    assert L.cknv_kv_placement(None, ctypes.byref(cache_struct()), ctypes.byref(out)) == cknv.EINVAL
+    assert L.cknv_kv_placement(ctypes.byref(shape(d=96)), ctypes.byref(cache_struct()),
+                               ctypes.byref(out)) == cknv.EUNSUPPORTED
+    assert out.value == -7
+
+
+def test_placement_bits_match_header():
+    text = open(HEADER).read()
+    for name in ("KV_ON_HOST", "SUMMARIES_ON_HOST"):
+        m = re.search(rf"#define CKNV_{name} (0x[0-9a-f]+)", text)
+        assert m and int(m.group(1), 16) == getattr(cknv, name)
