@@ -292,15 +292,14 @@ __device__ __forceinline__ void mean_var16(const float (&x)[16], int n, float& m
 // Workgroup -> (unit, part). With U a multiple of 8, all parts of a unit land
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin), so the
 // partials a unit's last workgroup merges stay in one L2.
+// (Both mappings are computed and one is selected: a branch here made the
+// compiler reload the kernel argument after it, one more memory round trip
+// before the first load of the workgroup.)
 __device__ __forceinline__ void map_wg(int L, int U, int parts, int xcd, int& unit, int& part) {
-  if (xcd) {
-    const int x = L & 7, y = L >> 3;
-    unit = x + 8 * (y / parts);
-    part = y % parts;
-  } else {
-    unit = L / parts;
-    part = L % parts;
-  }
+  const int x = L & 7, y = L >> 3;
+  const int yq = y / parts, lq = L / parts;
+  unit = xcd ? x + 8 * yq : lq;
+  part = xcd ? y - yq * parts : L - lq * parts;
 }
 
 #endif

@@ -256,7 +256,8 @@ template <int G, int DM, int ROWS, bool NC>
 constexpr int score_waves_per_simd() { return score_defers_vbar<G, DM, ROWS, NC>() && ROWS == 4 ? 5 : 1; }
 
 // NC: the no-compensation ablation; the mean values are neither read nor summed.
-template <int D, int G, int DM, int ROWS, bool NC>
+// ONE: a batch of one sequence (the loads do not wait for seq_len).
+template <int D, int G, int DM, int ROWS, bool NC, bool ONE>
 __global__ __launch_bounds__(kScoreThreads)
 __attribute__((amdgpu_waves_per_eu(score_waves_per_simd<G, DM, ROWS, NC>())))
 void score_kernel(ScoreArgs a) {
@@ -274,6 +275,10 @@ void score_kernel(ScoreArgs a) {
   __shared__ __align__(16) float4 q_s[G * D / 4];            // the G query heads
   __shared__ float e_s[G * kRowMaxR];                        // kDbarRow: group energies E[g][t]
 
+  // The scoring path's kernel arguments are read with the first batch: used
+  // only after the branch below, their loads would otherwise be issued (and
+  // waited for) there, one more round trip before the first summary load.
+  asm volatile("" ::"s"(a.NG), "s"(a.C), "s"(a.xcd), "s"(a.rows));
   if ((int)blockIdx.x < a.nfresh) {
     fresh_block<D, G>(a, blockIdx.x);
     return;
@@ -294,12 +299,9 @@ void score_kernel(ScoreArgs a) {
   // ---- every load of the workgroup, issued before any result is needed.
   // Block indices are clamped into [0, MB); blocks past the scored range are
   // masked once seq_len has arrived.
-  const int T = a.seq_len[s];
   // the query goes to LDS (registers are what limits resident waves here)
   static_assert(G * D / 4 <= kScoreThreads, "one float4 of q per thread");
   const float4 qown = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : 0];
-  int NB = a.closed_only ? T / kBlock : (T + kBlock - 1) / kBlock;
-  NB = NB < MB ? NB : MB;
   float4 kv[ROWS][KC], vv[ROWS][KC];
   DbarTile<DM, ROWS, KC> dt;
   float n;
@@ -328,11 +330,27 @@ void score_kernel(ScoreArgs a) {
     }
   };
   // One sequence: the addresses do not wait for seq_len (max_blocks bounds
-  // it). A batch of several: a chunk past its sequence's end reads one row
-  // again and again (cached) instead of max_blocks' worth of unused rows.
-  if (a.S == 1) issue_loads(MB - 1);
-  else issue_loads(NB > 0 ? NB - 1 : 0);
-  const int lim = a.S == 1 ? MB - 1 : (NB > 0 ? NB - 1 : 0);
+  // it), which is read after the loads are issued. A batch of several: a
+  // chunk past its sequence's end reads one row again and again (cached)
+  // instead of max_blocks' worth of unused rows. (Two kernel instances: a
+  // run-time branch between the two made the loads wait for seq_len.)
+  auto blocks_of = [&](int T) {
+    const int nb = a.closed_only ? T / kBlock : (T + kBlock - 1) / kBlock;
+    return nb < MB ? nb : MB;
+  };
+  int T, NB, lim;
+  if constexpr (ONE) {
+    issue_loads(MB - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    T = a.seq_len[s];
+    NB = blocks_of(T);
+    lim = MB - 1;
+  } else {
+    T = a.seq_len[s];
+    NB = blocks_of(T);
+    lim = NB > 0 ? NB - 1 : 0;
+    issue_loads(lim);
+  }
   // Keep the load block above: without this the scheduler sinks loads next
   // to their uses and the wave pays several dependent memory round trips.
   __builtin_amdgcn_sched_barrier(0);
@@ -544,11 +562,14 @@ hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st)
   const int dm = a.r <= kRowMaxR ? kDbarRow : gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
   const void* f = nullptr;
   const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
+  const bool one = a.S == 1;
+#define CKNV_SCORE_ONE(DD, GG, RR, NC, ONE)                                       \
+  f = dm == kDbarRow ? (const void*)score_kernel<DD, GG, kDbarRow, RR, NC, ONE>   \
+    : dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR, NC, ONE>   \
+    : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair, RR, NC, ONE> \
+                      : (const void*)score_kernel<DD, GG, kDbarQuad, RR, NC, ONE>;
 #define CKNV_SCORE_NC(DD, GG, RR, NC)                                             \
-  f = dm == kDbarRow ? (const void*)score_kernel<DD, GG, kDbarRow, RR, NC>        \
-    : dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR, NC>        \
-    : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair, RR, NC>      \
-                      : (const void*)score_kernel<DD, GG, kDbarQuad, RR, NC>;
+  if (one) { CKNV_SCORE_ONE(DD, GG, RR, NC, true) } else { CKNV_SCORE_ONE(DD, GG, RR, NC, false) }
 #define CKNV_SCORE_R(DD, GG, RR)                                                  \
   if (d == DD && G == GG && a.rows == RR) {                                       \
     if (nc) { CKNV_SCORE_NC(DD, GG, RR, true) } else { CKNV_SCORE_NC(DD, GG, RR, false) } \
@@ -559,6 +580,7 @@ hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st)
 #undef CKNV_SCORE_CASE
 #undef CKNV_SCORE_R
 #undef CKNV_SCORE_NC
+#undef CKNV_SCORE_ONE
   if (!f) return hipErrorInvalidValue;
   return hipLaunchKernel(f, dim3(a.nfresh + U * a.C), dim3(kScoreThreads), args, 0, st);
 }

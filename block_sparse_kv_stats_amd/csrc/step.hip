@@ -178,6 +178,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   float* recs = areaA;                   // [NW][G][W] after the selection
 
   const int P = a.P;
+  // The input loads' kernel arguments are read with the first batch (left to
+  // the compiler, they came in a second round trip after the part mapping).
+  // (Not for 8 query heads at the largest bucket: their registers are full.)
+  if constexpr (G < 8 || KPTB < 24) asm volatile("" ::"s"(a.t0), "s"(a.u), "s"(a.hdr), "s"(a.finfo));
   // the parts of a unit run on the XCD whose L2 the scoring pass wrote that
   // unit's workspace through
   int unit, p;
