@@ -509,7 +509,7 @@ def run_workload(torch, timer, wname, args, stream, full=True, kv_on_host=False)
 # ---------------------------------------------------------------- profiles
 PROFILE_COMMANDS = {
     "trace": 'rocprofv3 --kernel-trace --stats -f csv -d $OUT/trace -o trace -- '
-             'python3 bench.py --no-cpu --no-dense --no-host-offload --also ""',
+             'python3 bench.py --steps 64 --warmup 8 --no-cpu --no-host-offload --also qwen8b_128k',
     "fetch": 'rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/fetch -o fetch -- '
              'python3 bench.py --steps 8 --warmup 2 --no-cpu --no-dense --no-host-offload --also ""',
     "write": 'rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/write -o write -- '
@@ -525,7 +525,7 @@ PROFILE_COMMANDS = {
     "summary": 'python3 bench.py --summarize-profiles $OUT',
 }
 COPY_PROBE_BYTES = 268435456
-TRACE_SUMMARY = "kernels_llama8b_32k_trace.md"
+TRACE_SUMMARY = "kernels_llama8b_32k_qwen8b_128k_trace.md"
 
 
 def copy_probe(nbytes: int, reps: int):
@@ -578,7 +578,11 @@ def summarize_profiles(out_dir):
         key = (name.split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]))
         stats.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     if stats:
-        lines = ["# Kernel durations, bench.py default workload (Llama-3.1-8B layer, 32K, budget 512)", "",
+        lines = ["# Kernel durations: Llama-3.1-8B layer at 32K (budget 512) and Qwen3-8B layer at "
+                 "128K (budget 2048)", "",
+                 "The fused step (score_kernel + step_kernel), the three-call path (append_kernel, "
+                 "score_kernel, select_kernel, attend_kernel, merge_kernel), the dense baseline "
+                 "(dense_kernel + merge_kernel) and the bulk build (build_kernel), as bench.py runs them.", "",
                  "Command (from the repository root, OUT = an output directory):", "",
                  "    " + PROFILE_COMMANDS["trace"], "    " + PROFILE_COMMANDS["summary"], "",
                  "rocprofv3 kernel trace of every dispatch of the run (graph replays included),",
