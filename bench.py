@@ -56,10 +56,16 @@ def log(msg):
 
 
 def kernel_source_hash(paths) -> str:
+    """Hash of a kernel's sources with comments and blank space removed, so
+    that a profile stays valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -545,6 +545,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   // stores; once every thread's stores are complete, one thread counts the
   // part in. The part that completes the count merges all P records, read
   // with agent-scope loads, into out and lse. No workgroup waits on another.
+  // The ordering rests on the gfx950 instructions, not on a fence of the
+  // memory model: the record stores carry sc1 (written through to the level
+  // every XCD sees), s_waitcnt vmcnt(0) and the barrier complete them before
+  // the relaxed counter add, and the merging part's loads carry sc1. A test
+  // reads the built assembly of every instance for exactly that order.
   float* mine = a.part + ((size_t)unit * P + p) * G * W;
   merge_records<D, G, NT, true>(recs, NW, mine, scl);
   __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
