@@ -133,15 +133,22 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   // unit's waves read one contiguous stretch of the cache, spread over every
   // memory channel, rather than P far-apart streams in lockstep.
   const int stride = a.P * NWV;
-  // NBUF tiles per wave in flight: the loads of the wave's tile j + NBUF-1
-  // are issued before its tile j is absorbed (eight query heads leave room
-  // for one). The first tiles' loads go out before the query is staged.
-  constexpr int NBUF = G >= 8 ? 1 : kDenseTilesInFlight;
-  int b = p * NWV + wave;
-  TileM<D> t[NBUF];
-#pragma unroll
-  for (int i = 0; i + 1 < NBUF; ++i)
-    if (b + i * stride < NB) load_tile_whole<D>(t[i], kc, vc, (long)(b + i * stride) * kBlock, T, lane);
+  // This wave's tiles are blocks b0, b0 + stride, ... below NB (n_w of
+  // them). Up to 4 query heads the wave keeps two tiles in flight: tile j+1's
+  // loads are issued before tile j is absorbed. The loop body is straight
+  // line and every load unconditional, so each wait counts only the older
+  // tile's loads; past the wave's last tile a slot is empty (no valid
+  // token, its loads re-read the last tile from the cache). The first tile's
+  // loads go out before the query is staged.
+  const int b0 = p * NWV + wave;
+  const int n_w = b0 < NB ? (NB - 1 - b0) / stride + 1 : 0;
+  const int blast = n_w > 0 ? b0 + (n_w - 1) * stride : 0;
+  auto tile_at = [&](TileM<D>& t, int j) {
+    const bool in = j < n_w;
+    load_tile_whole<D>(t, kc, vc, (long)(in ? b0 + j * stride : blast) * kBlock, in ? T : 0, lane);
+  };
+  TileM<D> t0;
+  tile_at(t0, 0);
   if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
   lds_barrier();
   WaveState<D, G> st;
@@ -154,15 +161,26 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   QMfma<D> qm;
   qm.template build<G>(q_l, lane);
   float* pw = pbuf + wave * 16 * G;
-  for (; b < NB; b += NBUF * stride) {
-#pragma unroll
-    for (int i = 0; i < NBUF; ++i) {
-      const int bi = b + i * stride;
-      if (bi >= NB) break;
-      const int bn = bi + (NBUF - 1) * stride;
-      if (bn < NB) load_tile_whole<D>(t[(i + NBUF - 1) % NBUF], kc, vc, (long)bn * kBlock, T, lane);
-      __builtin_amdgcn_sched_barrier(0);  // the later tiles' loads issued before this one is used
-      absorb_mfma<D, G, false>(st, t[i], none, qm, q_l, pw, lane, a.isd);
+  if constexpr (G >= 8) {
+    // eight query heads: one tile at a time (a second does not fit the registers)
+    for (int j = 0; j < n_w; ++j) {
+      if (j > 0) tile_at(t0, j);
+      __builtin_amdgcn_sched_barrier(0);
+      absorb_mfma<D, G, false>(st, t0, none, qm, q_l, pw, lane, a.isd);
+    }
+  } else {
+    TileM<D> t1;
+    // (the barriers keep each tile's last use ahead of its reload, so that the
+    // reload lands in the same registers: a copy would wait for the loads)
+    for (int j = 0; j < n_w; j += 2) {
+      tile_at(t1, j + 1);
+      __builtin_amdgcn_sched_barrier(0);  // the next tile's loads issued before this one is used
+      absorb_mfma<D, G, false>(st, t0, none, qm, q_l, pw, lane, a.isd);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_at(t0, j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      absorb_mfma<D, G, false>(st, t1, none, qm, q_l, pw, lane, a.isd);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
