@@ -27,8 +27,8 @@
 //   loads      T0, finfo, the chunk headers, the thread's score groups and
 //              u terms, the query, and (waves AW..NW-1) their first chunk
 //              records;
-//   LSE        every wave reduces the chunk headers and the fresh block's a
-//              itself (the same bits in every wave); factors
+//   LSE        wave g reduces query head g's chunk headers and the fresh
+//              block's a to LSE_g, shared through LDS; factors
 //              e^{group max - LSE} of the thread's score groups to LDS;
 //   keys       S_b per block (fp32 bits order like the values, S_b >= 0);
 //              scores; 2048-bin histogram of the candidates' top 11 bits;
@@ -172,6 +172,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   __shared__ int cnt[KPT * NW + 1];
   __shared__ float scl[NW * G + 2 * G];
   __shared__ int ctl[8];
+  __shared__ float lse_s[G];  // the normalisers LSE_g
   __shared__ int klist[KPART];
   __shared__ __align__(16) float pbuf[AW * 16 * G];  // attending waves' tile probabilities
   float* fgrp = areaA;                   // [NGMAX][G] exp(group max - LSE_g)
@@ -271,22 +272,38 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   if (tid == 0) ctl[3] = 0;
 
   // ================================================================ LSE
-  float lse_g[G], fa[G];
+  // Wave g < G reduces query head g's chunk headers and the fresh block's a
+  // to LSE_g (one reduction chain per wave: every wave doing all G of them
+  // made the phase bound by the SIMDs' shared VALU); the normalisers reach
+  // every wave through LDS.
+  float fa[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) fa[g] = fb >= 0 ? fi[g].x : -INFINITY;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float r = -INFINITY;
+    if (wave == g) {  // wave-uniform
+      float r = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) r = fmaxf(r, lane + 64 * k < NC ? hd[k][g].x : -INFINITY);
-    const float Mw = group_max<64>(r);
-    float l = 0.f;
+      for (int k = 0; k < CPL; ++k) r = fmaxf(r, lane + 64 * k < NC ? hd[k][g].x : -INFINITY);
+      const float Mw = group_max<64>(r);
+      float l = 0.f;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) l += lane + 64 * k < NC ? hd[k][g].y * rescale(hd[k][g].x, Mw) : 0.f;
-    const float Lw = group_sum<64>(l);
-    fa[g] = fb >= 0 ? fi[g].x : -INFINITY;
-    const float M = fmaxf(Mw, fa[g]);
-    const float L = Lw * rescale(Mw, M) + rescale(fa[g], M);
-    lse_g[g] = L > 0.f ? M + __logf(L) : INFINITY;
+      for (int k = 0; k < CPL; ++k) l += lane + 64 * k < NC ? hd[k][g].y * rescale(hd[k][g].x, Mw) : 0.f;
+      const float Lw = group_sum<64>(l);
+      const float M = fmaxf(Mw, fa[g]);
+      const float L = Lw * rescale(Mw, M) + rescale(fa[g], M);
+      if (lane == 0) lse_s[g] = L > 0.f ? M + __logf(L) : INFINITY;
+    }
   }
+#pragma unroll
+  for (int k = 0; k < NQ4; ++k) {
+    const int i = tid + k * NT;
+    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
+  }
+  lds_barrier();
+  float lse_g[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) lse_g[g] = lse_s[g];
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
     const int gi = tid + k * NT;
@@ -294,11 +311,6 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
       for (int g = 0; g < G; ++g) fgrp[gi * G + g] = __expf(gp[k][g].x - lse_g[g]);
     }
-  }
-#pragma unroll
-  for (int k = 0; k < NQ4; ++k) {
-    const int i = tid + k * NT;
-    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
   }
   WaveState<D, G> st;
   st.init();
