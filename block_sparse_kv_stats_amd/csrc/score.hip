@@ -348,7 +348,19 @@ void score_kernel(ScoreArgs a) {
   } else {
     T = a.seq_len[s];
     NB = blocks_of(T);
-    lim = NB > 0 ? NB - 1 : 0;
+    if (chunk * BPWG >= NB) {
+      // The whole chunk lies past this sequence's end (a shorter sequence of
+      // the batch): an empty header and an empty compensation record, no
+      // loads. Its groups and u terms are never read.
+      if (tid < G)
+        reinterpret_cast<float2*>(a.hdr)[((size_t)unit * a.C + chunk) * G + tid] = make_float2(-INFINITY, 0.f);
+      if constexpr (!NC) {
+        float* co = a.comp + ((size_t)unit * a.C + chunk) * G * W;
+        for (int i = tid; i < G * W; i += kScoreThreads) co[i] = i % W == 0 ? -INFINITY : 0.f;
+      }
+      return;
+    }
+    lim = NB - 1;
     issue_loads(lim);
   }
   // Keep the load block above: without this the scheduler sinks loads next
