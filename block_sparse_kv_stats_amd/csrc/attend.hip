@@ -102,6 +102,154 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   merge_records<D, G>(recs, kWaves + nrec, po, scl);
 }
 
+namespace {
+
+// The dense kernel's tiles: the keys as the logits MFMA reads them (lane l,
+// token l%16), the values in 16-byte pieces: load i, lane l holds token
+// 4i + l/16, coordinates VP*(l%16) .. +VP-1 (VP = d/16), so a tile's values
+// take 4 loads per lane (a bandwidth-bound stream is bound by its load
+// instructions as well as its bytes). Token rows past the last valid one
+// read that one (their probabilities are 0).
+template <int D>
+struct TileW {
+  static constexpr int NI = D / 32, VP = D / 16, VW = VP / 2;
+  u32x4_t k[NI];
+  uint32_t v[4][VW];
+  int nt;  // valid tokens
+  __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
+    const long left = T - tok0;
+    nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+    const int last = nt > 0 ? nt - 1 : 0;
+    const int t = lane & 15, c = lane >> 4;
+    const uint16_t* ks = kc + (size_t)(tok0 + (t < last ? t : last)) * D + (D / 4) * c;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) k[i] = ldg<true>(reinterpret_cast<const u32x4_t*>(ks + 8 * i));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + c;
+      const uint16_t* vs = vc + (size_t)(tok0 + (row < last ? row : last)) * D + VP * t;
+      if constexpr (VW == 4) {
+        const uint4 x = stream_load_u4<true>(vs);
+        v[i][0] = x.x; v[i][1 % VW] = x.y; v[i][2 % VW] = x.z; v[i][3 % VW] = x.w;
+      } else {
+        const uint2 x = stream_load_u2<true>(vs);
+        v[i][0] = x.x; v[i][1 % VW] = x.y;
+      }
+    }
+  }
+};
+
+// Running state of a dense wave: per query head the max m and normaliser l
+// (wave-uniform) and the value sums of the lane's VP coordinates over the
+// tokens 4i + l/16 it has seen (summed over the four lane groups at the end).
+template <int D, int G>
+struct WaveStateW {
+  static constexpr int VP = D / 16;
+  float m[G], l[G], acc[G][VP];
+  __device__ void init() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VP; ++e) acc[g][e] = 0.f;
+    }
+  }
+};
+
+// Add one tile's exact terms (logits on MFMA, probabilities through the
+// wave's LDS scratch `pw` of 16*G floats). A tile with no valid token adds
+// nothing.
+template <int D, int G>
+__device__ __forceinline__ void absorb_w(WaveStateW<D, G>& st, const TileW<D>& t, const QMfma<D>& qm,
+                                         float* pw, int lane, float isd) {
+  constexpr int NI = D / 32, VP = D / 16, VW = VP / 2;
+  const int j = lane & 15, c = lane >> 4;
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, t.k[i]);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qm.hi[i], s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qm.lo[i], s, 0, 0, 0);
+  }
+  float z[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = 4 * c + e < t.nt ? s[e] * isd : -INFINITY;
+  const float cmax = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));  // head j's tile max
+  float M[G], sc[G];
+  float Mj = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    M[g] = fmaxf(st.m[g], lane_value(cmax, g));
+    sc[g] = rescale(st.m[g], M[g]);
+    Mj = j == g ? M[g] : Mj;
+  }
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = z[e] == -INFINITY ? 0.f : __expf(z[e] - Mj);
+  const float ps = rows_sum((p[0] + p[1]) + (p[2] + p[3]));
+  if (j < G) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pw[(4 * c + e) * G + j] = p[e];
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.l[g] = st.l[g] * sc[g] + lane_value(ps, g);
+    st.m[g] = M[g];
+#pragma unroll
+    for (int e = 0; e < VP; ++e) st.acc[g][e] *= sc[g];
+  }
+  // lanes read the probabilities other lanes of the wave just wrote: the
+  // fence keeps the reads after the writes (the wave's LDS operations then
+  // run in program order)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (t.nt > 0) {  // wave-uniform; an empty tile's rows may hold anything
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float pv[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) pv[g] = pw[(4 * i + c) * G + g];
+#pragma unroll
+      for (int w = 0; w < VW; ++w) {
+        const float lo = bf16_lo(t.v[i][w]), hi = bf16_hi(t.v[i][w]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          st.acc[g][2 * w] += pv[g] * lo;
+          st.acc[g][2 * w + 1] += pv[g] * hi;
+        }
+      }
+    }
+  }
+  // the next tile's probability writes must not pass these reads
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// Write a WaveStateW's record [m, l, 0, 0, acc[D]] per g (value sums summed
+// over the four lane groups).
+template <int D, int G>
+__device__ __forceinline__ void store_wave_record_w(const WaveStateW<D, G>& st, float* rec, int lane) {
+  constexpr int VP = D / 16, W = rec_words(D);
+  const int t = lane & 15, c = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < VP; ++e) {
+      const float x = rows_sum(st.acc[g][e]);
+      if (c == 0) rec[g * W + 4 + VP * t + e] = x;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      rec[g * W] = st.m[g];
+      rec[g * W + 1] = st.l[g];
+      rec[g * W + 2] = 0.f;
+      rec[g * W + 3] = 0.f;
+    }
+  }
+}
+
+}  // namespace
+
 // Full attention, every block exact, no compensation: P workgroups of
 // kDenseThreads threads per unit, the unit's blocks dealt round-robin over
 // all their waves, each wave keeping several tiles of non-temporal loads in
@@ -143,21 +291,16 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   const int b0 = p * NWV + wave;
   const int n_w = b0 < NB ? (NB - 1 - b0) / stride + 1 : 0;
   const int blast = n_w > 0 ? b0 + (n_w - 1) * stride : 0;
-  auto tile_at = [&](TileM<D>& t, int j) {
+  auto tile_at = [&](TileW<D>& t, int j) {
     const bool in = j < n_w;
-    load_tile_whole<D>(t, kc, vc, (long)(in ? b0 + j * stride : blast) * kBlock, in ? T : 0, lane);
+    t.load(kc, vc, (long)(in ? b0 + j * stride : blast) * kBlock, in ? T : 0, lane);
   };
-  TileM<D> t0;
+  TileW<D> t0;
   tile_at(t0, 0);
   if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
   lds_barrier();
-  WaveState<D, G> st;
+  WaveStateW<D, G> st;
   st.init();
-  BlockMean<D> none;
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) none.kb[e] = none.vb[e] = 0.f;
-  none.n = 0.f;
-  none.on = false;
   QMfma<D> qm;
   qm.template build<G>(q_l, lane);
   float* pw = pbuf + wave * 16 * G;
@@ -166,24 +309,24 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
     for (int j = 0; j < n_w; ++j) {
       if (j > 0) tile_at(t0, j);
       __builtin_amdgcn_sched_barrier(0);
-      absorb_mfma<D, G, false>(st, t0, none, qm, q_l, pw, lane, a.isd);
+      absorb_w<D, G>(st, t0, qm, pw, lane, a.isd);
     }
   } else {
-    TileM<D> t1;
+    TileW<D> t1;
     // (the barriers keep each tile's last use ahead of its reload, so that the
     // reload lands in the same registers: a copy would wait for the loads)
     for (int j = 0; j < n_w; j += 2) {
       tile_at(t1, j + 1);
       __builtin_amdgcn_sched_barrier(0);  // the next tile's loads issued before this one is used
-      absorb_mfma<D, G, false>(st, t0, none, qm, q_l, pw, lane, a.isd);
+      absorb_w<D, G>(st, t0, qm, pw, lane, a.isd);
       __builtin_amdgcn_sched_barrier(0);
       tile_at(t0, j + 2);
       __builtin_amdgcn_sched_barrier(0);
-      absorb_mfma<D, G, false>(st, t1, none, qm, q_l, pw, lane, a.isd);
+      absorb_w<D, G>(st, t1, qm, pw, lane, a.isd);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  store_wave_record<D, G>(st, recs + wave * G * W, lane);
+  store_wave_record_w<D, G>(st, recs + wave * G * W, lane);
   lds_barrier();
   merge_records<D, G, kDenseThreads>(recs, NWV, a.part + ((size_t)unit * a.P + p) * G * W, scl);
 }

@@ -208,27 +208,6 @@ struct TileM {
   }
 };
 
-// A TileM of block tok0/16 read whole (all 16 token slots; the block must lie
-// inside the cache's capacity): the addresses are one base plus fixed
-// offsets; slots at or past T are masked at use. Non-temporal (a streaming
-// pass).
-template <int D>
-__device__ __forceinline__ void load_tile_whole(TileM<D>& t, const uint16_t* kc, const uint16_t* vc,
-                                                long tok0, long T, int lane) {
-  constexpr int NI = D / 32, VPL = D / 64;
-  const long left = T - tok0;
-  t.nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
-  const int tk = lane & 15, c = lane >> 4;
-  const uint16_t* ks = kc + (size_t)(tok0 + tk) * D + (D / 4) * c;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) t.k[i] = ldg<true>(reinterpret_cast<const u32x4_t*>(ks + 8 * i));
-  const uint16_t* vs = vc + (size_t)tok0 * D + lane * VPL;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    t.v[j] = VPL == 2 ? stream_load_u1<true>(vs + j * D) : stream_load_h<true>(vs + j * D);  // masked at use
-  }
-}
-
 // The query heads as MFMA B operands (head l%16 < G, zero columns after).
 template <int D>
 struct QMfma {
@@ -312,9 +291,12 @@ __device__ __forceinline__ void absorb_mfma(WaveState<D, G>& st, const TileM<D>&
 #pragma unroll
     for (int e = 0; e < VPL; ++e) st.acc[g][e] *= sc[g];
   }
-  // the wave reads back its own LDS writes (LDS operations of a wave run in
-  // order), four tokens at a time: LDS reads do not move across the groups,
-  // so at most 4*G probabilities are held at once
+  // The wave reads back what its lanes just wrote (the fence keeps the
+  // compiler from moving the reads ahead of the writes; the wave's LDS
+  // operations then run in program order), four tokens at a time: LDS reads
+  // do not move across the groups, so at most 4*G probabilities are held at
+  // once.
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
   for (int t4 = 0; t4 < 16; t4 += 4) {
     if (t4 > 0) __builtin_amdgcn_sched_barrier(0x7F);  // ALU and global memory may cross, LDS may not
@@ -333,6 +315,8 @@ __device__ __forceinline__ void absorb_mfma(WaveState<D, G>& st, const TileM<D>&
       }
     }
   }
+  // the next tile's probability writes must not pass these reads
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   if constexpr (COMP) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
