@@ -189,6 +189,20 @@ static int decode_score_impl(const Plan& p, const cknv_shape* shape, const cknv_
   return hip_status(launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream));
 }
 
+// Where a pointer lies for device dev: 0 its device memory, 1 pinned host
+// memory it maps at the same address, -1 anything else (pageable host memory
+// included; the error the runtime records for it is cleared).
+static int mem_where(const void* ptr, int dev) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  if (at.type == hipMemoryTypeDevice) return at.device == dev ? 0 : -1;
+  if (at.type == hipMemoryTypeHost) return at.devicePointer == ptr ? 1 : -1;
+  return -1;
+}
+
 static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv_cache* cache,
                               const float* q, int32_t max_blocks, float* scores, int32_t* sel,
                               int32_t* n_sel, float* out, float* lse, char* w, void* stream) {
@@ -378,18 +392,7 @@ int cknv_kv_placement(const cknv_shape* shape, const cknv_cache* cache, int32_t*
     (void)hipGetLastError();
     return CKNV_EHIP;
   }
-  // 0: device memory of this device, 1: pinned host memory this device maps
-  // at the same address, -1: anything else
-  auto where = [dev](const void* ptr) {
-    hipPointerAttribute_t at{};
-    if (hipPointerGetAttributes(&at, ptr) != hipSuccess) {
-      (void)hipGetLastError();  // unknown to the runtime: pageable host memory
-      return -1;
-    }
-    if (at.type == hipMemoryTypeDevice) return at.device == dev ? 0 : -1;
-    if (at.type == hipMemoryTypeHost) return at.devicePointer == ptr ? 1 : -1;
-    return -1;
-  };
+  auto where = [dev](const void* ptr) { return mem_where(ptr, dev); };
   const int k = where(cache->k), v = where(cache->v);
   if (k < 0 || k != v) return CKNV_EINVAL;
   const int sm = where(cache->kbar);

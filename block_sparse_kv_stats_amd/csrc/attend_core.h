@@ -71,7 +71,7 @@ template <int D>
 struct BlockMean {
   static constexpr int VPL = D / 64;
   float kb[VPL], vb[VPL], n;
-  bool on;  // false: the block removes no compensation (n is then not used)
+  float on;  // 1: the block removes its compensation, 0: it removes none
   __device__ void load(const float* kbar_row, const float* vbar_row, const float* cnt, int lane) {
 #pragma unroll
     for (int e = 0; e < VPL; ++e) {
@@ -79,11 +79,13 @@ struct BlockMean {
       vb[e] = vbar_row[lane * VPL + e];
     }
     n = *cnt;
-    on = true;
+    on = 1.f;
   }
-  // n, or 0 where the block removes nothing (taken at use, so that setting
-  // `on` does not wait for the load of n)
-  __device__ __forceinline__ float mass() const { return on ? n : 0.f; }
+  // n, or 0 where the block removes nothing: a product, not a select, so
+  // that the load of n stays unconditional and is waited for at use (a
+  // select lets the compiler move the load under the condition and wait for
+  // it, and everything issued before it, right there)
+  __device__ __forceinline__ float mass() const { return n * on; }
 };
 
 // p of token 4*m + R (held by the lanes of row R) for R = 0..3, in every lane.
@@ -190,21 +192,24 @@ struct TileM {
   u32x4_t k[NI];   // keys, MFMA A layout
   uint32_t v[16];  // values: lane's VPL coordinates of every token (as Tile)
   int nt;          // valid tokens
-  // NT: non-temporal loads (a streaming pass) or plain ones (a latency-bound gather)
+  // NT: non-temporal loads (a streaming pass) or plain ones (a latency-bound gather).
+  // All 16 token rows of the block are read (they lie inside the cache, the
+  // block being below its capacity); rows at or past T hold anything and are
+  // masked at use. One base address per lane then serves every load (the
+  // rows are immediate offsets), which keeps two tiles' addresses out of the
+  // registers.
   template <bool NT = false>
   __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
     const long left = T - tok0;
     nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
-    const int last = nt > 0 ? nt - 1 : 0;  // loads read token min(t, last), values masked at use
     const int t = lane & 15, c = lane >> 4;
-    const uint16_t* ks = kc + (size_t)(tok0 + (t < last ? t : last)) * D + (D / 4) * c;
+    const uint16_t* ks = kc + (size_t)(tok0 + t) * D + (D / 4) * c;
 #pragma unroll
     for (int i = 0; i < NI; ++i) k[i] = ldg<NT>(reinterpret_cast<const u32x4_t*>(ks + 8 * i));
+    const uint16_t* vs = vc + (size_t)tok0 * D + lane * VPL;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint16_t* src = vc + (size_t)(tok0 + (j < last ? j : last)) * D + lane * VPL;
-      v[j] = VPL == 2 ? stream_load_u1<NT>(src) : stream_load_h<NT>(src);  // masked at use
-    }
+    for (int j = 0; j < 16; ++j)
+      v[j] = VPL == 2 ? stream_load_u1<NT>(vs + j * D) : stream_load_h<NT>(vs + j * D);  // masked at use
   }
 };
 

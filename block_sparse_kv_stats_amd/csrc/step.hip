@@ -483,51 +483,64 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   lds_barrier();
 
   // ================================================================ attend
-  // Wave w < AW: kept blocks lo + w + AW*i (i < kpw) of this part's slice
+  // Wave w < AW: kept blocks lo + w + AW*i (i < n_w) of this part's slice
   // (exact terms, minus their compensation where the scoring pass counted
-  // them), up to 4 query heads one tile ahead: the next tile's loads are
-  // issued before the current one is absorbed.
+  // them). Up to 4 query heads the wave keeps two tiles in flight: tile i+1's
+  // loads are issued before tile i is absorbed. That loop is straight line
+  // with unconditional loads (a slot past the wave's last block is empty: no
+  // valid token, n = 0), so each wait counts only the older tile's loads and
+  // each reload lands in the registers the loop expects; only the arithmetic
+  // of an empty second tile is skipped. A block's means and count are
+  // loaded ahead of its tokens: z̄ needs them first.
   if (wave < AW) {
-    const int kpw = a.kpw;
+    const int left = nk - lo - wave;  // kept blocks at or past this wave's first slot
+    const int n_w = left <= 0 ? 0 : ((left + AW - 1) / AW < a.kpw ? (left + AW - 1) / AW : a.kpw);
     auto load_block = [&](TileM<D>& t, BlockMean<D>& m, int i) {
-      const int e = wave + AW * i;
-      const int bk = lo + e < nk ? klist[e] : -1;
+      const int bk = i < n_w ? klist[wave + AW * i] : -1;
       const int b = bk >= 0 ? bk : 0;
-      // an empty slot (bk < 0) holds no valid token and n = 0: it adds nothing
-      t.load(kc, vc, (long)b * kBlock, bk >= 0 ? (long)T : 0, lane);
       m.load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
+      // an empty slot (bk < 0) holds no valid token and removes nothing
+      t.load(kc, vc, (long)b * kBlock, bk >= 0 ? (long)T : 0, lane);
       // one code path: a block whose compensation the scoring pass did not
       // count removes a zero-mass term
-      m.on = bk >= 0 && bk < NBa && !nc;
+      m.on = bk >= 0 && bk < NBa && !nc ? 1.f : 0.f;
     };
     TileM<D> t0;
     BlockMean<D> m0;
     load_block(t0, m0, 0);
     QMfma<D> qm;
     qm.template build<G>(q_l, lane);
+    float* pw = pbuf + wave * 16 * G;
     if constexpr (G <= 4) {
-      TileM<D> t1;
-      BlockMean<D> m1;
-      for (int i = 0; i < kpw; i += 2) {
-        const bool more = i + 1 < kpw;
-        if (more) load_block(t1, m1, i + 1);
-        __builtin_amdgcn_sched_barrier(0);  // the next tile's loads issued before this one is used
-        absorb_mfma<D, G>(st, t0, m0, qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
-        if (!more) break;
-        if (i + 2 < kpw) load_block(t0, m0, i + 2);
+      if (n_w == 1) {
         __builtin_amdgcn_sched_barrier(0);
-        absorb_mfma<D, G>(st, t1, m1, qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
+        absorb_mfma<D, G>(st, t0, m0, qm, q_l, pw, lane, a.isd);
+      } else if (n_w > 1) {
+        TileM<D> t1;
+        BlockMean<D> m1;
+        // (the barriers keep each tile's last use ahead of its reload)
+        for (int i = 0; i < n_w; i += 2) {
+          load_block(t1, m1, i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          absorb_mfma<D, G>(st, t0, m0, qm, q_l, pw, lane, a.isd);
+          __builtin_amdgcn_sched_barrier(0);
+          load_block(t0, m0, i + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i + 1 < n_w) absorb_mfma<D, G>(st, t1, m1, qm, q_l, pw, lane, a.isd);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     } else {
       // 8 query heads: one tile at a time (a second would not fit the registers)
-      for (int i = 0; i < kpw; ++i) {
+      for (int i = 0; i < n_w; ++i) {
         if (i > 0) load_block(t0, m0, i);
         __builtin_amdgcn_sched_barrier(0);
-        absorb_mfma<D, G>(st, t0, m0, qm, q_l, pbuf + wave * 16 * G, lane, a.isd);
+        absorb_mfma<D, G>(st, t0, m0, qm, q_l, pw, lane, a.isd);
       }
     }
-  }
-  if (rw >= 0 && !nc) {
+  } else if (!nc) {
+    // (an else branch: the records loaded with the inputs are dead in the
+    // attending waves, whose tiles reuse their registers)
 #pragma unroll
     for (int i = 0; i < RPF; ++i)
       if (c0 + rw + RW * i < c1) fold_record<D, G>(st, rf[i]);  // wave-uniform
