@@ -259,7 +259,6 @@ template <int D, int G>
 __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   constexpr int W = rec_words(D);
   constexpr int NWV = kDenseThreads / 64;
-  __shared__ __align__(16) float q_l[G * D];
   __shared__ __align__(16) float recs[NWV * G * W];
   __shared__ float scl[NWV * G + 3 * G];
   __shared__ __align__(16) float pbuf[NWV * 16 * G];
@@ -268,8 +267,6 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
   const int s = unit / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  static_assert(G * D / 4 <= kDenseThreads, "one float4 of q per thread");
-  const float4 qv = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : G * D / 4 - 1];
   const int T = a.seq_len[s];
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < a.max_blocks ? NB : a.max_blocks;
@@ -286,8 +283,8 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   // loads are issued before tile j is absorbed. The loop body is straight
   // line and every load unconditional, so each wait counts only the older
   // tile's loads; past the wave's last tile a slot is empty (no valid
-  // token, its loads re-read the last tile from the cache). The first tile's
-  // loads go out before the query is staged.
+  // token, its loads re-read the last tile from the cache). The query's
+  // MFMA operand is read before the first tile, from global memory.
   const int b0 = p * NWV + wave;
   const int n_w = b0 < NB ? (NB - 1 - b0) / stride + 1 : 0;
   const int blast = n_w > 0 ? b0 + (n_w - 1) * stride : 0;
@@ -295,14 +292,13 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
     const bool in = j < n_w;
     t.load(kc, vc, (long)(in ? b0 + j * stride : blast) * kBlock, in ? T : 0, lane);
   };
+  const typename QMfma<D>::Raw qr = QMfma<D>::template fetch<G>(a.q + (size_t)unit * G * D, lane);
   TileW<D> t0;
   tile_at(t0, 0);
-  if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
-  lds_barrier();
   WaveStateW<D, G> st;
   st.init();
   QMfma<D> qm;
-  qm.template build<G>(q_l, lane);
+  qm.template build_from<G>(qr, lane);
   float* pw = pbuf + wave * 16 * G;
   if constexpr (G >= 8) {
     // eight query heads: one tile at a time (a second does not fit the registers)

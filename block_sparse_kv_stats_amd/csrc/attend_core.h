@@ -214,18 +214,42 @@ struct TileM {
 };
 
 // The query heads as MFMA B operands (head l%16 < G, zero columns after).
+// Lane l needs q of head l%16 at coordinates (D/4)*(l/16) + 8i + e: 32
+// consecutive floats, read straight from global memory (the query is a few
+// KB and cached). Read from the LDS instead, the 16 heads' rows are D floats
+// apart and every such read falls on one bank (a 64-way conflict per
+// instruction, about 1.5 us per wave). fetch issues the loads; build_from
+// converts once they have arrived, so a caller can put other loads between.
 template <int D>
 struct QMfma {
   static constexpr int NI = D / 32;
   bf16x8_t hi[NI], lo[NI];
+  struct Raw {
+    float4 x[NI][2];
+  };
+  // q: the unit's G heads, [G][D] floats, 16-byte aligned
   template <int G>
-  __device__ void build(const float* q_l, int lane) {
+  __device__ static Raw fetch(const float* q, int lane) {
     const int j = lane & 15, c = lane >> 4;
+    const float4* src = reinterpret_cast<const float4*>(q + (size_t)(j < G ? j : 0) * D + (D / 4) * c);
+    Raw r;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      r.x[i][0] = src[2 * i];
+      r.x[i][1] = src[2 * i + 1];
+    }
+    return r;
+  }
+  template <int G>
+  __device__ void build_from(const Raw& r, int lane) {
+    const float keep = (lane & 15) < G ? 1.f : 0.f;  // columns past the G heads are zero
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float v[8] = {r.x[i][0].x, r.x[i][0].y, r.x[i][0].z, r.x[i][0].w,
+                          r.x[i][1].x, r.x[i][1].y, r.x[i][1].z, r.x[i][1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = j < G ? q_l[j * D + (D / 4) * c + 8 * i + e] : 0.f;
+        const float x = v[e] * keep;
         const __bf16 h = (__bf16)x;
         hi[i][e] = h;
         lo[i][e] = (__bf16)(x - (float)h);

@@ -505,11 +505,14 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       // count removes a zero-mass term
       m.on = bk >= 0 && bk < NBa && !nc ? 1.f : 0.f;
     };
+    // the query's MFMA operand loads go first: waiting for them then does
+    // not wait for the tile's
+    const typename QMfma<D>::Raw qr = QMfma<D>::template fetch<G>(a.q + (size_t)unit * G * D, lane);
     TileM<D> t0;
     BlockMean<D> m0;
     load_block(t0, m0, 0);
     QMfma<D> qm;
-    qm.template build<G>(q_l, lane);
+    qm.template build_from<G>(qr, lane);
     float* pw = pbuf + wave * 16 * G;
     if constexpr (G <= 4) {
       if (n_w == 1) {
