@@ -243,7 +243,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   // (w >= AW), while the others attend: wave w folds records
   // c0 + (w - AW) + RW*i. The first RPF are loaded now; they do not depend
   // on the selection.
-  const int c0 = (int)((long)p * NC / P), c1 = (int)((long)(p + 1) * NC / P);
+  // (32-bit: p*NC stays below 2^31, NC <= 384 and P <= 12288/4)
+  const int c0 = (int)((unsigned)(p * NC) / (unsigned)P), c1 = (int)((unsigned)((p + 1) * NC) / (unsigned)P);
   const int clast = c1 > 0 ? c1 - 1 : 0;
   const int rw = wave - AW;  // record wave index (negative: an attending wave)
   RecordRegs<D, G> rf[RPF];
