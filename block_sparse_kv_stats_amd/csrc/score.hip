@@ -42,11 +42,13 @@ namespace {
 
 // How σ̂² is formed. kDbarRow (r <= 8): per (block, head) from the block's r
 // D̄ entries and the head's r group energies E_t = sum_{i in G_t} q_i^2, the
-// page's form. Otherwise per coordinate and summed over the block's lanes
-// with z̄; then how a lane's 4 coordinates 4c..4c+3 map to D̄ entries (group
-// size gs = d/r).
-enum DbarMode { kDbarOne = 0, kDbarPair = 1, kDbarQuad = 2, kDbarRow = 3 };  // gs >= 4, gs == 2, gs == 1; r <= 8
+// page's form; kDbarRow4 is the same for r = 4, the block's D̄ in one 16-byte
+// load. Otherwise per coordinate and summed over the block's lanes with z̄;
+// then how a lane's 4 coordinates 4c..4c+3 map to D̄ entries (group size
+// gs = d/r).
+enum DbarMode { kDbarOne = 0, kDbarPair = 1, kDbarQuad = 2, kDbarRow = 3, kDbarRow4 = 4 };  // gs >= 4, gs == 2, gs == 1; r <= 8; r == 4
 constexpr int kRowMaxR = 8;
+constexpr bool row_mode(int dm) { return dm == kDbarRow || dm == kDbarRow4; }
 
 __device__ __forceinline__ float dot4(const float4 a, const float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
@@ -81,6 +83,8 @@ struct DbarTile<kDbarRow, ROWS, KC> {  // unused: σ̂² is formed per (block, h
   __device__ void load(const float*, size_t, int, int, int, int, int) {}
   __device__ float qsq_dot(const float4, int, int) const { return 0.f; }
 };
+template <int ROWS, int KC>
+struct DbarTile<kDbarRow4, ROWS, KC> : DbarTile<kDbarRow, ROWS, KC> {};
 template <int ROWS, int KC>
 struct DbarTile<kDbarQuad, ROWS, KC> {
   float4 x[ROWS][KC];
@@ -251,7 +255,7 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
 // per SIMD: a grid of 4096 scoring waves plus the append workgroups is then
 // resident in one round on 256 CUs.
 template <int G, int DM, int ROWS, bool NC>
-constexpr bool score_defers_vbar() { return !NC && DM == kDbarRow && G == 4; }
+constexpr bool score_defers_vbar() { return !NC && row_mode(DM) && G == 4; }
 template <int G, int DM, int ROWS, bool NC>
 constexpr int score_waves_per_simd() { return score_defers_vbar<G, DM, ROWS, NC>() && ROWS == 4 ? 5 : 1; }
 
@@ -273,7 +277,7 @@ void score_kernel(ScoreArgs a) {
   __shared__ float cml[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of z̄
   __shared__ float cma[kScoreWaves * G * 2];                 // per-wave (max, normaliser) of a
   __shared__ __align__(16) float4 q_s[G * D / 4];            // the G query heads
-  __shared__ float e_s[G * kRowMaxR];                        // kDbarRow: group energies E[g][t]
+  __shared__ float e_s[G * kRowMaxR];                        // row modes: group energies E[g][t]
 
   // The scoring path's kernel arguments are read with the first batch: used
   // only after the branch below, their loads would otherwise be issued (and
@@ -305,7 +309,7 @@ void score_kernel(ScoreArgs a) {
   float4 kv[ROWS][KC], vv[ROWS][KC];
   DbarTile<DM, ROWS, KC> dt;
   float n;
-  float dbr[kRowMaxR];  // kDbarRow: D̄ of this lane's block tb
+  float dbr[kRowMaxR];  // kDbarRow, kDbarRow4: D̄ of this lane's block tb
   const float4* kbar4 = reinterpret_cast<const float4*>(a.kbar);
   const float4* vbar4 = reinterpret_cast<const float4*>(a.vbar);
   // lim: the highest block index read (indices are clamped to it)
@@ -324,9 +328,12 @@ void score_kernel(ScoreArgs a) {
     }
     const size_t trow_idx = ubase + (tb < lim ? tb : lim);
     n = a.cnt[trow_idx];
-    if constexpr (DM == kDbarRow) {
+    if constexpr (DM == kDbarRow4) {
+      const float4 d4 = *reinterpret_cast<const float4*>(a.dbar + trow_idx * 4);
+      dbr[0] = d4.x; dbr[1] = d4.y; dbr[2] = d4.z; dbr[3] = d4.w;
+    } else if constexpr (DM == kDbarRow) {
 #pragma unroll
-      for (int t = 0; t < kRowMaxR; ++t) dbr[t] = t < r ? a.dbar[trow_idx * r + t] : 0.f;
+      for (int t = 0; t < kRowMaxR; ++t) dbr[t] = a.dbar[trow_idx * r + (t < r ? t : r - 1)];  // masked at use
     }
   };
   // One sequence: the addresses do not wait for seq_len (max_blocks bounds
@@ -341,9 +348,6 @@ void score_kernel(ScoreArgs a) {
   int T, NB, lim;
   if constexpr (ONE) {
     issue_loads(MB - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    T = a.seq_len[s];
-    NB = blocks_of(T);
     lim = MB - 1;
   } else {
     T = a.seq_len[s];
@@ -368,7 +372,7 @@ void score_kernel(ScoreArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   if (tid < G * D / 4) q_s[tid] = qown;
   lds_barrier();
-  if constexpr (DM == kDbarRow) {
+  if constexpr (row_mode(DM)) {
     // E[g][t]: thread g*r + t sums its group's squared coordinates
     if (tid < G * r) {
       const int g = tid / r, t = tid - g * r, gs4 = D / r / 4;
@@ -379,6 +383,13 @@ void score_kernel(ScoreArgs a) {
     }
     lds_barrier();
   }
+  if constexpr (ONE) {
+    // seq_len is read after the query is staged: it is the last load issued,
+    // so waiting for it waits for every summary load, and the staging and
+    // the group energies above then run while the summaries are in flight
+    T = a.seq_len[s];
+    NB = blocks_of(T);
+  }
 
   const float invd = 1.0f / (float)D;
 
@@ -386,7 +397,7 @@ void score_kernel(ScoreArgs a) {
   // every (row, head), then summed over the block's 16 lanes, transposed: lane
   // j ends with (tb, tg).
   float z, s2;
-  if constexpr (DM == kDbarRow) {
+  if constexpr (row_mode(DM)) {
     float x[NP];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -405,7 +416,8 @@ void score_kernel(ScoreArgs a) {
     z = x[0] * a.isd;
     float sp = 0.f;
 #pragma unroll
-    for (int t = 0; t < kRowMaxR; ++t) sp += t < r ? e_s[tg * kRowMaxR + t] * dbr[t] : 0.f;
+    for (int t = 0; t < (DM == kDbarRow4 ? 4 : kRowMaxR); ++t)
+      sp += (DM == kDbarRow4 || t < r) ? e_s[tg * kRowMaxR + t] * dbr[t] : 0.f;
     s2 = sp * invd;
   } else {
     float x[2 * NP];
@@ -571,12 +583,13 @@ void score_kernel(ScoreArgs a) {
 hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const int gs = d / a.r;
-  const int dm = a.r <= kRowMaxR ? kDbarRow : gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
+  const int dm = a.r == 4 ? kDbarRow4 : a.r <= kRowMaxR ? kDbarRow : gs >= 4 ? kDbarOne : (gs == 2 ? kDbarPair : kDbarQuad);
   const void* f = nullptr;
   const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
   const bool one = a.S == 1;
 #define CKNV_SCORE_ONE(DD, GG, RR, NC, ONE)                                       \
-  f = dm == kDbarRow ? (const void*)score_kernel<DD, GG, kDbarRow, RR, NC, ONE>   \
+  f = dm == kDbarRow4 ? (const void*)score_kernel<DD, GG, kDbarRow4, RR, NC, ONE> \
+    : dm == kDbarRow ? (const void*)score_kernel<DD, GG, kDbarRow, RR, NC, ONE>   \
     : dm == kDbarOne ? (const void*)score_kernel<DD, GG, kDbarOne, RR, NC, ONE>   \
     : dm == kDbarPair ? (const void*)score_kernel<DD, GG, kDbarPair, RR, NC, ONE> \
                       : (const void*)score_kernel<DD, GG, kDbarQuad, RR, NC, ONE>;
