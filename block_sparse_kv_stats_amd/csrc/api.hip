@@ -40,7 +40,7 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   Plan q{};
   q.U = sh->S * sh->H;
   q.NBmax = max_blocks;
-  q.rows = score_rows(G, max_blocks, q.U);
+  q.rows = score_rows(G);
   q.bpw = 4 * q.rows;
   q.NG = (max_blocks + q.bpw - 1) / q.bpw;
   q.Kb = budget_tokens / kBlock;

@@ -14,16 +14,15 @@ constexpr int kBlock = 16;          // tokens per block (CompKV page, "Assumptio
 constexpr int kThreads = 256;       // threads per workgroup of the score and attend kernels
 constexpr int kWaves = kThreads / 64;
 // Score-kernel geometry: a wave covers 4 blocks per row (16 lanes each) and
-// 2 or 4 rows (a score group of 8 or 16 blocks; 2 rows at G = 8). Fewer rows
-// give more waves, which pays while the grid is small (measured at 32K with
-// the deferred mean values: 2 rows end the scoring pass 0.4 us sooner); the
-// workspace plan picks the rows. The selection works with either group size.
+// 2 or 4 rows (a score group of 8 or 16 blocks; 2 rows at G = 8, where 4
+// do not fit the registers). 4 rows halve the score groups, chunk headers
+// and chunk records that every fused-step workgroup reduces afterwards
+// (measured at 32K: the scoring pass takes as long with 4 rows as with 2, and
+// the step kernel 0.3 us less). The selection works with either group size.
 constexpr int kScoreThreads = 256;  // score kernel: 4 waves per workgroup (one chunk record each)
 constexpr int kScoreWaves = kScoreThreads / 64;
 constexpr int kScoreMinGroup = 8;  // blocks of the smaller score group
-__host__ __device__ constexpr int score_rows(int G, int max_blocks, int units) {
-  return G >= 8 ? 2 : G <= 2 ? 4 : ((long)units * ((max_blocks + 7) / 8) <= 4096 ? 2 : 4);
-}
+__host__ __device__ constexpr int score_rows(int G) { return G >= 8 ? 2 : 4; }
 constexpr int kAppendThreads = 1024;
 constexpr int kMaxChunksPerAttendWG = 8;  // score-chunk partials folded by one attend workgroup
 constexpr int kDenseThreads = 512;        // dense attention: 8 waves per workgroup

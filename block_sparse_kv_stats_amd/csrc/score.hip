@@ -600,7 +600,7 @@ hipError_t launch_score(int d, int G, const ScoreArgs& a, int U, hipStream_t st)
     if (nc) { CKNV_SCORE_NC(DD, GG, RR, true) } else { CKNV_SCORE_NC(DD, GG, RR, false) } \
   }
 #define CKNV_SCORE_CASE(DD) \
-  CKNV_SCORE_R(DD, 1, 4) CKNV_SCORE_R(DD, 2, 4) CKNV_SCORE_R(DD, 4, 2) CKNV_SCORE_R(DD, 4, 4) CKNV_SCORE_R(DD, 8, 2)
+  CKNV_SCORE_R(DD, 1, 4) CKNV_SCORE_R(DD, 2, 4) CKNV_SCORE_R(DD, 4, 4) CKNV_SCORE_R(DD, 8, 2)
   CKNV_SCORE_CASE(64) CKNV_SCORE_CASE(128)
 #undef CKNV_SCORE_CASE
 #undef CKNV_SCORE_R
