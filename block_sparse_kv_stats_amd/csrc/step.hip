@@ -31,7 +31,8 @@
 //              block's a to LSE_g, shared through LDS; factors
 //              e^{group max - LSE} of the thread's score groups to LDS;
 //   keys       S_b per block (fp32 bits order like the values, S_b >= 0);
-//              scores; 2048-bin histogram of the candidates' top 11 bits;
+//              scores; 2048-bin histogram of the candidates' key bits
+//              30..20 (S >= 0, so bit 31 is 0: all 2048 bins are used);
 //              the keys through LDS into the threads' contiguous runs;
 //   select     the bin holding the (Kb-3)-th largest candidate key; keys
 //              in that bin are ranked exactly (or, for long runs of equal
@@ -51,6 +52,11 @@
 namespace cknv {
 
 namespace {
+
+// First histogram pass: key >> 20, 2048 bins over the exponent and three
+// mantissa bits of S (its sign bit is 0). Long runs of equal keys are pinned
+// by two more passes, over bits 19..9 (2048 bins) and 8..0 (512 bins).
+constexpr int kBinShift = 20;
 
 template <int D, int G, int KPTB>
 struct StepCfg {
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       key[j] = (inr && S > 0.f) ? __float_as_uint(S) : 0u;
       const bool c = inr && b >= 1 && b <= NB - 3;  // a Top-K candidate
       if (scores && inr) scores[b] = S;
-      if (c && count) atomicAdd(&hist[key[j] >> 21], 1);
+      if (c && count) atomicAdd(&hist[key[j] >> kBinShift], 1);
     }
   }
 
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const bool c = (cand >> i) & 1u;
-        const uint32_t kb = kr[i] >> 21;
+        const uint32_t kb = kr[i] >> kBinShift;
         pin |= (uint64_t)(c && kb == tau_bin) << i;
         gtm |= (uint64_t)(c && kb > tau_bin) << i;
       }
@@ -406,24 +412,24 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       lds_barrier();
     } else {
       // long runs of equal keys: pin the exact threshold key with two more radix passes
-      uint32_t prefix = tau_bin << 21;
+      uint32_t prefix = tau_bin << kBinShift;
       for (int i = tid; i < 2048; i += NT) hist[i] = 0;
       lds_barrier();
 #pragma unroll
       for (int i = 0; i < KPT; ++i)
-        if (((cand >> i) & 1u) && (kr[i] >> 21) == (prefix >> 21)) atomicAdd(&hist[(kr[i] >> 10) & 2047u], 1);
+        if (((cand >> i) & 1u) && (kr[i] >> kBinShift) == (prefix >> kBinShift)) atomicAdd(&hist[(kr[i] >> 9) & 2047u], 1);
       lds_barrier();
       if (wave == 0) find_bin<2048>(hist, krem, ctl);
       lds_barrier();
-      prefix |= ((uint32_t)ctl[0]) << 10;
+      prefix |= ((uint32_t)ctl[0]) << 9;
       krem = ctl[1];
-      for (int i = tid; i < 1024; i += NT) hist[i] = 0;
+      for (int i = tid; i < 512; i += NT) hist[i] = 0;
       lds_barrier();
 #pragma unroll
       for (int i = 0; i < KPT; ++i)
-        if (((cand >> i) & 1u) && (kr[i] >> 10) == (prefix >> 10)) atomicAdd(&hist[kr[i] & 1023u], 1);
+        if (((cand >> i) & 1u) && (kr[i] >> 9) == (prefix >> 9)) atomicAdd(&hist[kr[i] & 511u], 1);
       lds_barrier();
-      if (wave == 0) find_bin<1024>(hist, krem, ctl);
+      if (wave == 0) find_bin<512>(hist, krem, ctl);
       lds_barrier();
       prefix |= (uint32_t)ctl[0];
       krem = ctl[1];
