@@ -327,20 +327,72 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   merge_records<D, G, kDenseThreads>(recs, NWV, a.part + ((size_t)unit * a.P + p) * G * W, scl);
 }
 
-// Merge each unit's P part records into out and lse: kMergeCols workgroups
-// per unit, one output column per thread, all of a column's records loaded
-// in one round trip (up to 32 parts).
-constexpr int kMergeCols = kThreads;
+// Merge each unit's P part records into out and lse. A workgroup takes 64
+// output columns of one unit; its four waves each merge every fourth part
+// record for those columns (8 records per round trip, lane = column, so a
+// record's values are one coalesced 256-byte read and its (m, l) one
+// broadcast), and the four partial (M, L, A) are combined through the LDS.
+// Splitting the records over waves keeps each thread's load count at P/4:
+// with one thread per column taking all P records, the loads' issue, not
+// their latency, set the kernel's time.
+constexpr int kMergeCols = 64;
 template <int D, int G>
-constexpr int merge_wgs() { return (G * D + kMergeCols - 1) / kMergeCols; }
+constexpr int merge_wgs() { return G * D / kMergeCols; }
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttendArgs a) {
-  constexpr int W = rec_words(D), CB = merge_wgs<D, G>();
+  constexpr int W = rec_words(D), CB = merge_wgs<D, G>(), Q = kThreads / kMergeCols, RB = 8;
+  static_assert(D % kMergeCols == 0, "a workgroup's columns lie in one head");
+  __shared__ float part_s[Q][3][kMergeCols];
   const int unit = blockIdx.x / CB, cb = blockIdx.x - unit * CB;
-  merge_parts<D, G, kMergeCols, 32, 1, false>(a.part + (size_t)unit * a.P * G * W, a.P,
-                                              a.out + (size_t)unit * G * D,
-                                              a.lse ? a.lse + (size_t)unit * G : nullptr, cb * kMergeCols);
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int col = cb * kMergeCols + lane, g = col / D, c = col - g * D;
+  const int P = a.P;
+  const float* parts = a.part + (size_t)unit * P * G * W + (size_t)g * W;
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  for (int i0 = q; i0 < P; i0 += Q * RB) {
+    float m[RB], l[RB], x[RB];
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const int i = i0 + Q * k;
+      const float* r = parts + (size_t)(i < P ? i : P - 1) * G * W;
+      m[k] = r[0] + (i < P ? 0.f : -INFINITY);  // a slot past the last record weighs 0
+      l[k] = r[1];
+      x[k] = r[4 + c];
+    }
+    float MM = M;
+#pragma unroll
+    for (int k = 0; k < RB; ++k) MM = fmaxf(MM, m[k]);
+    const float so = rescale(M, MM);
+    L *= so;
+    A *= so;
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      const float f = rescale(m[k], MM);
+      L += l[k] * f;
+      A += x[k] * f;
+    }
+    M = MM;
+  }
+  part_s[q][0][lane] = M;
+  part_s[q][1][lane] = L;
+  part_s[q][2][lane] = A;
+  lds_barrier();
+  if (q == 0) {
+    float MM = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < Q; ++k) MM = fmaxf(MM, part_s[k][0][lane]);
+    float LL = 0.f, AA = 0.f;
+#pragma unroll
+    for (int k = 0; k < Q; ++k) {
+      const float f = rescale(part_s[k][0][lane], MM);
+      LL += part_s[k][1][lane] * f;
+      AA += part_s[k][2][lane] * f;
+    }
+    const bool ok = LL > 0.f;
+    a.out[(size_t)unit * G * D + col] = ok ? AA / LL : 0.f;
+    if (c == 0 && a.lse) a.lse[(size_t)unit * G + g] = ok ? MM + __logf(LL) : -INFINITY;
+  }
 }
 
 hipError_t launch_attend(int d, int G, bool dense, const AttendArgs& a, int U, hipStream_t st) {
