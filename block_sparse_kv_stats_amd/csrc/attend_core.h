@@ -466,6 +466,52 @@ __device__ __forceinline__ void stage_records(const float* src, int n, float* ld
   }
 }
 
+// Merge a unit's P <= 64 part records into out and lse, one output column
+// per thread (columns tid + NT*k, k < COLS). The 64 columns of a wave lie in
+// one query head, so the records' (m, l) are loaded once per wave, lane i
+// holding record i's, and each record's weight e^{m_i - M} reaches the
+// lanes by readlane: P + 2 loads per thread instead of 3P (the loads'
+// issue, not their latency, bounds a merge of 32 records). Loads are issued
+// 16 records at a time. COHERENT: agent-scope loads, as merge_parts.
+template <int D, int G, int NT, int COLS, bool COHERENT>
+__device__ void merge_parts_lanes(const float* parts, int P, float* out, float* lse) {
+  constexpr int W = rec_words(D), RB = 16;
+  static_assert(D % 64 == 0, "a wave's columns lie in one head");
+  const int tid = threadIdx.x, lane = tid & 63;
+  auto ld = [](const float* p) {
+    if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+  };
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) {
+    const int colw = tid - lane + NT * k;  // the wave's first column (wave-uniform)
+    if (colw >= G * D) break;
+    const int g = colw / D, col = colw + lane, c = col - g * D;
+    const float* pg = parts + (size_t)g * W;
+    const int li = lane < P ? lane : P - 1;
+    const float ml = ld(pg + (size_t)li * G * W) + (lane < P ? 0.f : -INFINITY);
+    const float ll = ld(pg + (size_t)li * G * W + 1);
+    const float M = group_max<64>(ml);
+    const float f = rescale(ml, M);  // 0 past the last record
+    const float L = group_sum<64>(ll * f);
+    float A = 0.f;
+    for (int i0 = 0; i0 < P; i0 += RB) {
+      float x[RB];
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        const int i = i0 + t < P ? i0 + t : P - 1;
+        x[t] = ld(pg + (size_t)i * G * W + 4 + c);
+      }
+#pragma unroll
+      for (int t = 0; t < RB; ++t)
+        A += x[t] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i0 + t));
+    }
+    const bool ok = L > 0.f;
+    out[col] = ok ? A / L : 0.f;
+    if (c == 0 && lse) lse[g] = ok ? M + __logf(L) : -INFINITY;
+  }
+}
+
 // Merge a unit's P part records into out and lse. Thread t owns output
 // columns col0 + t + NT*k (k < COLS); records are read in batches of PB,
 // every load of a batch issued before the first use. COHERENT: agent-scope

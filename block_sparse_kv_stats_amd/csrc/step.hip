@@ -595,15 +595,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   }
   lds_barrier();
   if (!ctl[4]) return;
-  // up to 32 parts in one batch (one round trip) while a thread owns one
-  // output column (more would spill), else batches of 8
   // (the other parts' records were written with agent-scope stores, so they
   // are read with agent-scope loads)
+  // (up to 8 parts, one batch of 3P loads per thread is as fast: P = 8 at 32K)
   constexpr int COLS = (G * D + NT - 1) / NT;
-  if (G * D <= NT && P > 8 && P <= 32)
-    merge_parts<D, G, NT, (G * D <= NT ? 32 : 8), COLS, true>(
-        a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
-        a.lse ? a.lse + (size_t)unit * G : nullptr, 0);
+  if (P > 8 && P <= 64)
+    merge_parts_lanes<D, G, NT, COLS, true>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
+                                            a.lse ? a.lse + (size_t)unit * G : nullptr);
   else
     merge_parts<D, G, NT, 8, COLS, true>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
                                          a.lse ? a.lse + (size_t)unit * G : nullptr, 0);
