@@ -123,16 +123,16 @@ struct TileW {
     const int t = lane & 15, c = lane >> 4;
     const uint16_t* ks = kc + (size_t)(tok0 + (t < last ? t : last)) * D + (D / 4) * c;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) k[i] = ldg<true>(reinterpret_cast<const u32x4_t*>(ks + 8 * i));
+    for (int i = 0; i < NI; ++i) k[i] = ldg<false>(reinterpret_cast<const u32x4_t*>(ks + 8 * i));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * i + c;
       const uint16_t* vs = vc + (size_t)(tok0 + (row < last ? row : last)) * D + VP * t;
       if constexpr (VW == 4) {
-        const uint4 x = stream_load_u4<true>(vs);
+        const uint4 x = stream_load_u4<false>(vs);
         v[i][0] = x.x; v[i][1 % VW] = x.y; v[i][2 % VW] = x.z; v[i][3 % VW] = x.w;
       } else {
-        const uint2 x = stream_load_u2<true>(vs);
+        const uint2 x = stream_load_u2<false>(vs);
         v[i][0] = x.x; v[i][1 % VW] = x.y;
       }
     }
@@ -252,7 +252,7 @@ __device__ __forceinline__ void store_wave_record_w(const WaveStateW<D, G>& st, 
 
 // Full attention, every block exact, no compensation: P workgroups of
 // kDenseThreads threads per unit, the unit's blocks dealt round-robin over
-// all their waves, each wave keeping several tiles of non-temporal loads in
+// all their waves, each wave keeping several tiles of plain loads in
 // flight, logits on MFMA; the waves' records merge into the workgroup's part
 // record, and merge_kernel merges the P part records.
 template <int D, int G>

@@ -199,7 +199,12 @@ __device__ __forceinline__ float rows_max(float x) {
 // Global loads. NT = true marks data streamed once per step (non-temporal: it
 // does not displace reused lines from the caches). The hint costs latency (a
 // cold random 16-token tile took 3.3 us with it against 2.8 us without, on
-// MI355X), so loads on a latency-bound path use NT = false.
+// MI355X), so loads on a latency-bound path use NT = false. Which streams
+// gain from it was measured, not assumed: the score kernel's summary stream
+// and the bulk build are faster with it (without: 130 against 119 us on the
+// 16-sequence batch; 0.64 against 0.70 of peak), the dense kernel's K/V tile
+// stream without it (0.53 against 0.49 of peak at 32K, 0.70 against 0.62 at
+// 128K).
 template <bool NT, typename V>
 __device__ __forceinline__ V ldg(const V* p) {
   if constexpr (NT) return __builtin_nontemporal_load(p);
