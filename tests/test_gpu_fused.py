@@ -117,6 +117,15 @@ def test_fused_many_parts_and_records():
     run_steps(w, summaries_every=1)
 
 
+def test_fused_more_than_64_parts():
+    """One KV head, 40K context, a budget of 8192 tokens: 128 parts per unit,
+    past the 64 whose records the last part merges lane-parallel, so the
+    merge takes its batched path, against the oracle."""
+    w = synth.WORKLOADS["llama8b_32k"].replace(name="one head, 128 parts", H=1, prefill=(40000,),
+                                              budget=8192, steps=2)
+    run_steps(w, summaries_every=1)
+
+
 def test_fused_constant_blocks_tie_to_lower_index():
     w = synth.Workload("const", 79, S=1, H=2, G=4, d=128, r=4, budget=160, prefill=(16 * 50 - 1,),
                        steps=1, needles=False)
