@@ -70,6 +70,8 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   off = align256(off + (size_t)sh->S * 4);
   q.off_fpart = off;
   off = align256(off + (size_t)q.U * q.Pf * G * W * 4);
+  q.off_fphdr = off;
+  off = align256(off + (size_t)q.U * G * q.Pf * 2 * 4);
   q.off_finfo = off;
   off = align256(off + (size_t)q.U * G * 2 * 4);
   q.off_hdr = off;
@@ -219,6 +221,7 @@ static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv
   sa.hdr = reinterpret_cast<const float*>(w + p.off_hdr);
   sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel; sa.out = out; sa.lse = lse;
   sa.part = reinterpret_cast<float*>(w + p.off_fpart);
+  sa.phdr = reinterpret_cast<float*>(w + p.off_fphdr);
   sa.S = shape->S; sa.H = shape->H; sa.r = shape->r; sa.cap_blocks = shape->cap_blocks;
   sa.max_blocks = max_blocks; sa.NG = p.NG; sa.C = p.C; sa.Kb = p.Kb; sa.P = p.Pf; sa.kpw = p.kpw;
   sa.bpw_shift = p.bpw == 8 ? 3 : 4;

@@ -441,6 +441,48 @@ __device__ __forceinline__ void merge_records(const float* recs, int n, float* d
   }
 }
 
+// Merge N records of G x W words (LDS, consecutive) into one record at dst
+// (global), with no barrier: each thread forms its columns' scale factors
+// e^{m_i - M} itself (the m_i reads are broadcasts within a wave, whose
+// columns lie in one query head). Query head g's (m, l) is also written as
+// one float pair at hdr + 2*g*hstride. COHERENT: agent-scope stores, as
+// merge_records.
+template <int D, int G, int NT, int N, bool COHERENT>
+__device__ __forceinline__ void merge_wave_records(const float* recs, float* dst, float* hdr, int hstride) {
+  constexpr int W = rec_words(D);
+  auto st = [](float* p, float v) {
+    if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+  };
+  for (int col = threadIdx.x; col < G * D; col += NT) {
+    const int g = col / D, c = col - g * D;
+    float m[N], M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      m[i] = recs[(i * G + g) * W];
+      M = fmaxf(M, m[i]);
+    }
+    float A = 0.f, L = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float f = rescale(m[i], M);
+      A += recs[(i * G + g) * W + 4 + c] * f;
+      L += recs[(i * G + g) * W + 1] * f;
+    }
+    st(dst + g * W + 4 + c, A);
+    if (c == 0) {
+      st(dst + g * W, M);
+      st(dst + g * W + 1, L);
+      st(dst + g * W + 2, 0.f);
+      st(dst + g * W + 3, 0.f);
+      uint64_t* h = reinterpret_cast<uint64_t*>(hdr) + (size_t)g * hstride;
+      const uint64_t bits = (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(L) << 32);
+      if constexpr (COHERENT) __hip_atomic_store(h, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else *h = bits;
+    }
+  }
+}
+
 template <int G>
 constexpr int stage_cap() { return G <= 4 ? 24 : 12; }
 
@@ -466,17 +508,23 @@ __device__ __forceinline__ void stage_records(const float* src, int n, float* ld
   }
 }
 
-// Merge a unit's P <= 64 part records into out and lse, one output column
-// per thread (columns tid + NT*k, k < COLS). The 64 columns of a wave lie in
-// one query head, so the records' (m, l) are loaded once per wave, lane i
-// holding record i's, and each record's weight e^{m_i - M} reaches the
-// lanes by readlane: P + 2 loads per thread instead of 3P (the loads'
-// issue, not their latency, bounds a merge of 32 records). Loads are issued
-// 16 records at a time. COHERENT: agent-scope loads, as merge_parts.
-template <int D, int G, int NT, int COLS, bool COHERENT>
-__device__ void merge_parts_lanes(const float* parts, int P, float* out, float* lse) {
-  constexpr int W = rec_words(D), RB = 16;
+// Merge a unit's P <= RB part records (RB <= 64) into out and lse, one
+// output column per thread (columns tid + NT*k, k < COLS). The 64 columns of
+// a wave lie in one query head, so the records' (m, l) are loaded once per
+// wave, lane i holding record i's, and each record's weight e^{m_i - M}
+// reaches the lanes by readlane: P + 1 loads per thread instead of 3P. The
+// pairs come from `hdr` ([G][P] float pairs, parts contiguous: a wave's pair
+// load touches 4 cache lines, where the records' own headers, a record
+// apart, touch 64; the lines a merge requests, not its round trips, bound
+// it). Every load is issued before the first use, the pair first (the
+// reductions wait only for it). Slots past P reload record P - 1 with
+// weight 0. COHERENT: agent-scope loads, as merge_parts.
+template <int D, int G, int NT, int COLS, int RB, bool COHERENT>
+__device__ __forceinline__ void merge_parts_lanes(const float* parts, const float* hdr, int P, float* out,
+                                                  float* lse) {
+  constexpr int W = rec_words(D);
   static_assert(D % 64 == 0, "a wave's columns lie in one head");
+  static_assert(RB <= 64, "one record per lane");
   const int tid = threadIdx.x, lane = tid & 63;
   auto ld = [](const float* p) {
     if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -489,23 +537,21 @@ __device__ void merge_parts_lanes(const float* parts, int P, float* out, float* 
     const int g = colw / D, col = colw + lane, c = col - g * D;
     const float* pg = parts + (size_t)g * W;
     const int li = lane < P ? lane : P - 1;
-    const float ml = ld(pg + (size_t)li * G * W) + (lane < P ? 0.f : -INFINITY);
-    const float ll = ld(pg + (size_t)li * G * W + 1);
-    const float M = group_max<64>(ml);
-    const float f = rescale(ml, M);  // 0 past the last record
+    const uint64_t* hp = reinterpret_cast<const uint64_t*>(hdr) + (size_t)g * P + li;
+    uint64_t mlb;
+    if constexpr (COHERENT) mlb = __hip_atomic_load(hp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else mlb = *hp;
+    const float ml = __uint_as_float((uint32_t)mlb), ll = __uint_as_float((uint32_t)(mlb >> 32));
+    float x[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) x[t] = ld(pg + (size_t)(t < P ? t : P - 1) * G * W + 4 + c);
+    const float mb = ml + (lane < P ? 0.f : -INFINITY);
+    const float M = group_max<64>(mb);
+    const float f = rescale(mb, M);  // 0 past the last record
     const float L = group_sum<64>(ll * f);
     float A = 0.f;
-    for (int i0 = 0; i0 < P; i0 += RB) {
-      float x[RB];
 #pragma unroll
-      for (int t = 0; t < RB; ++t) {
-        const int i = i0 + t < P ? i0 + t : P - 1;
-        x[t] = ld(pg + (size_t)i * G * W + 4 + c);
-      }
-#pragma unroll
-      for (int t = 0; t < RB; ++t)
-        A += x[t] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), i0 + t));
-    }
+    for (int t = 0; t < RB; ++t) A += x[t] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), t));
     const bool ok = L > 0.f;
     out[col] = ok ? A / L : 0.f;
     if (c == 0 && lse) lse[g] = ok ? M + __logf(L) : -INFINITY;
@@ -518,7 +564,7 @@ __device__ void merge_parts_lanes(const float* parts, int P, float* out, float* 
 // loads (records written by other workgroups of the same launch with
 // agent-scope stores).
 template <int D, int G, int NT, int PB, int COLS, bool COHERENT>
-__device__ void merge_parts(const float* parts, int P, float* out, float* lse, int col0) {
+__device__ __forceinline__ void merge_parts(const float* parts, int P, float* out, float* lse, int col0) {
   constexpr int W = rec_words(D);
   const int tid = threadIdx.x;
   auto ld = [](const float* p) {

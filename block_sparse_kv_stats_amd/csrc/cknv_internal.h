@@ -50,8 +50,8 @@ struct Plan {
   int Pf;           // fused-step workgroups per unit = ceil(Kb/(kStepAttendWaves*kpw))
   int kpw;          // fused step: kept blocks per attending wave
   int Pd;           // dense-attend workgroups per unit
-  size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, off_finfo, off_hdr, off_pcnt,
-      total;
+  size_t off_grp, off_u, off_comp, off_attp, off_dense, off_t0, off_fpart, off_fphdr, off_finfo, off_hdr,
+      off_pcnt, total;
 };
 
 int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p);
@@ -105,6 +105,7 @@ struct StepArgs {
   int32_t* seq_len; const int32_t* t0; const float* q;
   const float* grp; const float* u; const float* comp; const float* hdr;
   float* scores; int32_t* sel; int32_t* n_sel; float* out; float* lse; float* part;
+  float* phdr;         // per unit, query head and part: the part record's (m, l), parts contiguous
   const float* finfo;  // per unit and query head: (a, factor) of the block the token landed in
   uint32_t* pcnt;      // per unit: parts done this step (zeroed by the scoring launch)
   int S, H, r, cap_blocks, max_blocks, NG, C, Kb, P, bpw_shift;

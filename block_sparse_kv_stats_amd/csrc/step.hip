@@ -586,7 +586,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   // the relaxed counter add, and the merging part's loads carry sc1. A test
   // reads the built assembly of every instance for exactly that order.
   float* mine = a.part + ((size_t)unit * P + p) * G * W;
-  merge_records<D, G, NT, true>(recs, NW, mine, scl);
+  merge_wave_records<D, G, NT, NW, true>(recs, mine, a.phdr + ((size_t)unit * G * P + p) * 2, P);
   __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
   __syncthreads();
   if (tid == 0) {
@@ -597,14 +597,22 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   if (!ctl[4]) return;
   // (the other parts' records were written with agent-scope stores, so they
   // are read with agent-scope loads)
-  // (up to 8 parts, one batch of 3P loads per thread is as fast: P = 8 at 32K)
+  // (up to 8 parts, one batch of 3P loads per thread is as fast: P = 8 at 32K;
+  // 9-64 parts: one straight-line instance per size class, so that every load
+  // is issued before the first wait)
   constexpr int COLS = (G * D + NT - 1) / NT;
-  if (P > 8 && P <= 64)
-    merge_parts_lanes<D, G, NT, COLS, true>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
-                                            a.lse ? a.lse + (size_t)unit * G : nullptr);
+  const float* pr = a.part + (size_t)unit * P * G * W;
+  const float* ph = a.phdr + (size_t)unit * G * P * 2;
+  float* po = a.out + (size_t)unit * G * D;
+  float* pl = a.lse ? a.lse + (size_t)unit * G : nullptr;
+  if (P <= 8 || P > 64)
+    merge_parts<D, G, NT, 8, COLS, true>(pr, P, po, pl, 0);
+  else if (P <= 16)
+    merge_parts_lanes<D, G, NT, COLS, 16, true>(pr, ph, P, po, pl);
+  else if (P <= 32)
+    merge_parts_lanes<D, G, NT, COLS, 32, true>(pr, ph, P, po, pl);
   else
-    merge_parts<D, G, NT, 8, COLS, true>(a.part + (size_t)unit * P * G * W, P, a.out + (size_t)unit * G * D,
-                                         a.lse ? a.lse + (size_t)unit * G : nullptr, 0);
+    merge_parts_lanes<D, G, NT, COLS, 64, true>(pr, ph, P, po, pl);
   if (tid == 0) {
     __hip_atomic_store(a.pcnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (h == 0 && app) a.seq_len[s] = T;
