@@ -76,8 +76,9 @@ int make_plan(const cknv_shape* sh, int max_blocks, int budget_tokens, Plan* p) 
   off = align256(off + (size_t)q.U * G * 2 * 4);
   q.off_hdr = off;
   off = align256(off + (size_t)q.U * q.C * G * 2 * 4);
+  q.pstride = q.Pf > kFlatParts ? 1 + (q.Pf + kPartGroup - 1) / kPartGroup : 1;
   q.off_pcnt = off;
-  off = align256(off + (size_t)q.U * 4);
+  off = align256(off + (size_t)q.U * q.pstride * 4);
   q.total = off;
   if (max_blocks > kSelThreads * kSelKeysPerThread) return CKNV_EUNSUPPORTED;
   *p = q;
@@ -186,6 +187,7 @@ static int decode_score_impl(const Plan& p, const cknv_shape* shape, const cknv_
   a.t0_out = reinterpret_cast<int32_t*>(w + p.off_t0);
   a.finfo = reinterpret_cast<float*>(w + p.off_finfo);
   a.pcnt = reinterpret_cast<uint32_t*>(w + p.off_pcnt);
+  a.pstride = p.pstride;
   a.flags = (int)shape->flags;
   a.isd = 1.0f / sqrtf((float)shape->d);
   return hip_status(launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream));
@@ -215,6 +217,7 @@ static int decode_finish_impl(const Plan& p, const cknv_shape* shape, const cknv
   sa.q = q;
   sa.finfo = reinterpret_cast<const float*>(w + p.off_finfo);
   sa.pcnt = reinterpret_cast<uint32_t*>(w + p.off_pcnt);
+  sa.pstride = p.pstride;
   sa.grp = reinterpret_cast<const float*>(w + p.off_grp);
   sa.u = reinterpret_cast<const float*>(w + p.off_u);
   sa.comp = reinterpret_cast<const float*>(w + p.off_comp);
@@ -316,7 +319,7 @@ static int noalloc_workspace(const Plan& p, const cknv_shape* sh, void* stream, 
   char* base = static_cast<char*>(d.ptr);
   if (d.plan_total != p.total || d.plan_U != p.U || d.plan_S != sh->S || d.plan_pcnt != p.off_pcnt) {
     const hipError_t e = launch_zero_u32(reinterpret_cast<uint32_t*>(base + p.off_pcnt),
-                                         (size_t)p.U, (hipStream_t)stream);
+                                         (size_t)p.U * p.pstride, (hipStream_t)stream);
     if (e != hipSuccess) return CKNV_EHIP;
     d.plan_total = p.total;
     d.plan_U = p.U;

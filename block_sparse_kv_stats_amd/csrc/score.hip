@@ -191,7 +191,7 @@ __device__ void fresh_block(const ScoreArgs& a, int unit) {
   const int fblk = T0 / kBlock;
   const bool app = T0 < cap_tok && fblk < a.max_blocks;
   float2* fi = reinterpret_cast<float2*>(a.finfo) + (size_t)unit * G;
-  if (lane == 0) a.pcnt[unit] = 0u;  // read by the step kernel after this launch
+  for (int i = lane; i < a.pstride; i += 64) a.pcnt[(size_t)unit * a.pstride + i] = 0u;  // read by the step kernel
   if (!app) {
     if (lane < G) fi[lane] = make_float2(-INFINITY, 0.f);
     if (h == 0 && lane == 0) a.t0_out[s] = T0;

@@ -589,9 +589,28 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   merge_wave_records<D, G, NT, NW, true>(recs, mine, a.phdr + ((size_t)unit * G * P + p) * 2, P);
   __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
   __syncthreads();
+  uint32_t* uc = a.pcnt + (size_t)unit * a.pstride;  // the unit's counter, then its group counters
   if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(a.pcnt + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ctl[4] = done == (uint32_t)(P - 1);
+    auto count_in = [](uint32_t* c) {
+      return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    bool last;
+    if (P <= kFlatParts) {
+      last = count_in(uc) == (uint32_t)(P - 1);
+    } else {
+      // the group's last part counts the group in (its own stores, and so
+      // those of every part that counted into the group before it, are
+      // complete), and resets the group's counter: no part of the group
+      // counts again this step
+      const int grp = p / kPartGroup, ng = (P + kPartGroup - 1) / kPartGroup;
+      const int gsize = P - grp * kPartGroup < kPartGroup ? P - grp * kPartGroup : kPartGroup;
+      last = false;
+      if (count_in(uc + 1 + grp) == (uint32_t)(gsize - 1)) {
+        __hip_atomic_store(uc + 1 + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = count_in(uc) == (uint32_t)(ng - 1);
+      }
+    }
+    ctl[4] = last;
   }
   lds_barrier();
   if (!ctl[4]) return;
@@ -605,8 +624,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   const float* ph = a.phdr + (size_t)unit * G * P * 2;
   float* po = a.out + (size_t)unit * G * D;
   float* pl = a.lse ? a.lse + (size_t)unit * G : nullptr;
-  if (P <= 8 || P > 64)
+  if (P > 64)
     merge_parts<D, G, NT, 8, COLS, true>(pr, P, po, pl, 0);
+  else if (P <= 8)
+    merge_parts_lanes<D, G, NT, COLS, 8, true>(pr, ph, P, po, pl);
   else if (P <= 16)
     merge_parts_lanes<D, G, NT, COLS, 16, true>(pr, ph, P, po, pl);
   else if (P <= 32)
@@ -614,7 +635,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   else
     merge_parts_lanes<D, G, NT, COLS, 64, true>(pr, ph, P, po, pl);
   if (tid == 0) {
-    __hip_atomic_store(a.pcnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(uc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (h == 0 && app) a.seq_len[s] = T;
   }
 }
