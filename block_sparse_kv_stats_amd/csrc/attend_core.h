@@ -449,25 +449,37 @@ __device__ __forceinline__ void merge_records(const float* recs, int n, float* d
 // merge_records.
 template <int D, int G, int NT, int N, bool COHERENT>
 __device__ __forceinline__ void merge_wave_records(const float* recs, float* dst, float* hdr, int hstride) {
-  constexpr int W = rec_words(D);
+  constexpr int W = rec_words(D), CW = (G * D + NT - 1) / NT;  // columns per thread
+  static_assert(G * D % NT == 0 || CW == 1, "every thread owns CW columns");
   auto st = [](float* p, float v) {
     if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else *p = v;
   };
-  for (int col = threadIdx.x; col < G * D; col += NT) {
-    const int g = col / D, c = col - g * D;
-    float m[N], M = -INFINITY;
+  if (CW == 1 && (int)threadIdx.x >= G * D) return;
+  // every LDS read of every column first
+  float m[CW][N], l[CW][N], x[CW][N];
+#pragma unroll
+  for (int k = 0; k < CW; ++k) {
+    const int col = threadIdx.x + NT * k, g = col / D, c = col - g * D;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      m[i] = recs[(i * G + g) * W];
-      M = fmaxf(M, m[i]);
+      m[k][i] = recs[(i * G + g) * W];
+      l[k][i] = recs[(i * G + g) * W + 1];
+      x[k][i] = recs[(i * G + g) * W + 4 + c];
     }
+  }
+#pragma unroll
+  for (int k = 0; k < CW; ++k) {
+    const int col = threadIdx.x + NT * k, g = col / D, c = col - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < N; ++i) M = fmaxf(M, m[k][i]);
     float A = 0.f, L = 0.f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const float f = rescale(m[i], M);
-      A += recs[(i * G + g) * W + 4 + c] * f;
-      L += recs[(i * G + g) * W + 1] * f;
+      const float f = rescale(m[k][i], M);
+      A += x[k][i] * f;
+      L += l[k][i] * f;
     }
     st(dst + g * W + 4 + c, A);
     if (c == 0) {
@@ -525,33 +537,43 @@ __device__ __forceinline__ void merge_parts_lanes(const float* parts, const floa
   constexpr int W = rec_words(D);
   static_assert(D % 64 == 0, "a wave's columns lie in one head");
   static_assert(RB <= 64, "one record per lane");
+  static_assert(G * D % NT == 0 || COLS == 1, "every thread owns COLS columns");
   const int tid = threadIdx.x, lane = tid & 63;
   auto ld = [](const float* p) {
     if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else return *p;
   };
+  if (tid - lane >= G * D) return;  // (COLS == 1 only) a wave with no column
+  const int li = lane < P ? lane : P - 1;
+  // every load of every column first: the pairs, then the columns' values
+  float ml[COLS], ll[COLS], x[COLS][RB];
 #pragma unroll
   for (int k = 0; k < COLS; ++k) {
-    const int colw = tid - lane + NT * k;  // the wave's first column (wave-uniform)
-    if (colw >= G * D) break;
-    const int g = colw / D, col = colw + lane, c = col - g * D;
-    const float* pg = parts + (size_t)g * W;
-    const int li = lane < P ? lane : P - 1;
+    const int g = (tid + NT * k) / D;
     const uint64_t* hp = reinterpret_cast<const uint64_t*>(hdr) + (size_t)g * P + li;
     uint64_t mlb;
     if constexpr (COHERENT) mlb = __hip_atomic_load(hp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else mlb = *hp;
-    const float ml = __uint_as_float((uint32_t)mlb), ll = __uint_as_float((uint32_t)(mlb >> 32));
-    float x[RB];
+    ml[k] = __uint_as_float((uint32_t)mlb);
+    ll[k] = __uint_as_float((uint32_t)(mlb >> 32));
+  }
 #pragma unroll
-    for (int t = 0; t < RB; ++t) x[t] = ld(pg + (size_t)(t < P ? t : P - 1) * G * W + 4 + c);
-    const float mb = ml + (lane < P ? 0.f : -INFINITY);
+  for (int k = 0; k < COLS; ++k) {
+    const int col = tid + NT * k, g = col / D, c = col - g * D;
+    const float* pg = parts + (size_t)g * W;
+#pragma unroll
+    for (int t = 0; t < RB; ++t) x[k][t] = ld(pg + (size_t)(t < P ? t : P - 1) * G * W + 4 + c);
+  }
+#pragma unroll
+  for (int k = 0; k < COLS; ++k) {
+    const int col = tid + NT * k, g = col / D, c = col - g * D;
+    const float mb = ml[k] + (lane < P ? 0.f : -INFINITY);
     const float M = group_max<64>(mb);
     const float f = rescale(mb, M);  // 0 past the last record
-    const float L = group_sum<64>(ll * f);
+    const float L = group_sum<64>(ll[k] * f);
     float A = 0.f;
 #pragma unroll
-    for (int t = 0; t < RB; ++t) A += x[t] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), t));
+    for (int t = 0; t < RB; ++t) A += x[k][t] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), t));
     const bool ok = L > 0.f;
     out[col] = ok ? A / L : 0.f;
     if (c == 0 && lse) lse[g] = ok ? M + __logf(L) : -INFINITY;
