@@ -126,6 +126,16 @@ def test_fused_more_than_64_parts():
     run_steps(w, summaries_every=1)
 
 
+def test_fused_part_groups_with_a_partial_last_group():
+    """Two KV heads, 12K context, a budget of 1296 tokens (81 blocks): 21
+    parts per unit, past the 16 that count in on one counter, so they count
+    in by groups of 8, 8 and 5, and the last part merges 21 records, against
+    the oracle over three steps."""
+    w = synth.WORKLOADS["llama8b_32k"].replace(name="two heads, 21 parts", H=2, prefill=(12000,),
+                                              budget=1296, steps=3)
+    run_steps(w, summaries_every=1)
+
+
 def test_fused_constant_blocks_tie_to_lower_index():
     w = synth.Workload("const", 79, S=1, H=2, G=4, d=128, r=4, budget=160, prefill=(16 * 50 - 1,),
                        steps=1, needles=False)
