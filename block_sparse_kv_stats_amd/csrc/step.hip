@@ -42,9 +42,9 @@
 //   attend     waves w < AW: kept block w of this part's slice (exact terms
 //              minus its compensation); meanwhile waves w >= AW fold this
 //              part's chunk records;
-//   merge      the waves' records -> out, lse (P == 1) or a part record;
-//              the part that completes the unit's count merges the P part
-//              records into out and lse.
+//   merge      the waves' records -> out, lse (P == 1) or a part record
+//              and its (m, l) pairs; the part that completes the unit's count
+//              merges the P part records into out and lse.
 #include "attend_core.h"
 #include "select_core.h"
 #include "step_config.h"
@@ -576,10 +576,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     if (h == 0 && tid == 0 && app) a.seq_len[s] = T;
     return;
   }
-  // P > 1: this part's record goes out with agent-scope (cross-XCD coherent)
+  // P > 1: this part's record (and a copy of its (m, l) pairs in the unit's
+  // compact pair array) goes out with agent-scope (cross-XCD coherent)
   // stores; once every thread's stores are complete, one thread counts the
-  // part in. The part that completes the count merges all P records, read
-  // with agent-scope loads, into out and lse. No workgroup waits on another.
+  // part in (past kFlatParts parts on its group's counter, whose last part
+  // then counts the group in). The part that completes the count merges all
+  // P records, read with agent-scope loads, into out and lse. No workgroup
+  // waits on another.
   // The ordering rests on the gfx950 instructions, not on a fence of the
   // memory model: the record stores carry sc1 (written through to the level
   // every XCD sees), s_waitcnt vmcnt(0) and the barrier complete them before
@@ -616,9 +619,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   if (!ctl[4]) return;
   // (the other parts' records were written with agent-scope stores, so they
   // are read with agent-scope loads)
-  // (up to 8 parts, one batch of 3P loads per thread is as fast: P = 8 at 32K;
-  // 9-64 parts: one straight-line instance per size class, so that every load
-  // is issued before the first wait)
+  // (2-64 parts: the lane merge, one straight-line instance per size class so
+  // that every load is issued before the first wait; more parts: batches of 8)
   constexpr int COLS = (G * D + NT - 1) / NT;
   const float* pr = a.part + (size_t)unit * P * G * W;
   const float* ph = a.phdr + (size_t)unit * G * P * 2;
