@@ -73,7 +73,7 @@ struct StepCfg {
   // Chunk records per record-folding wave loaded with the inputs (what the
   // registers left by the other inputs hold, 1..4), and per later batch.
   static constexpr int RWORDS = G * (2 + D / 64);
-  static constexpr int RBUDGET = 112 - UB * G - 2 * GPT * G - 2 * CPL * G;
+  static constexpr int RBUDGET = 112 - UB * G - 2 * GPT * G - 2 * CPL;
   static constexpr int RPF = RBUDGET / RWORDS < 1 ? 1 : (RBUDGET / RWORDS > 4 ? 4 : RBUDGET / RWORDS);
   static constexpr int RPW = 32 / RWORDS < 1 ? 1 : (32 / RWORDS > 4 ? 4 : 32 / RWORDS);
   static constexpr int AW = kStepAttendWaves;                      // attending waves
@@ -213,14 +213,16 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   const int T0 = a.t0[s];
   float2 fi[G];
   load_pairs<G>(reinterpret_cast<const float2*>(a.finfo) + (size_t)unit * G, fi);
-  float2 hd[CPL][G];  // chunk lane + 64k: (max, sum) of a
+  // chunk lane + 64k: (max, sum) of a for query head `wave` (waves < G; the
+  // others form no normaliser: they read head 0's, 8 bytes a lane, unused)
+  float2 hd[CPL];
   {
-    const float2* hp = reinterpret_cast<const float2*>(a.hdr) + (size_t)unit * NC * G;
+    const float2* hp = reinterpret_cast<const float2*>(a.hdr) + (size_t)unit * NC * G + (wave < G ? wave : 0);
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
       const int c = lane + 64 * k;
       const int cc = c < NC ? c : NC - 1;
-      load_pairs<G>(hp + (size_t)cc * G, hd[k]);
+      hd[k] = hp[(size_t)cc * G];
     }
   }
   float2 gp[GPT][G];
@@ -291,11 +293,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     if (wave == g) {  // wave-uniform
       float r = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) r = fmaxf(r, lane + 64 * k < NC ? hd[k][g].x : -INFINITY);
+      for (int k = 0; k < CPL; ++k) r = fmaxf(r, lane + 64 * k < NC ? hd[k].x : -INFINITY);
       const float Mw = group_max<64>(r);
       float l = 0.f;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) l += lane + 64 * k < NC ? hd[k][g].y * rescale(hd[k][g].x, Mw) : 0.f;
+      for (int k = 0; k < CPL; ++k) l += lane + 64 * k < NC ? hd[k].y * rescale(hd[k].x, Mw) : 0.f;
       const float Lw = group_sum<64>(l);
       const float M = fmaxf(Mw, fa[g]);
       const float L = Lw * rescale(Mw, M) + rescale(fa[g], M);
