@@ -240,6 +240,34 @@ struct QMfma {
     }
     return r;
   }
+  // An LDS copy of q to build the operand from: head h's quarter c
+  // (coordinates (D/4)c ..) at word h*kRowStride + c*kQuarterStride. The
+  // strides (row = 16 words mod 32, quarter = 4 words mod 32) spread the
+  // (head, quarter) pieces a wave reads at once over the banks: at 4 heads
+  // at most two share a bank group (the unpadded [G][D] layout puts all of
+  // them in one).
+  static constexpr int kQuarterStride = D / 4 + 4;
+  static constexpr int kRowStride = 4 * kQuarterStride;
+  template <int G>
+  static constexpr int lds_words() { return G * kRowStride; }
+  // thread t < G*D/4: float4 t of the G heads (head t/(D/4)) into the copy
+  __device__ static void stage(float* qm, int t, float4 v) {
+    const int h = t / (D / 4), f = t - h * (D / 4);
+    const int c = f / (D / 16), o = 4 * f - c * (D / 4);
+    *reinterpret_cast<float4*>(qm + h * kRowStride + c * kQuarterStride + o) = v;
+  }
+  template <int G>
+  __device__ static Raw fetch_lds(const float* qm, int lane) {
+    const int j = lane & 15, c = lane >> 4;
+    const float4* src = reinterpret_cast<const float4*>(qm + (j < G ? j : 0) * kRowStride + c * kQuarterStride);
+    Raw r;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      r.x[i][0] = src[2 * i];
+      r.x[i][1] = src[2 * i + 1];
+    }
+    return r;
+  }
   template <int G>
   __device__ void build_from(const Raw& r, int lane) {
     const float keep = (lane & 15) < G ? 1.f : 0.f;  // columns past the G heads are zero

@@ -171,6 +171,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   constexpr int A_WORDS = NGMAX * G > NW * G * W ? NGMAX * G : NW * G * W;
   __shared__ __align__(16) float areaA[A_WORDS];
   __shared__ __align__(16) float q_l[G * D];  // the G query heads
+  __shared__ __align__(16) float q_m[QMfma<D>::template lds_words<G>()];  // the same, for the MFMA operand
   __shared__ __align__(16) int hist[2048];
   __shared__ __align__(16) uint64_t plist[kListMax + kListPad];  // pivot-bin (key, index) words
   __shared__ uint32_t keys_l[KPT * NT];                            // every block's key, block order
@@ -307,7 +308,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
 #pragma unroll
   for (int k = 0; k < NQ4; ++k) {
     const int i = tid + k * NT;
-    if (i < G * D / 4) reinterpret_cast<float4*>(q_l)[i] = q4[k];
+    if (i < G * D / 4) {
+      reinterpret_cast<float4*>(q_l)[i] = q4[k];
+      QMfma<D>::stage(q_m, i, q4[k]);
+    }
   }
   lds_barrier();
   float lse_g[G];
@@ -514,12 +518,13 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
       // count removes a zero-mass term
       m.on = bk >= 0 && bk < NBa && !nc ? 1.f : 0.f;
     };
-    // the query's MFMA operand loads go first: waiting for them then does
-    // not wait for the tile's
-    const typename QMfma<D>::Raw qr = QMfma<D>::template fetch<G>(a.q + (size_t)unit * G * D, lane);
     TileM<D> t0;
     BlockMean<D> m0;
     load_block(t0, m0, 0);
+    // the query's MFMA operand from its LDS copy, read after the kept list
+    // (LDS reads complete in order; from global memory, its 8 KB per wave
+    // took the L1 path ahead of the tile's loads)
+    const typename QMfma<D>::Raw qr = QMfma<D>::template fetch_lds<G>(q_m, lane);
     QMfma<D> qm;
     qm.template build_from<G>(qr, lane);
     float* pw = pbuf + wave * 16 * G;
