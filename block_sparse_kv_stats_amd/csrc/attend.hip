@@ -262,6 +262,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   __shared__ __align__(16) float recs[NWV * G * W];
   __shared__ float scl[NWV * G + 3 * G];
   __shared__ __align__(16) float pbuf[NWV * 16 * G];
+  __shared__ __align__(16) float q_m[QMfma<D>::template lds_words<G>()];  // the query, for the MFMA operand
 
   int unit, p;
   map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
@@ -283,8 +284,10 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
   // loads are issued before tile j is absorbed. The loop body is straight
   // line and every load unconditional, so each wait counts only the older
   // tile's loads; past the wave's last tile a slot is empty (no valid
-  // token, its loads re-read the last tile from the cache). The query's
-  // MFMA operand is read before the first tile, from global memory.
+  // token, its loads re-read the last tile from the cache). The query is
+  // read once per workgroup into an LDS copy that every wave builds its
+  // MFMA operand from (read by every wave from global memory, it was 8 KB of
+  // L1 traffic per wave ahead of the first tile).
   const int b0 = p * NWV + wave;
   const int n_w = b0 < NB ? (NB - 1 - b0) / stride + 1 : 0;
   const int blast = n_w > 0 ? b0 + (n_w - 1) * stride : 0;
@@ -292,13 +295,16 @@ __global__ __launch_bounds__(kDenseThreads) void dense_kernel(AttendArgs a) {
     const bool in = j < n_w;
     t.load(kc, vc, (long)(in ? b0 + j * stride : blast) * kBlock, in ? T : 0, lane);
   };
-  const typename QMfma<D>::Raw qr = QMfma<D>::template fetch<G>(a.q + (size_t)unit * G * D, lane);
+  static_assert(G * D / 4 <= kDenseThreads, "one float4 of the query per thread");
+  const float4 qv = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[tid < G * D / 4 ? tid : 0];
   TileW<D> t0;
   tile_at(t0, 0);
+  if (tid < G * D / 4) QMfma<D>::stage(q_m, tid, qv);
+  lds_barrier();
   WaveStateW<D, G> st;
   st.init();
   QMfma<D> qm;
-  qm.template build_from<G>(qr, lane);
+  qm.template build_from<G>(QMfma<D>::template fetch_lds<G>(q_m, lane), lane);
   float* pw = pbuf + wave * 16 * G;
   if constexpr (G >= 8) {
     // eight query heads: one tile at a time (a second does not fit the registers)

@@ -214,12 +214,12 @@ struct TileM {
 };
 
 // The query heads as MFMA B operands (head l%16 < G, zero columns after).
-// Lane l needs q of head l%16 at coordinates (D/4)*(l/16) + 8i + e: 32
-// consecutive floats, read straight from global memory (the query is a few
-// KB and cached). Read from the LDS instead, the 16 heads' rows are D floats
-// apart and every such read falls on one bank (a 64-way conflict per
-// instruction, about 1.5 us per wave). fetch issues the loads; build_from
-// converts once they have arrived, so a caller can put other loads between.
+// Lane l needs q of head l%16 at coordinates (D/4)*(l/16) + 8i + e: D/4
+// consecutive floats, read from a padded LDS copy (below). From the plain
+// [G][D] layout every such read falls on one bank (a conflict per
+// instruction of about 1.5 us per wave); from global memory each wave's
+// 8 KB of reads share the L1 path with its tile's loads. fetch_lds issues
+// the LDS reads; build_from converts once they have arrived.
 template <int D>
 struct QMfma {
   static constexpr int NI = D / 32;
@@ -227,19 +227,6 @@ struct QMfma {
   struct Raw {
     float4 x[NI][2];
   };
-  // q: the unit's G heads, [G][D] floats, 16-byte aligned
-  template <int G>
-  __device__ static Raw fetch(const float* q, int lane) {
-    const int j = lane & 15, c = lane >> 4;
-    const float4* src = reinterpret_cast<const float4*>(q + (size_t)(j < G ? j : 0) * D + (D / 4) * c);
-    Raw r;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      r.x[i][0] = src[2 * i];
-      r.x[i][1] = src[2 * i + 1];
-    }
-    return r;
-  }
   // An LDS copy of q to build the operand from: head h's quarter c
   // (coordinates (D/4)c ..) at word h*kRowStride + c*kQuarterStride. The
   // strides (row = 16 words mod 32, quarter = 4 words mod 32) spread the
