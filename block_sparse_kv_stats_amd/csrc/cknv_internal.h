@@ -277,6 +277,21 @@ __device__ __forceinline__ void load_pairs(const float2* p, float2 (&x)[N]) {
   for (int i = 0; i < N; ++i) x[i] = make_float2(f[2 * i], f[2 * i + 1]);
 }
 
+// Loads of values that are the same for the whole workgroup and that no
+// workgroup of the running launch writes (an earlier launch did): through
+// the constant address space they become scalar loads, counted apart from
+// the vector loads, so waiting for them waits for no vector load and no
+// copy of a loaded vector register into a scalar one is needed.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) { return *(const_i32_ptr)p; }
+template <int N>
+__device__ __forceinline__ void load_pairs_uniform(const float2* p, float2 (&x)[N]) {
+  const_f32_ptr q = (const_f32_ptr)(const float*)p;
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = make_float2(q[2 * i], q[2 * i + 1]);
+}
+
 // Workgroup barrier for data exchanged through LDS only. __syncthreads()
 // also orders global memory, so it first waits for every outstanding global
 // load and store of the wave; kernels here never read in one wave what

@@ -211,9 +211,12 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   // groups tid + NT*k, k < GPT
 
   // ================================================================ loads
-  const int T0 = a.t0[s];
+  // T0 and finfo are the same for the whole workgroup: scalar loads, issued
+  // first (left to the scheduler they went out after the vector loads)
+  const int T0 = load_uniform(a.t0 + s);
   float2 fi[G];
-  load_pairs<G>(reinterpret_cast<const float2*>(a.finfo) + (size_t)unit * G, fi);
+  load_pairs_uniform<G>(reinterpret_cast<const float2*>(a.finfo) + (size_t)unit * G, fi);
+  __builtin_amdgcn_sched_barrier(0);
   // chunk lane + 64k: (max, sum) of a for query head `wave` (waves < G; the
   // others form no normaliser: they read head 0's, 8 bytes a lane, unused)
   float2 hd[CPL];
@@ -240,7 +243,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
     const int i = tid + k * NT;
     q4[k] = reinterpret_cast<const float4*>(a.q + (size_t)unit * G * D)[i < G * D / 4 ? i : 0];
   }
-  // the u terms last: the normalisers need only what came before them
+  // the u terms last: the normalisers need only what came before them (the
+  // barrier keeps the scheduler from moving the loads above, the query and
+  // finfo among them, behind the u terms: every wait for them would then
+  // also wait for the u terms)
+  __builtin_amdgcn_sched_barrier(0);
   float uv[UB][G];
 #pragma unroll
   for (int j = 0; j < UB; ++j) {
