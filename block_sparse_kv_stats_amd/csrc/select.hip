@@ -10,7 +10,9 @@
 //
 // One 1024-thread workgroup per unit; thread t computes the keys of blocks
 // t + 1024*m (coalesced) and, once they have passed through LDS, selects on
-// the run of kSelKeysPerThread consecutive blocks it then owns. The
+// the run of KPT consecutive blocks it then owns (KPT the smallest of 2, 4,
+// 6, 8 and 12 that covers max_blocks: a larger one only loads and scans
+// empty slots). The
 // score kernel left, per 16-block group, the partial (max, sum) of
 // a = ln|b| + z̄ + σ̂²/2 per query head and, per block,
 // u_{g,b} = exp(a - group max) σ̂². Here:
@@ -36,11 +38,11 @@ constexpr int kSelWaves = kSelThreads / 64;
 
 }  // namespace
 
-template <int G>
+template <int G, int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
-  constexpr int KPT = kSelKeysPerThread;
+  static_assert(KPT <= kSelKeysPerThread, "the plan's limit");
   constexpr int NW = KPT * kSelThreads / 32;  // words of the kept-block bitmap
-  constexpr int NGmax = kSelThreads * kSelKeysPerThread / kScoreMinGroup;  // score groups, at most
+  constexpr int NGmax = kSelThreads * KPT / kScoreMinGroup;  // score groups, at most
   __shared__ float f[NGmax * G];                 // exp(group max - LSE_g)
   __shared__ float red[kSelWaves * G * 2];
   __shared__ __align__(16) int hist[2048];
@@ -74,7 +76,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     }
   }
   // blocks of u per thread per batch: all of them up to 4 query heads (one round trip)
-  constexpr int UB0 = 48 / G < 4 ? 4 : (48 / G > KPT ? KPT : 48 / G);
+  // (8 query heads with 6 or 8 slots: 4 rows a batch, 6 spilled at the
+  // 1024-thread register cap)
+  constexpr int UB1 = G >= 8 && KPT < 12 ? 4 : 48 / G;
+  constexpr int UB0 = UB1 < 4 ? 4 : (UB1 > KPT ? KPT : UB1);
   float ub[UB0][G];
 #pragma unroll
   for (int m = 0; m < UB0; ++m) {
@@ -139,6 +144,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     if (m0 > 0 && m0 < nper) {
 #pragma unroll
       for (int m = 0; m < UB0; ++m) {
+        if (m0 + m >= KPT) break;  // (a last batch shorter than UB0)
         const int b = tid + (m0 + m) * kSelThreads;
         const int bc = b < NB ? b : NB - 1;
         load_row<G>(u + (size_t)bc * G, ub[m]);
@@ -146,6 +152,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     }
 #pragma unroll
     for (int m = 0; m < UB0; ++m) {
+      if (m0 + m >= KPT) break;
       const int b = tid + (m0 + m) * kSelThreads;
       const int bc = b < NB ? b : NB - 1;
       float S = 0.f;
@@ -272,11 +279,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
 hipError_t launch_select(int G, const SelectArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
-  const void* f = G == 1 ? (const void*)select_kernel<1>
-                : G == 2 ? (const void*)select_kernel<2>
-                : G == 4 ? (const void*)select_kernel<4>
-                : G == 8 ? (const void*)select_kernel<8> : nullptr;
-  if (!f) return hipErrorInvalidValue;
+  const int mb = a.max_blocks;
+  const int kpt = mb <= 2 * kSelThreads ? 2 : mb <= 4 * kSelThreads ? 4 : mb <= 6 * kSelThreads ? 6
+                : mb <= 8 * kSelThreads ? 8 : 12;
+  const void* f = nullptr;
+#define CKNV_SEL_G(GG)                                                                          \
+  if (G == GG)                                                                                  \
+    f = kpt == 2 ? (const void*)select_kernel<GG, 2> : kpt == 4 ? (const void*)select_kernel<GG, 4> \
+      : kpt == 6 ? (const void*)select_kernel<GG, 6> : kpt == 8 ? (const void*)select_kernel<GG, 8> \
+                 : (const void*)select_kernel<GG, 12>;
+  CKNV_SEL_G(1) CKNV_SEL_G(2) CKNV_SEL_G(4) CKNV_SEL_G(8)
+#undef CKNV_SEL_G
+  if (!f || mb > kSelThreads * kSelKeysPerThread) return hipErrorInvalidValue;
   return hipLaunchKernel(f, dim3(U), dim3(kSelThreads), args, 0, st);
 }
 
