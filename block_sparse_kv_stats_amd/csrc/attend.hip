@@ -10,7 +10,7 @@
 // The score kernel already summed the compensation of ALL blocks, per
 // chunk (one score workgroup: 32 or 64 blocks). Here workgroup p of a unit
 //   * adds the exact terms of its slice of the kept list (each wave one
-//     block: 16 tokens x d BF16 keys and values, 4 tokens per load),
+//     block: 16 tokens x d BF16 keys and values, logits on MFMA),
 //   * subtracts those blocks' own compensation terms |b| e^{z̄_b}(1, v̄_b),
 //   * folds in up to 8 of the score kernel's chunk records,
 // and writes one record; merge_kernel then combines a unit's P records into
@@ -39,8 +39,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   constexpr int CAP = stage_cap<G>();
   static_assert(CAP >= kWaves + kMaxChunksPerAttendWG, "record staging too small");
   __shared__ __align__(16) float q_l[G * D];
+  __shared__ __align__(16) float q_m[QMfma<D>::template lds_words<G>()];  // the query, for the MFMA operand
   __shared__ __align__(16) float recs[CAP * G * W];
   __shared__ float scl[CAP * G + 3 * G];
+  __shared__ __align__(16) float pbuf[kWaves * 16 * G];  // the waves' tile probabilities
 
   int unit, p;
   map_wg(blockIdx.x, a.S * a.H, a.P, a.xcd, unit, p);
@@ -65,35 +67,41 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttendArgs a) {
   const bool nc = (a.flags & CKNV_FLAG_NO_COMPENSATION) != 0;
   const int nrec = nc ? 0 : c1 - c0;
   stage_records<D, G>(a.comp + ((size_t)unit * a.C + c0) * G * W, nrec, recs + kWaves * G * W);
-  if (tid < G * D / 4) reinterpret_cast<float4*>(q_l)[tid] = qv;
+  if (tid < G * D / 4) {
+    reinterpret_cast<float4*>(q_l)[tid] = qv;
+    QMfma<D>::stage(q_m, tid, qv);
+  }
   lds_barrier();
 
-  // ---- round 2: the kept blocks' tokens, mean key and value
+  // ---- round 2: the kept blocks' tokens, mean key and value (logits on MFMA)
   int NB = (T + kBlock - 1) / kBlock;
   NB = NB < a.max_blocks ? NB : a.max_blocks;
   const long cap_tok = (long)a.cap_blocks * kBlock;
   const size_t ubase = (size_t)unit * a.cap_blocks;
   const uint16_t* kc = a.k + (size_t)unit * cap_tok * D;
   const uint16_t* vc = a.v + (size_t)unit * cap_tok * D;
-  Tile<D> tile[kBlocksPerAttendWave];
+  TileM<D> tile[kBlocksPerAttendWave];
   BlockMean<D> bm[kBlocksPerAttendWave];
   bool use[kBlocksPerAttendWave];
 #pragma unroll
   for (int i = 0; i < kBlocksPerAttendWave; ++i) {
     use[i] = bidx[i] >= 0 && bidx[i] < NB;
     const int b = use[i] ? bidx[i] : 0;
-    tile[i].load(kc, vc, (long)b * kBlock, use[i] ? (long)T : 0, lane);
     if (use[i]) bm[i].load(a.kbar + (ubase + b) * D, a.vbar + (ubase + b) * D, a.cnt + ubase + b, lane);
+    tile[i].load(kc, vc, (long)b * kBlock, use[i] ? (long)T : 0, lane);
   }
+  QMfma<D> qm;
+  qm.template build_from<G>(QMfma<D>::template fetch_lds<G>(q_m, lane), lane);
+  float* pw = pbuf + wave * 16 * G;
   WaveState<D, G> st;
   st.init();
 #pragma unroll
   for (int i = 0; i < kBlocksPerAttendWave; ++i)
     if (use[i]) {
       if (nc)
-        absorb<D, G, false>(st, tile[i], bm[i], q_l, lane, a.isd);
+        absorb_mfma<D, G, false>(st, tile[i], bm[i], qm, q_l, pw, lane, a.isd);
       else
-        absorb<D, G, true>(st, tile[i], bm[i], q_l, lane, a.isd);
+        absorb_mfma<D, G, true>(st, tile[i], bm[i], qm, q_l, pw, lane, a.isd);
     }
   store_wave_record<D, G>(st, recs + wave * G * W, lane);
   lds_barrier();

@@ -1,6 +1,7 @@
-// Device helpers shared by the attention kernels: BF16 token tiles of one
-// 16-token block, the running softmax state of a wave, the exact-plus-
-// compensation update, and partial-record merging. Internal to libcknv.
+// Device helpers shared by the attention kernels: the running softmax state
+// of a wave, the BF16 token tile of one 16-token block and its exact-plus-
+// compensation update with the logits on MFMA, and partial-record merging.
+// Internal to libcknv.
 #pragma once
 
 #include "cknv_internal.h"
@@ -22,45 +23,6 @@ struct WaveState {
       l[g] = 0.f;
 #pragma unroll
       for (int e = 0; e < VPL; ++e) acc[g][e] = 0.f;
-    }
-  }
-};
-
-// One block's BF16 tokens. Keys: token t = 4*m + tq, lane covers coordinates
-// [cc*EPL, +EPL) (16 lanes per token, 4 tokens per load). Values: every lane
-// loads its VPL coordinates of all 16 tokens. Tokens at or past T load as 0.
-template <int D>
-struct Tile {
-  static constexpr int EPL = D / 16, VPL = D / 64;
-  uint32_t k[4][EPL / 2];
-  uint32_t v[16];  // d=128: 2 bf16 (one word) per token; d=64: 1 bf16 in the low half
-  bool tv[4];
-  int nt;          // valid tokens
-  template <bool NT = false>
-  __device__ void load(const uint16_t* kc, const uint16_t* vc, long tok0, long T, int lane) {
-    const int tq = lane >> 4, cc = lane & 15;
-    const long left = T - tok0;
-    nt = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
-    const int last = nt > 0 ? nt - 1 : 0;  // loads read token min(t, last), values masked after
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = 4 * m + tq;
-      tv[m] = t < nt;
-      const uint16_t* src = kc + (size_t)(tok0 + (t < last ? t : last)) * D + cc * EPL;
-      if (EPL == 8) {
-        const uint4 kk = stream_load_u4<NT>(src);
-        k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
-        k[m][2] = tv[m] ? kk.z : 0u; k[m][3] = tv[m] ? kk.w : 0u;
-      } else {
-        const uint2 kk = stream_load_u2<NT>(src);
-        k[m][0] = tv[m] ? kk.x : 0u; k[m][1] = tv[m] ? kk.y : 0u;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint16_t* src = vc + (size_t)(tok0 + (t < last ? t : last)) * D + lane * VPL;
-      const uint32_t w = VPL == 2 ? stream_load_u1<NT>(src) : stream_load_h<NT>(src);
-      v[t] = t < nt ? w : 0u;
     }
   }
 };
@@ -87,88 +49,6 @@ struct BlockMean {
   // it, and everything issued before it, right there)
   __device__ __forceinline__ float mass() const { return n * on; }
 };
-
-// p of token 4*m + R (held by the lanes of row R) for R = 0..3, in every lane.
-__device__ __forceinline__ void spread_rows(float x, float& r0, float& r1, float& r2, float& r3) {
-  float b;
-  const float a = swap16_lo(x, b);  // a: rows 0,0,2,2   b: rows 1,1,3,3
-  r0 = swap32_lo(a, r2);
-  r1 = swap32_lo(b, r3);
-}
-
-// Add one block's exact terms (and, with COMP, remove its compensation terms;
-// a BlockMean with n = 0 removes nothing). A tile with no valid token adds
-// nothing and leaves the state unchanged.
-template <int D, int G, bool COMP>
-__device__ __forceinline__ void absorb(WaveState<D, G>& st, const Tile<D>& t, const BlockMean<D>& bm,
-                                       const float* q_l, int lane, float isd) {
-  constexpr int EPL = D / 16, VPL = D / 64;
-  const int cc = lane & 15;
-  float zbar[G];
-  if (COMP) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float zp = 0.f;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) zp += bm.kb[e] * q_l[g * D + lane * VPL + e];
-      zbar[g] = group_sum<64>(zp) * isd;
-    }
-  }
-  float z[4][G];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    float kf[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL / 2; ++e) { kf[2 * e] = bf16_lo(t.k[m][e]); kf[2 * e + 1] = bf16_hi(t.k[m][e]); }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float zp = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) zp += kf[e] * q_l[g * D + cc * EPL + e];
-      zp = group_sum<16>(zp) * isd;
-      z[m][g] = t.tv[m] ? zp : -INFINITY;
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float bmax = fmaxf(fmaxf(z[0][g], z[1][g]), fmaxf(z[2][g], z[3][g]));
-    bmax = rows_max(bmax);
-    if (COMP && bm.mass() > 0.f) bmax = fmaxf(bmax, zbar[g]);
-    const float M = fmaxf(st.m[g], bmax);
-    const float sc = rescale(st.m[g], M);
-    float l = st.l[g] * sc;
-    float acc[VPL];
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) acc[e] = st.acc[g][e] * sc;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float pz = t.tv[m] ? __expf(z[m][g] - M) : 0.f;
-      float p[4];
-      spread_rows(pz, p[0], p[1], p[2], p[3]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t vw = t.v[4 * m + q];
-        l += p[q];
-        if (VPL == 2) {
-          acc[0] += p[q] * bf16_lo(vw);
-          acc[1 % VPL] += p[q] * bf16_hi(vw);
-        } else {
-          acc[0] += p[q] * bf16_lo(vw);
-        }
-      }
-    }
-    if (COMP) {
-      const float w = bm.mass() > 0.f ? bm.mass() * __expf(zbar[g] - M) : 0.f;
-      l -= w;
-#pragma unroll
-      for (int e = 0; e < VPL; ++e) acc[e] -= w * bm.vb[e];
-    }
-    st.m[g] = M;
-    st.l[g] = l;
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) st.acc[g][e] = acc[e];
-  }
-}
 
 // ---------------------------------------------------------------- MFMA tiles
 // The logits of a 16-token tile on the matrix cores: S[t][g] = K[t] . q_g as
