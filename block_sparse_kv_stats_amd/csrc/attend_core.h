@@ -536,4 +536,46 @@ __device__ __forceinline__ void merge_parts(const float* parts, int P, float* ou
   }
 }
 
+// A part of a unit counts itself done once its record's agent-scope stores
+// are complete (the caller waits for them and holds a barrier first); true
+// for the part that completes the unit's count. `uc`: the unit's counter,
+// followed by its group counters. Up to kFlatParts parts count on the
+// unit's counter; past that, on their group's (kPartGroup parts), whose
+// last part resets it and counts the group in on the unit's (same-address
+// atomics serialise). One thread calls this.
+__device__ __forceinline__ bool count_part_in(uint32_t* uc, int p, int P) {
+  auto count_in = [](uint32_t* c) {
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (P <= kFlatParts) return count_in(uc) == (uint32_t)(P - 1);
+  // the group's last part counts the group in (its own stores, and so those
+  // of every part that counted into the group before it, are complete), and
+  // resets the group's counter: no part of the group counts again
+  const int grp = p / kPartGroup, ng = (P + kPartGroup - 1) / kPartGroup;
+  const int gsize = P - grp * kPartGroup < kPartGroup ? P - grp * kPartGroup : kPartGroup;
+  if (count_in(uc + 1 + grp) != (uint32_t)(gsize - 1)) return false;
+  __hip_atomic_store(uc + 1 + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return count_in(uc) == (uint32_t)(ng - 1);
+}
+
+// The completing part's merge of a unit's P part records (`parts`, G x W
+// words each; `hdr`: their (m, l) pairs, [G][P]) into out and lse, read with
+// agent-scope loads: 1-64 parts by the lane merge, one straight-line
+// instance per size class so that every load is issued before the first
+// wait; more in batches of 8 records.
+template <int D, int G, int NT>
+__device__ __forceinline__ void merge_parts_any(const float* parts, const float* hdr, int P, float* out, float* lse) {
+  constexpr int COLS = (G * D + NT - 1) / NT;
+  if (P > 64)
+    merge_parts<D, G, NT, 8, COLS, true>(parts, P, out, lse, 0);
+  else if (P <= 8)
+    merge_parts_lanes<D, G, NT, COLS, 8, true>(parts, hdr, P, out, lse);
+  else if (P <= 16)
+    merge_parts_lanes<D, G, NT, COLS, 16, true>(parts, hdr, P, out, lse);
+  else if (P <= 32)
+    merge_parts_lanes<D, G, NT, COLS, 32, true>(parts, hdr, P, out, lse);
+  else
+    merge_parts_lanes<D, G, NT, COLS, 64, true>(parts, hdr, P, out, lse);
+}
+
 }  // namespace cknv

@@ -607,49 +607,11 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs a) {
   __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are complete
   __syncthreads();
   uint32_t* uc = a.pcnt + (size_t)unit * a.pstride;  // the unit's counter, then its group counters
-  if (tid == 0) {
-    auto count_in = [](uint32_t* c) {
-      return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    bool last;
-    if (P <= kFlatParts) {
-      last = count_in(uc) == (uint32_t)(P - 1);
-    } else {
-      // the group's last part counts the group in (its own stores, and so
-      // those of every part that counted into the group before it, are
-      // complete), and resets the group's counter: no part of the group
-      // counts again this step
-      const int grp = p / kPartGroup, ng = (P + kPartGroup - 1) / kPartGroup;
-      const int gsize = P - grp * kPartGroup < kPartGroup ? P - grp * kPartGroup : kPartGroup;
-      last = false;
-      if (count_in(uc + 1 + grp) == (uint32_t)(gsize - 1)) {
-        __hip_atomic_store(uc + 1 + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = count_in(uc) == (uint32_t)(ng - 1);
-      }
-    }
-    ctl[4] = last;
-  }
+  if (tid == 0) ctl[4] = count_part_in(uc, p, P);
   lds_barrier();
   if (!ctl[4]) return;
-  // (the other parts' records were written with agent-scope stores, so they
-  // are read with agent-scope loads)
-  // (2-64 parts: the lane merge, one straight-line instance per size class so
-  // that every load is issued before the first wait; more parts: batches of 8)
-  constexpr int COLS = (G * D + NT - 1) / NT;
-  const float* pr = a.part + (size_t)unit * P * G * W;
-  const float* ph = a.phdr + (size_t)unit * G * P * 2;
-  float* po = a.out + (size_t)unit * G * D;
-  float* pl = a.lse ? a.lse + (size_t)unit * G : nullptr;
-  if (P > 64)
-    merge_parts<D, G, NT, 8, COLS, true>(pr, P, po, pl, 0);
-  else if (P <= 8)
-    merge_parts_lanes<D, G, NT, COLS, 8, true>(pr, ph, P, po, pl);
-  else if (P <= 16)
-    merge_parts_lanes<D, G, NT, COLS, 16, true>(pr, ph, P, po, pl);
-  else if (P <= 32)
-    merge_parts_lanes<D, G, NT, COLS, 32, true>(pr, ph, P, po, pl);
-  else
-    merge_parts_lanes<D, G, NT, COLS, 64, true>(pr, ph, P, po, pl);
+  merge_parts_any<D, G, NT>(a.part + (size_t)unit * P * G * W, a.phdr + (size_t)unit * G * P * 2, P,
+                            a.out + (size_t)unit * G * D, a.lse ? a.lse + (size_t)unit * G : nullptr);
   if (tid == 0) {
     __hip_atomic_store(uc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (h == 0 && app) a.seq_len[s] = T;
