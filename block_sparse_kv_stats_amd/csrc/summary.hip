@@ -61,14 +61,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       const uint16_t* vb = a.v + tok0 * D + c;
       const uint16_t nk = a.new_k[(size_t)unit * D + c];
       const uint16_t nv = a.new_v[(size_t)unit * D + c];
+      // all 16 rows are read (the block lies inside the cache); rows at or
+      // past the new token's are replaced or masked at use, so every load is
+      // issued before the first one is used
+      uint16_t kr[16], vr[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        kr[j] = kb[(size_t)j * D];
+        vr[j] = vb[(size_t)j * D];
+      }
       float kx[16], vx[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const bool old = j < n - 1;
-        const uint16_t kj = old ? kb[(size_t)j * D] : nk;
-        const uint16_t vj = old ? vb[(size_t)j * D] : nv;
-        kx[j] = j < n ? bf16_1(kj) : 0.f;
-        vx[j] = j < n ? bf16_1(vj) : 0.f;
+        kx[j] = j < n ? bf16_1(old ? kr[j] : nk) : 0.f;
+        vx[j] = j < n ? bf16_1(old ? vr[j] : nv) : 0.f;
       }
       a.k[(tok0 + n - 1) * D + c] = nk;
       a.v[(tok0 + n - 1) * D + c] = nv;
@@ -79,11 +86,20 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       a.vbar[row * D + c] = vm;
       if (c == 0) a.cnt[row] = (float)n;
     }
-    lds_barrier();
-    cvar[threadIdx.x] = kv;
-    group_tree_sums<D, kAppendThreads>(cvar, HPI, gs);
-    if (act && c % gs == 0) a.dbar[row * a.r + c / gs] = cvar[threadIdx.x] / (float)gs;
-    lds_barrier();
+    if (gs <= 64) {
+      // a group lies within the wave (coordinates c of one head are lanes):
+      // the same balanced pairwise tree by lane exchanges (lane c adds lane
+      // c^len: left + right, or right + left, which is the same sum)
+      float x = kv;
+      for (int len = 1; len < gs; len <<= 1) x += __shfl_xor(x, len);
+      if (act && c % gs == 0) a.dbar[row * a.r + c / gs] = x / (float)gs;
+    } else {
+      lds_barrier();
+      cvar[threadIdx.x] = kv;
+      group_tree_sums<D, kAppendThreads>(cvar, HPI, gs);
+      if (act && c % gs == 0) a.dbar[row * a.r + c / gs] = cvar[threadIdx.x] / (float)gs;
+      lds_barrier();
+    }
   }
   if (threadIdx.x == 0 && room) a.seq_len[s] = T + 1;
 }
