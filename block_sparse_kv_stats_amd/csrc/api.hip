@@ -161,7 +161,7 @@ int cknv_score_select(const cknv_shape* shape, const cknv_cache* cache, const fl
   hipError_t e = launch_score(shape->d, shape->G, a, p.U, (hipStream_t)stream);
   if (e != hipSuccess) return CKNV_EHIP;
   SelectArgs sa{};
-  sa.seq_len = cache->seq_len; sa.grp = a.grp; sa.u = a.u;
+  sa.seq_len = cache->seq_len; sa.grp = a.grp; sa.u = a.u; sa.hdr = a.hdr; sa.C = p.C;
   sa.scores = scores; sa.sel = sel; sa.n_sel = n_sel;
   sa.H = shape->H; sa.cap_blocks = shape->cap_blocks; sa.max_blocks = max_blocks; sa.NG = p.NG;
   sa.Kb = p.Kb; sa.bpw_shift = p.bpw == 8 ? 3 : 4;

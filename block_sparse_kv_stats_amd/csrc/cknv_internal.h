@@ -97,8 +97,9 @@ struct ScoreArgs {
 
 struct SelectArgs {
   const int32_t* seq_len; const float* grp; const float* u;
+  const float* hdr;  // per unit, chunk and query head: (max, sum) of a over the chunk's blocks
   float* scores; int32_t* sel; int32_t* n_sel;
-  int H, cap_blocks, max_blocks, NG, Kb, bpw_shift;
+  int H, cap_blocks, max_blocks, NG, C, Kb, bpw_shift;
 };
 
 struct AttendArgs {

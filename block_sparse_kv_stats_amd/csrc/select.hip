@@ -16,7 +16,8 @@
 // score kernel left, per 16-block group, the partial (max, sum) of
 // a = ln|b| + z̄ + σ̂²/2 per query head and, per block,
 // u_{g,b} = exp(a - group max) σ̂². Here:
-//   1. LSE_g from the group partials; S_b = sum_g u_{g,b} exp(group max - LSE_g);
+//   1. LSE_g from the chunk partials (wave g reduces query head g's);
+//      S_b = sum_g u_{g,b} exp(group max - LSE_g);
 //      the key of a block is the fp32 bit pattern of S_b (S_b >= 0, so keys
 //      order like values).
 //   2. A 2048-bin histogram of the candidates' (not forced) key top 11 bits;
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   constexpr int NW = KPT * kSelThreads / 32;  // words of the kept-block bitmap
   constexpr int NGmax = kSelThreads * KPT / kScoreMinGroup;  // score groups, at most
   __shared__ float f[NGmax * G];                 // exp(group max - LSE_g)
-  __shared__ float red[kSelWaves * G * 2];
+  __shared__ float lse_s[G];
   __shared__ __align__(16) int hist[2048];
   __shared__ int cnt[KPT * kSelWaves + 1];
   __shared__ __align__(16) uint64_t plist[kListMax + kListPad];  // pivot-bin (key, index) words
@@ -61,8 +62,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 
   // ---- loads, issued before the context length is known (clamped to max_blocks)
   const int T = a.seq_len[s];
+  // wave g < G: query head g's chunk partials, chunk lane + 64k (a chunk
+  // covers at least 32 blocks)
+  constexpr int CPL = (32 * KPT + 63) / 64;
+  const int NC = a.C;
+  float2 hd[CPL];
+  {
+    const float2* hp = reinterpret_cast<const float2*>(a.hdr) + (size_t)unit * NC * G + (wave < G ? wave : 0);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = lane + 64 * k;
+      hd[k] = hp[(size_t)(c < NC ? c : NC - 1) * G];
+    }
+  }
   constexpr int GPT = (NGmax + kSelThreads - 1) / kSelThreads;  // score groups per thread
-  float gr[GPT][G], gl[GPT][G];
+  float gr[GPT][G];  // the groups' max of a per query head
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
     const int gi = tid + k * kSelThreads;
@@ -72,7 +86,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       gr[k][g] = v[g].x;
-      gl[k][g] = v[g].y;
     }
   }
   // blocks of u per thread per batch: all of them up to 4 query heads (one round trip)
@@ -105,30 +118,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   const bool all = NB <= Kb;
   int krem = Kb - 3;
 
-  // ---- LSE_g over all blocks, f = exp(group max - LSE_g)
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
+  // ---- LSE_g over all blocks (wave g reduces head g's chunk partials),
+  // f = exp(group max - LSE_g)
+  if (wave < G) {
     float r = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < GPT; ++k) r = fmaxf(r, tid + k * kSelThreads < NGu ? gr[k][g] : -INFINITY);
-    const float Mw = group_max<64>(r);
+    for (int k = 0; k < CPL; ++k) r = fmaxf(r, lane + 64 * k < NC ? hd[k].x : -INFINITY);
+    const float M = group_max<64>(r);
     float l = 0.f;
 #pragma unroll
-    for (int k = 0; k < GPT; ++k)
-      l += tid + k * kSelThreads < NGu ? gl[k][g] * rescale(gr[k][g], Mw) : 0.f;
-    const float Lw = group_sum<64>(l);
-    if (lane == 0) { red[(wave * G + g) * 2] = Mw; red[(wave * G + g) * 2 + 1] = Lw; }
+    for (int k = 0; k < CPL; ++k) l += lane + 64 * k < NC ? hd[k].y * rescale(hd[k].x, M) : 0.f;
+    const float L = group_sum<64>(l);
+    if (lane == 0) lse_s[wave] = M + __logf(L);
   }
   lds_barrier();
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) M = fmaxf(M, red[(w * G + g) * 2]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) L += red[(w * G + g) * 2 + 1] * rescale(red[(w * G + g) * 2], M);
-    const float lse = M + __logf(L);
+    const float lse = lse_s[g];
 #pragma unroll
     for (int k = 0; k < GPT; ++k)
       if (tid + k * kSelThreads < NGu) f[(tid + k * kSelThreads) * G + g] = __expf(gr[k][g] - lse);
