@@ -63,12 +63,11 @@ def test_part_records_stored_coherently_and_waited_before_the_count(tmp_path):
     assert len(funcs) >= 50, f"only {len(funcs)} step_kernel instances found"
     for name, ins in funcs.items():
         # the part counters only: the unit's (up to kFlatParts parts), or a
-        # group's and then the unit's
+        # group's and then the unit's; the blocks of the two ways of counting
+        # may lie in either order, all after the first one's wait and barrier
         atomics = [i for i, x in enumerate(ins) if x.startswith("global_atomic_add")]
         assert 1 <= len(atomics) <= 3, f"{name}: {len(atomics)} atomic adds"
         at = atomics[0]
-        assert not any(ins[i].startswith("s_barrier") for i in range(at, atomics[-1])), \
-            f"{name}: a barrier between the part counters"
         barriers = [i for i, x in enumerate(ins[:at]) if x.startswith("s_barrier")]
         assert len(barriers) >= 3, name
         # the record is written between the barrier that follows the waves'
