@@ -29,8 +29,8 @@ constexpr int kDenseThreads = 512;        // dense attention: 8 waves per workgr
 constexpr int kDenseBlocksPerWG = 64;     // dense attention: blocks per workgroup (at least, on average)
 constexpr int kDenseMaxWGs = 32;          // dense attention: workgroups per unit (at most)
 constexpr int kDenseTilesInFlight = 3;   // dense attention: tiles per wave in flight (fewer than eight heads)
-constexpr int kSelThreads = 1024;       // selection: one workgroup per unit
-constexpr int kSelKeysPerThread = 12;   // blocks per selection thread: max_blocks <= 12288
+constexpr int kSelThreads = 512;        // selection: one workgroup per unit
+constexpr int kSelKeysPerThread = 24;   // blocks per selection thread: max_blocks <= 12288
 
 // A partial softmax record (per unit, part and query head): running max m,
 // normaliser l, two pad words, then the weighted value sum acc[d]; the pad

@@ -8,11 +8,11 @@
 // blocks are always kept and count against the budget; the remaining slots
 // go to the largest S_b (ties: lower block index).
 //
-// One 1024-thread workgroup per unit; thread t computes the keys of blocks
-// t + 1024*m (coalesced) and, once they have passed through LDS, selects on
-// the run of KPT consecutive blocks it then owns (KPT the smallest of 2, 4,
-// 6, 8 and 12 that covers max_blocks: a larger one only loads and scans
-// empty slots). The
+// One 512-thread workgroup per unit (8 waves: barriers stay cheap); thread t
+// computes the keys of blocks t + 512*m (coalesced) and, once they have
+// passed through LDS, selects on the run of KPT consecutive blocks it then
+// owns (KPT the smallest of 2, 4, 6, 8, 12, 17 and 24 that covers
+// max_blocks: a larger one only loads and scans empty slots). The
 // score kernel left, per 16-block group, the partial (max, sum) of
 // a = ln|b| + z̄ + σ̂²/2 per query head and, per block,
 // u_{g,b} = exp(a - group max) σ̂². Here:
@@ -42,6 +42,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 template <int G, int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   static_assert(KPT <= kSelKeysPerThread, "the plan's limit");
+  static_assert(G <= kSelWaves, "one wave per query head for the normalisers");
   constexpr int NW = KPT * kSelThreads / 32;  // words of the kept-block bitmap
   constexpr int NGmax = kSelThreads * KPT / kScoreMinGroup;  // score groups, at most
   __shared__ float f[NGmax * G];                 // exp(group max - LSE_g)
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   // ---- loads, issued before the context length is known (clamped to max_blocks)
   const int T = a.seq_len[s];
   // wave g < G: query head g's chunk partials, chunk lane + 64k (a chunk
-  // covers at least 32 blocks)
-  constexpr int CPL = (32 * KPT + 63) / 64;
+  // covers at least 32 blocks; G <= 8 waves)
+  constexpr int CPL = (KPT * kSelThreads / 32 + 63) / 64;
   const int NC = a.C;
   float2 hd[CPL];
   {
@@ -100,9 +101,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     const int bc = b < MB ? b : MB - 1;
     load_row<G>(u + (size_t)bc * G, ub[m]);
   }
-  hist[tid] = 0;
-  hist[tid + kSelThreads] = 0;
-  if (tid < NW) keep_bits[tid] = 0u;
+  for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
+  for (int i = tid; i < NW; i += kSelThreads) keep_bits[i] = 0u;
   if (tid == 0) ctl[3] = 0;  // list length
   if (tid < kListMax + kListPad) plist[tid] = 0ull;
 
@@ -220,8 +220,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
   } else if (krem > 0) {
     uint32_t prefix = tau_bin << 21;
     // bits 20..10 among the keys of the pivot bin
-    hist[tid] = 0;
-    hist[tid + kSelThreads] = 0;
+    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
@@ -232,7 +231,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
     prefix |= ((uint32_t)ctl[0]) << 10;
     krem = ctl[1];
     // bits 9..0
-    hist[tid] = 0;
+    for (int i = tid; i < 1024; i += kSelThreads) hist[i] = 0;
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
@@ -287,13 +286,14 @@ hipError_t launch_select(int G, const SelectArgs& a, int U, hipStream_t st) {
   void* args[] = {(void*)&a};
   const int mb = a.max_blocks;
   const int kpt = mb <= 2 * kSelThreads ? 2 : mb <= 4 * kSelThreads ? 4 : mb <= 6 * kSelThreads ? 6
-                : mb <= 8 * kSelThreads ? 8 : 12;
+                : mb <= 8 * kSelThreads ? 8 : mb <= 12 * kSelThreads ? 12 : mb <= 17 * kSelThreads ? 17 : 24;
   const void* f = nullptr;
 #define CKNV_SEL_G(GG)                                                                          \
   if (G == GG)                                                                                  \
     f = kpt == 2 ? (const void*)select_kernel<GG, 2> : kpt == 4 ? (const void*)select_kernel<GG, 4> \
       : kpt == 6 ? (const void*)select_kernel<GG, 6> : kpt == 8 ? (const void*)select_kernel<GG, 8> \
-                 : (const void*)select_kernel<GG, 12>;
+      : kpt == 12 ? (const void*)select_kernel<GG, 12> : kpt == 17 ? (const void*)select_kernel<GG, 17> \
+                  : (const void*)select_kernel<GG, 24>;
   CKNV_SEL_G(1) CKNV_SEL_G(2) CKNV_SEL_G(4) CKNV_SEL_G(8)
 #undef CKNV_SEL_G
   if (!f || mb > kSelThreads * kSelKeysPerThread) return hipErrorInvalidValue;
